@@ -1,0 +1,6 @@
+"""CPU oracle for the MLA hot path (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library.
+"""
+from .mla_oracle import *  # noqa: F401,F403

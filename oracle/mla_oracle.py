@@ -1,0 +1,271 @@
+"""Plain float64 CPU oracle of DeepSeek-V2/V3 multi-head latent attention (MLA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py``.  It shares no code with the HIP library and never reads
+anything the HIP library produced.
+
+The oracle computes the layer the *expanded* way: every head's key and value
+are materialised from the latent rows through ``wkv_b`` and ordinary softmax
+attention runs per head.  No absorption, blocking or fusion is applied.  All
+arithmetic is numpy float64; matrix products use numpy's ``@``.
+
+Page references (titles of the source pages):
+  [NeMo-MLA]   NVIDIA NeMo AutoModel, nemo_automodel.components.models.deepseek_v3.layers, class MLA
+  [Mla]        logicaffeine_compile, model::spec, Struct Mla
+  [MlaWeights] atlas docs, spark_model::layers::qwen3_attention, Struct MlaWeights
+  [NKI-Decode] AWS Neuron NKI, "MLA Decode QKV Kernel API Reference"
+  [NKI-CTE]    AWS Neuron NKI, "QKV CTE MLA Kernel API Reference"
+
+Readings where the pages are silent (each listed in the design notes too):
+  * RMSNorm is x * (mean(x^2) + eps)^-1/2 * gamma with gamma used as is.
+  * RoPE rotates element pair (2i, 2i+1) as the complex number x_2i + j x_2i+1
+    multiplied by exp(j * pos * theta^(-2i/qk_rope)), theta = 10000.
+  * The cached row is [normalised c_kv | roped k_pe]; k_pe is not normalised.
+  * Positions are 0-based; a decode token at position ctx-1 attends to all ctx
+    rows including its own.
+
+Parity pins: every function here is checked in tests/test_oracle_*.py against
+closed forms, textbook special cases, torch's CPU float8 decoding, or
+pure-Python brute force on tiny shapes.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "e4m3fn_value", "decode_tensor", "rms_norm", "rope_angles", "rope_interleaved",
+    "softmax_scale", "project", "expand_kv", "attention", "mla_prefill", "mla_decode",
+    "place_rows", "cache_read_dense", "decode_weights", "dims_of",
+]
+
+
+# ----------------------------------------------------------------------------- storage formats
+def e4m3fn_value(code: int) -> float:
+    """Value of one OCP FP8 E4M3FN code: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+
+    Subnormals (exponent field 0) are m * 2^-9; S.1111.111 is NaN; there is no
+    infinity, so the largest finite magnitude is S.1111.110 = 448.
+    [MlaWeights] fp8 fields: weights ship as FP8-E4M3 with 128x128 block scales."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return s * m * 2.0 ** -9
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3FN_TABLE = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_tensor(kind: str, data: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Exact float64 value of a host array in the library's storage format.
+
+    f32: the float32 values; bf16: uint16 patterns are the top half of a float32;
+    fp8: E4M3FN code value times its block's fp32 scale, the block being 128x128
+    over a [K, N] weight ([NKI-CTE] scale shapes [K/128, ceil(N/128)];
+    [MlaWeights] fp8 fields: the dequantisation multiplies by the block scale)."""
+    if kind == "f32":
+        return np.asarray(data, dtype=np.float32).astype(np.float64)
+    if kind == "bf16":
+        u = np.asarray(data, dtype=np.uint16).astype(np.uint32) << 16
+        return u.view(np.float32).astype(np.float64)
+    if kind == "fp8":
+        vals = _E4M3FN_TABLE[np.asarray(data, dtype=np.uint8)]
+        K, N = vals.shape
+        s = np.asarray(scale, dtype=np.float64)
+        rows = np.arange(K) // 128
+        cols = np.arange(N) // 128
+        return vals * s[rows][:, cols]
+    raise ValueError(kind)
+
+
+# ----------------------------------------------------------------------------- elementary steps
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """Root-mean-square normalisation over the last axis, times gamma.
+
+    [NKI-Decode] Parameters: q_norm_w / kv_norm_w are the RMSNorm gammas of the
+    query latent and the KV latent, norm_eps defaults to 1e-6.
+    [Mla] description: the shared latent is RMS-normed."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * gamma
+
+
+def rope_angles(positions: np.ndarray, rope_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """Angle of pair i at each position: pos * theta^(-2i/rope_dim), shape [T, rope_dim/2].
+
+    [MlaWeights] main_inv_freq: the plain theta = 10000 inverse frequencies with no YaRN."""
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / rope_dim)
+    return np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+
+
+def rope_interleaved(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
+    """Interleaved rotary embedding over the last axis.
+
+    x: [T, ..., rope_dim]; angles: [T, rope_dim/2].  Element 2i pairs with
+    element 2i+1 ([NKI-Decode] Notes: interleaved RoPE, not the half-split
+    pairing of the sparse indexer), rotated as a complex number by the angle
+    ([NeMo-MLA] forward takes complex freqs_cis)."""
+    x = np.asarray(x, dtype=np.float64)
+    shape = x.shape
+    z = x.reshape(shape[:-1] + (shape[-1] // 2, 2))
+    a = angles.reshape((angles.shape[0],) + (1,) * (x.ndim - 2) + (angles.shape[1],))
+    c, s = np.cos(a), np.sin(a)
+    re = z[..., 0] * c - z[..., 1] * s
+    im = z[..., 0] * s + z[..., 1] * c
+    return np.stack([re, im], axis=-1).reshape(shape)
+
+
+def softmax_scale(qk_nope: int, qk_rope: int) -> float:
+    """[NeMo-MLA] softmax_scale = qk_head_dim ** -0.5; [Mla] scale = 1/sqrt(qk_nope + qk_rope)."""
+    return 1.0 / math.sqrt(qk_nope + qk_rope)
+
+
+# ----------------------------------------------------------------------------- projections
+def project(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, dims: dict):
+    """Query and cache-row front end for tokens x [T, hidden] at the given positions.
+
+    Stage 1 ([NKI-CTE] Notes, combined Q/KV path stage 1 and its split):
+        x @ wq_a -> q latent,  x @ wkv_a -> [c_kv | k_pe].
+    Q path stage 2: RMSNorm(q latent) @ wq_b; with no q latent ([Mla] q_lora_rank
+    is optional) the query is x @ wq_b directly.
+    Per head the query is [q_nope | q_pe] ([NKI-Decode] wq_b parameter).
+    RoPE on each head's trailing qk_rope dims and once on k_pe ([Mla] description:
+    the rope key is shared by every head; [NKI-CTE] final assembly).
+
+    Returns q [T, H, dqk] (q_pe roped) and rows [T, kv_lora + qk_rope] = [c_norm | k_pe roped].
+    """
+    H, dn, dr, Lkv = dims["n_heads"], dims["qk_nope"], dims["qk_rope"], dims["kv_lora_rank"]
+    eps = dims["norm_eps"]
+    ang = rope_angles(positions, dr, dims.get("rope_theta", 10000.0))
+    if "wq_a" in W:
+        cq = rms_norm(x @ W["wq_a"], W["q_norm_w"], eps)
+        q = cq @ W["wq_b"]
+    else:
+        q = x @ W["wq_b"]
+    q = q.reshape(x.shape[0], H, dn + dr)
+    q = np.concatenate([q[..., :dn], rope_interleaved(q[..., dn:], ang)], axis=-1)
+    kva = x @ W["wkv_a"]
+    c = rms_norm(kva[:, :Lkv], W["kv_norm_w"], eps)
+    p = rope_interleaved(kva[:, Lkv:], ang)
+    return q, np.concatenate([c, p], axis=-1)
+
+
+def expand_kv(W: Dict[str, np.ndarray], rows: np.ndarray, dims: dict):
+    """Per-head keys and values from latent rows [T, R].
+
+    [NKI-CTE] KV path stage 2: norm(c_kv) @ wkv_b split per head into
+    [k_nope | v]; final assembly: K = [k_nope | k_pe broadcast to every head].
+    Returns K [T, H, dqk], V [T, H, dv]."""
+    H, dn, dv, Lkv = dims["n_heads"], dims["qk_nope"], dims["v_dim"], dims["kv_lora_rank"]
+    T = rows.shape[0]
+    kv = (rows[:, :Lkv] @ W["wkv_b"]).reshape(T, H, dn + dv)
+    p = np.broadcast_to(rows[:, None, Lkv:], (T, H, rows.shape[1] - Lkv))
+    return np.concatenate([kv[..., :dn], p], axis=-1), kv[..., dn:].copy()
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+              q_positions: np.ndarray) -> np.ndarray:
+    """softmax(scale * q K^T) V per head, query i seeing key positions j <= q_positions[i].
+
+    q [Tq, H, dqk], K [Tk, H, dqk], V [Tk, H, dv] -> [Tq, H, dv].  The softmax
+    subtracts the row maximum before exponentiating ([NeMo-MLA] forward with a
+    causal attention_mask; softmax_scale attribute)."""
+    s = np.einsum("ihd,jhd->hij", q, K) * scale
+    j = np.arange(K.shape[0])
+    mask = j[None, :] > np.asarray(q_positions)[:, None]
+    s = np.where(mask[None], -np.inf, s)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return np.einsum("hij,jhd->ihd", p, V)
+
+
+# ----------------------------------------------------------------------------- whole layer
+def mla_prefill(W: Dict[str, np.ndarray], x: np.ndarray, dims: dict) -> dict:
+    """Causal prefill of T tokens at positions 0..T-1 of one sequence.
+
+    Returns q, k, v (the per-head tensors the context-encoding QKV kernel emits,
+    [NKI-CTE] return values), rows (cache rows), o [T, H, dv] and
+    y = concat_h(o) @ wo [T, hidden] ([NeMo-MLA] o_proj)."""
+    T = x.shape[0]
+    pos = np.arange(T)
+    q, rows = project(W, x, pos, dims)
+    K, V = expand_kv(W, rows, dims)
+    o = attention(q, K, V, dims["softmax_scale"], pos)
+    y = o.reshape(T, -1) @ W["wo"]
+    return dict(q=q, k=K, v=V, rows=rows, o=o, y=y)
+
+
+def mla_decode(W: Dict[str, np.ndarray], x: np.ndarray, history: Sequence[np.ndarray],
+               dims: dict, head_chunk: int = 16) -> dict:
+    """One decode step for B sequences; sequence b has len(history[b]) earlier rows.
+
+    The new token sits at position len(history[b]); its row is appended and it
+    attends to every row including its own.  Keys and values are expanded per
+    head through wkv_b (head_chunk heads at a time to bound memory).
+    Returns q [B, H, dqk], rows [B, R], o [B, H, dv], y [B, hidden]."""
+    H, dv = dims["n_heads"], dims["v_dim"]
+    B = x.shape[0]
+    pos = np.array([len(h) for h in history])
+    q, rows = project(W, x, pos, dims)
+    o = np.zeros((B, H, dv))
+    for b in range(B):
+        allrows = np.concatenate([np.asarray(history[b], dtype=np.float64).reshape(-1, rows.shape[1]),
+                                  rows[b:b + 1]], axis=0)
+        for h0 in range(0, H, head_chunk):
+            hs = slice(h0, min(H, h0 + head_chunk))
+            sub = _head_slice(W, dims, hs)
+            K, V = expand_kv(sub, allrows, dict(dims, n_heads=hs.stop - hs.start))
+            o[b, hs] = attention(q[b:b + 1, hs], K, V, dims["softmax_scale"], pos[b:b + 1])[0]
+    y = o.reshape(B, -1) @ W["wo"]
+    return dict(q=q, rows=rows, o=o, y=y)
+
+
+def _head_slice(W, dims, hs: slice) -> dict:
+    w = dims["qk_nope"] + dims["v_dim"]
+    return {"wkv_b": W["wkv_b"][:, hs.start * w:hs.stop * w]}
+
+
+# ----------------------------------------------------------------------------- paged cache
+def place_rows(cache: np.ndarray, slot_mapping: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """Expected cache after writing row t to flat slot slot_mapping[t] ([NKI-Decode]
+    kv_cache / slot_mapping parameters); slot -1 skips the token."""
+    out = cache.copy()
+    flat = out.reshape(-1, out.shape[-1])
+    for t, s in enumerate(np.asarray(slot_mapping)):
+        if s >= 0:
+            flat[s] = rows[t]
+    return out
+
+
+def cache_read_dense(cache: np.ndarray, block_table_row: np.ndarray, n: int, block_size: int) -> np.ndarray:
+    """Rows 0..n-1 of one sequence read back through its block table (logical row t
+    lives in physical block block_table_row[t // block_size] at offset t % block_size)."""
+    out = np.empty((n, cache.shape[-1]), dtype=cache.dtype)
+    for t in range(n):
+        out[t] = cache[block_table_row[t // block_size], t % block_size]
+    return out
+
+
+def decode_weights(tensors: dict) -> Dict[str, np.ndarray]:
+    """float64 views of every weight/gamma of a synth weight dict."""
+    out = {}
+    for name, t in tensors.items():
+        out[name] = decode_tensor(t.kind, t.data, t.scale)
+    return out
+
+
+def dims_of(shape) -> dict:
+    """The scalar parameters of a layer as a plain dict (names follow [NKI-Decode] /
+    [NKI-CTE] parameters)."""
+    return dict(hidden=shape.hidden, n_heads=shape.n_heads, q_lora_rank=shape.q_lora_rank,
+                kv_lora_rank=shape.kv_lora_rank, qk_nope=shape.qk_nope, qk_rope=shape.qk_rope,
+                v_dim=shape.v_dim, norm_eps=shape.norm_eps, rope_theta=shape.rope_theta,
+                softmax_scale=softmax_scale(shape.qk_nope, shape.qk_rope))
