@@ -1,0 +1,185 @@
+"""ctypes binding of libmla.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls, takes torch tensors
+that already live on the GPU, passes their raw pointers and the current HIP
+stream, and raises :class:`MlaError` on a non-zero status.  All computation
+happens in the library's HIP kernels; torch supplies device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+FN_QKV_PREFILL, FN_PREFILL_ATTN, FN_DECODE_QKV, FN_DECODE_ATTN, FN_OUT_PROJ = range(5)
+_DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
+SYMBOLS = ("mla_qkv_prefill", "mla_prefill_attn", "mla_decode_qkv_and_scatter", "mla_decode_attn_absorbed",
+           "mla_out_proj", "mla_workspace_size", "mla_status_string")
+
+
+class MlaError(RuntimeError):
+    pass
+
+
+class MlaConfig(Structure):
+    _fields_ = [("hidden", c_int32), ("n_heads", c_int32), ("q_lora_rank", c_int32), ("kv_lora_rank", c_int32),
+                ("qk_nope", c_int32), ("qk_rope", c_int32), ("v_dim", c_int32), ("softmax_scale", c_float),
+                ("norm_eps", c_float), ("block_size", c_int32), ("act_dtype", c_int32), ("weight_dtype", c_int32)]
+
+
+class MlaWeight(Structure):
+    _fields_ = [("w", c_void_p), ("scale", c_void_p)]
+
+
+class MlaWeights(Structure):
+    _fields_ = [("wq_a", MlaWeight), ("wq_b", MlaWeight), ("wkv_a", MlaWeight), ("wkv_b", MlaWeight),
+                ("wo", MlaWeight), ("q_norm_w", c_void_p), ("kv_norm_w", c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla.so (built by head_latent_attention_amd.build); fails loudly if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m head_latent_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = c_void_p, c_int32, c_int64, c_size_t
+    C, W = POINTER(MlaConfig), POINTER(MlaWeights)
+    lib.mla_qkv_prefill.argtypes = [C, W, P, I32, P, P, P, P, P, P, P, I64, P, SZ, P]
+    lib.mla_prefill_attn.argtypes = [C, P, P, P, I32, P, P, SZ, P]
+    lib.mla_decode_qkv_and_scatter.argtypes = [C, W, P, I32, P, P, P, I64, P, P, P, SZ, P]
+    lib.mla_decode_attn_absorbed.argtypes = [C, W, P, I32, P, I64, P, I32, P, P, P, SZ, P]
+    lib.mla_out_proj.argtypes = [C, W, P, I32, P, P, SZ, P]
+    lib.mla_workspace_size.argtypes = [C, I32, I32, I32]
+    lib.mla_workspace_size.restype = SZ
+    lib.mla_status_string.argtypes = [I32]
+    lib.mla_status_string.restype = c_char_p
+    for name in SYMBOLS[:5]:
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+def config(hidden, n_heads, q_lora_rank, kv_lora_rank, qk_nope, qk_rope, v_dim, *, act="bf16",
+           weight="bf16", block_size=64, softmax_scale=None, norm_eps=1e-6) -> MlaConfig:
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(qk_nope + qk_rope)
+    return MlaConfig(hidden, n_heads, q_lora_rank or 0, kv_lora_rank, qk_nope, qk_rope, v_dim, softmax_scale,
+                     norm_eps, block_size, _DTYPES[act], _DTYPES[weight])
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MlaError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise MlaError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+class Weights:
+    """Holds the device tensors of one layer and their MlaWeights struct."""
+
+    def __init__(self, tensors: Dict[str, torch.Tensor], scales: Optional[Dict[str, torch.Tensor]] = None):
+        self.tensors = dict(tensors)
+        self.scales = dict(scales or {})
+        s = MlaWeights()
+        for name in ("wq_a", "wq_b", "wkv_a", "wkv_b", "wo"):
+            t = self.tensors.get(name)
+            sc = self.scales.get(name)
+            setattr(s, name, MlaWeight(_ptr(t) if t is not None else None, _ptr(sc) if sc is not None else None))
+        s.q_norm_w = _ptr(self.tensors.get("q_norm_w")) if "q_norm_w" in self.tensors else None
+        s.kv_norm_w = _ptr(self.tensors.get("kv_norm_w"))
+        self.struct = s
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(st: int) -> None:
+    if st != 0:
+        raise MlaError(f"libmla status {st}: {load().mla_status_string(st).decode()}")
+
+
+def workspace_size(cfg: MlaConfig, fn: int, n: int, max_context: int = 0) -> int:
+    return int(load().mla_workspace_size(ctypes.byref(cfg), fn, n, max_context))
+
+
+def workspace(cfg: MlaConfig, fn: int, n: int, max_context: int = 0, device="cuda") -> torch.Tensor:
+    size = workspace_size(cfg, fn, n, max_context)
+    return torch.empty(max(size, 1), dtype=torch.uint8, device=device)
+
+
+def _ws(ws, cfg, fn, n, max_context=0, device="cuda"):
+    if ws is None:
+        ws = workspace(cfg, fn, n, max_context, device)
+    return ws, ws.numel()
+
+
+def rope_cos_sin(positions, rope_dim: int, theta: float = 10000.0, device="cuda"):
+    """cos/sin tables [T, rope_dim/2] (fp32) of the interleaved-RoPE angles
+    pos * theta^(-2i/rope_dim), evaluated in float64 on the host.  These are the
+    cos/sin inputs of the projection entry points."""
+    pos = np.asarray(positions, dtype=np.float64)
+    inv = theta ** (-2.0 * np.arange(rope_dim // 2, dtype=np.float64) / rope_dim)
+    ang = pos[:, None] * inv[None, :]
+    c = torch.from_numpy(np.cos(ang).astype(np.float32)).to(device)
+    s = torch.from_numpy(np.sin(ang).astype(np.float32)).to(device)
+    return c, s
+
+
+def mla_qkv_prefill(cfg, w: Weights, x, cos, sin, q, k, v, kv_cache=None, slot_mapping=None, ws=None,
+                    stream=None):
+    T = x.shape[0]
+    ws, nb = _ws(ws, cfg, FN_QKV_PREFILL, T, device=x.device)
+    n_blocks = kv_cache.shape[0] if kv_cache is not None else 0
+    _check(load().mla_qkv_prefill(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(x), T, _ptr(cos), _ptr(sin),
+                                  _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), _ptr(slot_mapping), n_blocks,
+                                  _ptr(ws), nb, _stream(stream)))
+
+
+def mla_prefill_attn(cfg, q, k, v, o, ws=None, stream=None):
+    T = q.shape[0]
+    ws, nb = _ws(ws, cfg, FN_PREFILL_ATTN, T, device=q.device)
+    _check(load().mla_prefill_attn(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), T, _ptr(o), _ptr(ws), nb,
+                                   _stream(stream)))
+
+
+def mla_decode_qkv_and_scatter(cfg, w: Weights, x, cos, sin, kv_cache, slot_mapping, q, ws=None, stream=None):
+    B = x.shape[0]
+    ws, nb = _ws(ws, cfg, FN_DECODE_QKV, B, device=x.device)
+    _check(load().mla_decode_qkv_and_scatter(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(x), B, _ptr(cos),
+                                             _ptr(sin), _ptr(kv_cache), kv_cache.shape[0], _ptr(slot_mapping),
+                                             _ptr(q), _ptr(ws), nb, _stream(stream)))
+
+
+def mla_decode_attn_absorbed(cfg, w: Weights, q, kv_cache, block_table, context_lens, o, ws=None, stream=None):
+    B, max_blocks = block_table.shape
+    ws, nb = _ws(ws, cfg, FN_DECODE_ATTN, B, max_blocks * cfg.block_size, device=q.device)
+    _check(load().mla_decode_attn_absorbed(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(q), B, _ptr(kv_cache),
+                                           kv_cache.shape[0], _ptr(block_table), max_blocks, _ptr(context_lens),
+                                           _ptr(o), _ptr(ws), nb, _stream(stream)))
+
+
+def mla_out_proj(cfg, w: Weights, o, y, ws=None, stream=None):
+    M = o.shape[0]
+    ws, nb = _ws(ws, cfg, FN_OUT_PROJ, M, device=o.device)
+    _check(load().mla_out_proj(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(o.reshape(M, -1)), M, _ptr(y),
+                               _ptr(ws), nb, _stream(stream)))

@@ -1,0 +1,337 @@
+// C ABI of the MLA library: argument validation, workspace layout and kernel
+// dispatch.  Nothing here synchronises the host or allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstdio>
+
+#include "mla.h"
+#include "mla_kernels.h"
+#include "mla_fast.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carving of the caller's workspace into 256-byte aligned pieces.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + used) : nullptr;
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+size_t act_bytes(const Dims& d) { return d.act == 0 ? 4 : 2; }
+
+mla_status check_cfg(const mla_config* c, Dims* d) {
+  if (!c) return MLA_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->q_lora_rank < 0 || c->kv_lora_rank <= 0 || c->qk_nope <= 0 ||
+      c->qk_rope <= 0 || c->v_dim <= 0 || c->block_size <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (c->qk_rope % 2 != 0) return MLA_ERR_INVALID_ARG;
+  if (!(c->softmax_scale > 0.f) || !std::isfinite(c->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!(c->norm_eps >= 0.f) || !std::isfinite(c->norm_eps)) return MLA_ERR_INVALID_ARG;
+  const bool ok_pair = (c->act_dtype == MLA_F32 && c->weight_dtype == MLA_F32) ||
+                       (c->act_dtype == MLA_BF16 && c->weight_dtype == MLA_BF16) ||
+                       (c->act_dtype == MLA_BF16 && c->weight_dtype == MLA_FP8_E4M3);
+  if (!ok_pair) return MLA_ERR_UNSUPPORTED;
+  // limits of the general kernels' per-thread arrays and LDS tiles
+  if (c->kv_lora_rank > 1024 || c->qk_nope + c->qk_rope > 256 || c->v_dim > 256) return MLA_ERR_UNSUPPORTED;
+  d->D = c->hidden;
+  d->H = c->n_heads;
+  d->Lq = c->q_lora_rank;
+  d->Lkv = c->kv_lora_rank;
+  d->dn = c->qk_nope;
+  d->dr = c->qk_rope;
+  d->dv = c->v_dim;
+  d->scale = c->softmax_scale;
+  d->eps = c->norm_eps;
+  d->bs = c->block_size;
+  d->act = c->act_dtype == MLA_F32 ? 0 : 1;
+  d->wk = c->weight_dtype == MLA_F32 ? W_F32 : (c->weight_dtype == MLA_BF16 ? W_BF16 : W_FP8);
+  return MLA_OK;
+}
+
+bool check_weight(const Dims& d, const mla_weight& w) {
+  if (!w.w) return false;
+  if (d.wk == W_FP8) return w.scale != nullptr;
+  return true;
+}
+
+WeightView view(const Dims& d, const mla_weight& w, int64_t N) {
+  WeightView v;
+  v.w = w.w;
+  v.scale = w.scale;
+  v.ld = N;
+  v.scale_ld = (int)((N + 127) / 128);
+  return v;
+}
+
+// ---- workspace layouts (the single source of truth for sizes and pointers) ----------
+struct QkvWs {
+  float* Y1;     // [n, Lq + R]   stage-1 outputs (fp32)
+  float* Qraw;   // [n, H*dqk]    stage-2 query (fp32)
+  void* cqn;     // [n, Lq]       RMSNorm(q latent) * gamma (act)
+  void* cn;      // [n, Lkv]      RMSNorm(c_kv) * gamma (act), prefill only
+  float* KVraw;  // [n, H*(dn+dv)] prefill only
+};
+
+size_t qkv_ws(const Dims& d, int n, bool prefill, void* base, QkvWs* out) {
+  Carver c(base);
+  QkvWs w;
+  w.Y1 = c.take<float>((size_t)n * (d.Lq + d.R()));
+  w.Qraw = c.take<float>((size_t)n * d.H * d.dqk());
+  w.cqn = c.take<char>((size_t)n * (d.Lq > 0 ? d.Lq : 1) * act_bytes(d));
+  w.cn = prefill ? c.take<char>((size_t)n * d.Lkv * act_bytes(d)) : nullptr;
+  w.KVraw = prefill ? c.take<float>((size_t)n * d.H * (d.dn + d.dv)) : nullptr;
+  if (out) *out = w;
+  return c.used;
+}
+
+struct DecodeAttnWs {
+  float* Qabs;     // [B, H, R]
+  float* part_o;   // [B*H*nsplit, Lkv]
+  float* part_ml;  // [B*H*nsplit, 2]
+  int nsplit, chunk;
+  FastDecodeWs fast;
+};
+
+void decode_split_plan(int max_context, int* nsplit, int* chunk) {
+  int ch = 1024;
+  while ((max_context + ch - 1) / ch > 16) ch *= 2;
+  *chunk = ch;
+  *nsplit = (max_context + ch - 1) / ch;
+  if (*nsplit < 1) *nsplit = 1;
+}
+
+size_t decode_attn_ws(const Dims& d, int B, int max_context, void* base, DecodeAttnWs* out) {
+  Carver c(base);
+  DecodeAttnWs w;
+  if (fast_decode_supported(d)) {
+    const size_t need = fast_decode_ws_bytes(d, B, max_context);
+    w.fast.base = c.take<char>(need);
+    w.fast.bytes = need;
+    w.Qabs = nullptr;
+    w.part_o = w.part_ml = nullptr;
+    w.nsplit = w.chunk = 0;
+  } else {
+    decode_split_plan(max_context, &w.nsplit, &w.chunk);
+    w.Qabs = c.take<float>((size_t)B * d.H * d.R());
+    w.part_o = c.take<float>((size_t)B * d.H * w.nsplit * d.Lkv);
+    w.part_ml = c.take<float>((size_t)B * d.H * w.nsplit * 2);
+  }
+  if (out) *out = w;
+  return c.used;
+}
+
+size_t out_proj_ws(const Dims& d, int M, void* base, float** Y) {
+  Carver c(base);
+  float* y = c.take<float>((size_t)M * d.D);
+  if (Y) *Y = y;
+  return c.used;
+}
+
+mla_status hip_status(hipError_t e) {
+  if (e != hipSuccess) {
+    if (std::getenv("MLA_TRACE")) std::fprintf(stderr, "mla: HIP error %s\n", hipGetErrorString(e));
+    return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+#define HIP_TRY(expr)                                     \
+  do {                                                    \
+    hipError_t e_ = (expr);                               \
+    if (e_ != hipSuccess) return hip_status(e_);          \
+  } while (0)
+
+// Shared front end of prefill and decode: stage-1 GEMMs, row builder, query.
+mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, const float* cosT,
+                     const float* sinT, void* q, void* kbuf, void* kv_cache, int64_t n_blocks,
+                     const int32_t* slot_mapping, const QkvWs& ws, hipStream_t s) {
+  const int ldy = d.Lq + d.R();
+  const int64_t n_slots = kv_cache ? n_blocks * d.bs : 0;
+  const int HQ = d.H * d.dqk();
+  if (fast_proj_supported(d)) {
+    if (d.Lq > 0) {
+      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wq_a, d.Lq), ws.Y1, ldy, n, d.Lq, d.D, s));
+      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1 + d.Lq, ldy, n, d.R(), d.D, s));
+    } else {
+      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.D, s));
+      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1, ldy, n, d.R(), d.D, s));
+    }
+  } else {
+    if (d.Lq > 0) {
+      HIP_TRY(gemm_simt(d, x, d.D, view(d, w->wq_a, d.Lq), ws.Y1, ldy, n, d.Lq, d.D, s));
+      HIP_TRY(gemm_simt(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1 + d.Lq, ldy, n, d.R(), d.D, s));
+    } else {
+      HIP_TRY(gemm_simt(d, x, d.D, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.D, s));
+      HIP_TRY(gemm_simt(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1, ldy, n, d.R(), d.D, s));
+    }
+  }
+  HIP_TRY(row_builder(d, ws.Y1, ldy, n, w->q_norm_w, w->kv_norm_w, cosT, sinT, d.Lq > 0 ? ws.cqn : nullptr,
+                      ws.cn, kv_cache, n_slots, slot_mapping, kbuf, s));
+  if (d.Lq > 0) {
+    if (fast_proj_supported(d))
+      HIP_TRY(fast_gemm(d, ws.cqn, d.Lq, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.Lq, s));
+    else
+      HIP_TRY(gemm_simt(d, ws.cqn, d.Lq, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.Lq, s));
+  }
+  HIP_TRY(q_epilogue(d, ws.Qraw, HQ, n, cosT, sinT, q, s));
+  return MLA_OK;
+}
+
+bool check_weights_front(const Dims& d, const mla_weights* w) {
+  if (!w) return false;
+  if (d.Lq > 0 && (!check_weight(d, w->wq_a) || !w->q_norm_w)) return false;
+  return check_weight(d, w->wq_b) && check_weight(d, w->wkv_a) && w->kv_norm_w != nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dtype combination or shape";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t max_context) {
+  Dims d;
+  if (check_cfg(cfg, &d) != MLA_OK || n <= 0) return 0;
+  switch (fn) {
+    case MLA_FN_QKV_PREFILL: return qkv_ws(d, n, true, nullptr, nullptr);
+    case MLA_FN_PREFILL_ATTN: return fast_prefill_attn_ws_bytes(d, n);
+    case MLA_FN_DECODE_QKV: return qkv_ws(d, n, false, nullptr, nullptr);
+    case MLA_FN_DECODE_ATTN:
+      if (max_context <= 0) return 0;
+      return decode_attn_ws(d, n, max_context, nullptr, nullptr);
+    case MLA_FN_OUT_PROJ: return out_proj_ws(d, n, nullptr, nullptr);
+  }
+  return 0;
+}
+
+mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const void* x, int32_t T,
+                           const float* cos, const float* sin, void* q, void* k, void* v,
+                           void* kv_cache, const int32_t* slot_mapping, int64_t n_blocks,
+                           void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  mla_status st = check_cfg(cfg, &d);
+  if (st != MLA_OK) return st;
+  if (T <= 0 || !x || !cos || !sin || !q || !k || !v || !check_weights_front(d, w) || !check_weight(d, w->wkv_b))
+    return MLA_ERR_INVALID_ARG;
+  if ((kv_cache == nullptr) != (slot_mapping == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (kv_cache && n_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  QkvWs L;
+  const size_t need = qkv_ws(d, T, true, ws, &L);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  st = front_end(d, w, x, T, cos, sin, q, k, kv_cache, n_blocks, slot_mapping, L, s);
+  if (st != MLA_OK) return st;
+  const int NKV = d.H * (d.dn + d.dv);
+  if (fast_proj_supported(d))
+    HIP_TRY(fast_gemm(d, L.cn, d.Lkv, view(d, w->wkv_b, NKV), L.KVraw, NKV, T, NKV, d.Lkv, s));
+  else
+    HIP_TRY(gemm_simt(d, L.cn, d.Lkv, view(d, w->wkv_b, NKV), L.KVraw, NKV, T, NKV, d.Lkv, s));
+  HIP_TRY(kv_split(d, L.KVraw, T, k, v, s));
+  return MLA_OK;
+}
+
+mla_status mla_prefill_attn(const mla_config* cfg, const void* q, const void* k, const void* v, int32_t T,
+                            void* o, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  mla_status st = check_cfg(cfg, &d);
+  if (st != MLA_OK) return st;
+  if (T <= 0 || !q || !k || !v || !o) return MLA_ERR_INVALID_ARG;
+  const size_t need = fast_prefill_attn_ws_bytes(d, T);
+  if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (fast_prefill_attn_supported(d))
+    HIP_TRY(fast_prefill_attn(d, q, k, v, T, o, ws, s));
+  else
+    HIP_TRY(prefill_attn_simt(d, q, k, v, T, o, s));
+  return MLA_OK;
+}
+
+mla_status mla_decode_qkv_and_scatter(const mla_config* cfg, const mla_weights* w, const void* x,
+                                      int32_t B, const float* cos, const float* sin, void* kv_cache,
+                                      int64_t n_blocks, const int32_t* slot_mapping, void* q,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  mla_status st = check_cfg(cfg, &d);
+  if (st != MLA_OK) return st;
+  if (B <= 0 || !x || !cos || !sin || !q || !kv_cache || !slot_mapping || n_blocks <= 0 ||
+      !check_weights_front(d, w))
+    return MLA_ERR_INVALID_ARG;
+  QkvWs L;
+  const size_t need = qkv_ws(d, B, false, ws, &L);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  return front_end(d, w, x, B, cos, sin, q, nullptr, kv_cache, n_blocks, slot_mapping, L, (hipStream_t)stream);
+}
+
+mla_status mla_decode_attn_absorbed(const mla_config* cfg, const mla_weights* w, const void* q,
+                                    int32_t B, const void* kv_cache, int64_t n_blocks,
+                                    const int32_t* block_table, int32_t max_blocks,
+                                    const int32_t* context_lens, void* o, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  Dims d;
+  mla_status st = check_cfg(cfg, &d);
+  if (st != MLA_OK) return st;
+  if (B <= 0 || !w || !q || !kv_cache || n_blocks <= 0 || !block_table || max_blocks <= 0 || !context_lens ||
+      !o || !check_weight(d, w->wkv_b))
+    return MLA_ERR_INVALID_ARG;
+  const int64_t max_ctx64 = (int64_t)max_blocks * d.bs;
+  if (max_ctx64 > (1 << 30)) return MLA_ERR_UNSUPPORTED;
+  const int max_ctx = (int)max_ctx64;
+  DecodeAttnWs L;
+  const size_t need = decode_attn_ws(d, B, max_ctx, ws, &L);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const WeightView wkv_b = view(d, w->wkv_b, (int64_t)d.H * (d.dn + d.dv));
+  if (fast_decode_supported(d)) {
+    HIP_TRY(fast_decode_attn(d, q, B, kv_cache, n_blocks, block_table, max_blocks, context_lens, wkv_b, o,
+                             L.fast, s));
+    return MLA_OK;
+  }
+  HIP_TRY(fold_simt(d, q, B, wkv_b, L.Qabs, s));
+  HIP_TRY(decode_attn_simt(d, L.Qabs, B, kv_cache, n_blocks, block_table, max_blocks, context_lens, L.nsplit,
+                           L.chunk, L.part_o, L.part_ml, s));
+  HIP_TRY(combine_simt(d, B, L.nsplit, L.part_o, L.part_ml, wkv_b, o, s));
+  return MLA_OK;
+}
+
+mla_status mla_out_proj(const mla_config* cfg, const mla_weights* w, const void* o, int32_t M, void* y,
+                        void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  mla_status st = check_cfg(cfg, &d);
+  if (st != MLA_OK) return st;
+  if (M <= 0 || !w || !o || !y || !check_weight(d, w->wo)) return MLA_ERR_INVALID_ARG;
+  float* Y = nullptr;
+  const size_t need = out_proj_ws(d, M, ws, &Y);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int K = d.H * d.dv;
+  if (fast_proj_supported(d))
+    HIP_TRY(fast_gemm(d, o, K, view(d, w->wo, d.D), Y, d.D, M, d.D, K, s));
+  else
+    HIP_TRY(gemm_simt(d, o, K, view(d, w->wo, d.D), Y, d.D, M, d.D, K, s));
+  HIP_TRY(cast_rows(d, Y, (int64_t)M * d.D, y, s));
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// MFMA kernels for gfx950 (filled in incrementally; unsupported shapes fall back).
+#include "mla_fast.h"
+
+namespace mla {
+
+bool fast_proj_supported(const Dims&) { return false; }
+hipError_t fast_gemm(const Dims&, const void*, int64_t, const WeightView&, float*, int64_t, int, int, int,
+                     hipStream_t) {
+  return hipErrorInvalidValue;
+}
+bool fast_decode_supported(const Dims&) { return false; }
+size_t fast_decode_ws_bytes(const Dims&, int, int) { return 0; }
+hipError_t fast_decode_attn(const Dims&, const void*, int, const void*, int64_t, const int32_t*, int,
+                            const int32_t*, const WeightView&, void*, const FastDecodeWs&, hipStream_t) {
+  return hipErrorInvalidValue;
+}
+bool fast_prefill_attn_supported(const Dims&) { return false; }
+size_t fast_prefill_attn_ws_bytes(const Dims&, int) { return 0; }
+hipError_t fast_prefill_attn(const Dims&, const void*, const void*, const void*, int, void*, void*,
+                             hipStream_t) {
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

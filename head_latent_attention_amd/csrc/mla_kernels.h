@@ -1,0 +1,63 @@
+// Host-side launchers of the gfx950 MLA kernels.  Every launcher only enqueues
+// on `s` and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_device.h"
+
+namespace mla {
+
+struct Dims {
+  int D, H, Lq, Lkv, dn, dr, dv;
+  float scale, eps;
+  int bs;
+  int act;      // 0 f32, 1 bf16
+  int wk;       // WeightKind
+  int dqk() const { return dn + dr; }
+  int R() const { return Lkv + dr; }
+};
+
+// ---- general (any shape) kernels: SIMT fp32 arithmetic ------------------------------
+// C[M, N] fp32 (row stride ldc) = A[M, K] (act, row stride lda) @ W[K, N]
+hipError_t gemm_simt(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C,
+                     int64_t ldc, int M, int N, int K, hipStream_t s);
+
+// Row builder.  Y [T, ldy] fp32 holds [cq (Lq) | c_kv (Lkv) | k_pe (dr)] starting at column 0
+// (cq absent when Lq == 0).  Writes cqn = RMSNorm(cq)*gq (act [T, Lq], if non-null),
+// cn = RMSNorm(c_kv)*gkv (act [T, Lkv], if non-null), the cache row [cn | RoPE(k_pe)] at
+// slot_mapping[t] (if cache and slot_mapping are non-null), and K[t, h, dn:] = RoPE(k_pe)
+// for every head (if kbuf is non-null).
+hipError_t row_builder(const Dims& d, const float* Y, int64_t ldy, int T, const float* gq,
+                       const float* gkv, const float* cosT, const float* sinT, void* cqn, void* cn,
+                       void* cache, int64_t n_slots, const int32_t* slot_mapping, void* kbuf,
+                       hipStream_t s);
+
+// q[t, h, :] (act) = [Y[t, h*dqk : h*dqk+dn] | RoPE(Y[t, h*dqk+dn : (h+1)*dqk])]
+hipError_t q_epilogue(const Dims& d, const float* Y, int64_t ldy, int T, const float* cosT,
+                      const float* sinT, void* q, hipStream_t s);
+
+// KV[t, h*(dn+dv) + j] fp32 -> K[t, h, j] (j < dn) and V[t, h, j - dn] (act)
+hipError_t kv_split(const Dims& d, const float* KV, int T, void* k, void* v, hipStream_t s);
+
+// y (act, [M, N]) = Y (fp32, [M, N])
+hipError_t cast_rows(const Dims& d, const float* Y, int64_t n, void* y, hipStream_t s);
+
+// Absorbed decode, general version.  Qabs fp32 [B, H, R] = [q_nope @ W_UK | q_pe].
+hipError_t fold_simt(const Dims& d, const void* q, int B, const WeightView& wkv_b, float* Qabs,
+                     hipStream_t s);
+// Split-context attention over the paged cache: partial (o_lat[Lkv], m, l) per
+// (b, h, split) with split s covering tokens [s*chunk, (s+1)*chunk).
+hipError_t decode_attn_simt(const Dims& d, const float* Qabs, int B, const void* cache,
+                            int64_t n_blocks, const int32_t* block_table, int max_blocks,
+                            const int32_t* ctx, int nsplit, int chunk, float* part_o,
+                            float* part_ml, hipStream_t s);
+// Log-sum-exp merge of the splits, then o[b, h] = o_lat @ W_UV[h] (act).
+hipError_t combine_simt(const Dims& d, int B, int nsplit, const float* part_o, const float* part_ml,
+                        const WeightView& wkv_b, void* o, hipStream_t s);
+
+// Causal flash attention, general version: q, k [T, H, dqk], v [T, H, dv] -> o [T, H, dv].
+hipError_t prefill_attn_simt(const Dims& d, const void* q, const void* k, const void* v, int T,
+                             void* o, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,488 @@
+// General-shape MLA kernels for gfx950 (SIMT fp32 arithmetic).
+//
+// These cover every shape the ABI accepts (including the fp32 activation path)
+// and serve as the fallback where the MFMA kernels' shape constraints do not
+// hold.  Each kernel is written for clarity first: fp32 accumulation, LDS tiling
+// where it is cheap, no atomics, fixed reduction order (bitwise reproducible).
+#include "mla_kernels.h"
+
+namespace mla {
+
+// ===================================================================================
+// GEMM: C[M,N] = A[M,K] @ W[K,N], 64x64 tile, BK = 16, 256 threads, 4x4 per thread.
+// ===================================================================================
+template <typename TA, int WK>
+__global__ __launch_bounds__(256) void gemm_simt_kernel(const TA* __restrict__ A, int64_t lda,
+                                                        WeightView W, float* __restrict__ C,
+                                                        int64_t ldc, int M, int N, int K) {
+  __shared__ float As[16][65];
+  __shared__ float Ws[16][64];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = tid + 256 * i;
+      int r = e >> 4, kk = e & 15;
+      int m = m0 + r, k = k0 + kk;
+      As[kk][r] = (m < M && k < K) ? Act<TA>::ld(A, (size_t)m * lda + k) : 0.f;
+      int kw = e >> 6, nn = e & 63;
+      int n = n0 + nn, k2 = k0 + kw;
+      Ws[kw][nn] = (n < N && k2 < K) ? load_w<WK>(W, k2, n) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Ws[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int m = m0 + ty + 16 * i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int n = n0 + tx + 16 * j;
+      if (n < N) C[(size_t)m * ldc + n] = acc[i][j];
+    }
+  }
+}
+
+template <typename TA>
+static hipError_t gemm_simt_t(const Dims& d, const void* A, int64_t lda, const WeightView& W,
+                              float* C, int64_t ldc, int M, int N, int K, hipStream_t s) {
+  dim3 grid((N + 63) / 64, (M + 63) / 64);
+  switch (d.wk) {
+    case W_F32: gemm_simt_kernel<TA, W_F32><<<grid, 256, 0, s>>>((const TA*)A, lda, W, C, ldc, M, N, K); break;
+    case W_BF16: gemm_simt_kernel<TA, W_BF16><<<grid, 256, 0, s>>>((const TA*)A, lda, W, C, ldc, M, N, K); break;
+    default: gemm_simt_kernel<TA, W_FP8><<<grid, 256, 0, s>>>((const TA*)A, lda, W, C, ldc, M, N, K); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t gemm_simt(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C,
+                     int64_t ldc, int M, int N, int K, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  return d.act == 0 ? gemm_simt_t<float>(d, A, lda, W, C, ldc, M, N, K, s)
+                    : gemm_simt_t<bf16_t>(d, A, lda, W, C, ldc, M, N, K, s);
+}
+
+// ===================================================================================
+// Row builder: RMSNorm of both latents, RoPE of k_pe, cache-row scatter, k_pe broadcast.
+// One block of 256 threads per token.
+// ===================================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void row_builder_kernel(
+    const float* __restrict__ Y, int64_t ldy, int Lq, int Lkv, int dr, const float* __restrict__ gq,
+    const float* __restrict__ gkv, float eps, const float* __restrict__ cosT,
+    const float* __restrict__ sinT, T* __restrict__ cqn, T* __restrict__ cn, T* __restrict__ cache,
+    int64_t n_slots, const int32_t* __restrict__ slot_mapping, T* __restrict__ kbuf, int H, int dn) {
+  __shared__ float red[16];
+  const int t = blockIdx.x;
+  const float* y = Y + (size_t)t * ldy;
+  const int R = Lkv + dr, dqk = dn + dr;
+  if (Lq > 0 && cqn != nullptr) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < Lq; i += blockDim.x) ss += y[i] * y[i];
+    float r = rsqrtf(block_sum(ss, red) / (float)Lq + eps);
+    for (int i = threadIdx.x; i < Lq; i += blockDim.x) Act<T>::st(cqn, (size_t)t * Lq + i, y[i] * r * gq[i]);
+  }
+  const float* ckv = y + Lq;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < Lkv; i += blockDim.x) ss += ckv[i] * ckv[i];
+  const float r = rsqrtf(block_sum(ss, red) / (float)Lkv + eps);
+  int64_t slot = -1;
+  if (cache != nullptr && slot_mapping != nullptr) {
+    slot = slot_mapping[t];
+    if (slot >= n_slots) slot = -1;
+  }
+  for (int i = threadIdx.x; i < Lkv; i += blockDim.x) {
+    float v = Act<T>::round(ckv[i] * r * gkv[i]);
+    if (cn) Act<T>::st(cn, (size_t)t * Lkv + i, v);
+    if (slot >= 0) Act<T>::st(cache, (size_t)slot * R + i, v);
+  }
+  const float* pe = ckv + Lkv;
+  const int half = dr >> 1;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    float c = cosT[(size_t)t * half + i], sn = sinT[(size_t)t * half + i];
+    float x0 = pe[2 * i], x1 = pe[2 * i + 1];
+    float y0 = Act<T>::round(x0 * c - x1 * sn), y1 = Act<T>::round(x0 * sn + x1 * c);
+    if (slot >= 0) {
+      Act<T>::st(cache, (size_t)slot * R + Lkv + 2 * i, y0);
+      Act<T>::st(cache, (size_t)slot * R + Lkv + 2 * i + 1, y1);
+    }
+    if (kbuf) {
+      for (int h = 0; h < H; ++h) {
+        size_t base = ((size_t)t * H + h) * dqk + dn + 2 * i;
+        Act<T>::st(kbuf, base, y0);
+        Act<T>::st(kbuf, base + 1, y1);
+      }
+    }
+  }
+}
+
+hipError_t row_builder(const Dims& d, const float* Y, int64_t ldy, int T, const float* gq,
+                       const float* gkv, const float* cosT, const float* sinT, void* cqn, void* cn,
+                       void* cache, int64_t n_slots, const int32_t* slot_mapping, void* kbuf,
+                       hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (d.act == 0)
+    row_builder_kernel<float><<<T, 256, 0, s>>>(Y, ldy, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT,
+                                                 (float*)cqn, (float*)cn, (float*)cache, n_slots,
+                                                 slot_mapping, (float*)kbuf, d.H, d.dn);
+  else
+    row_builder_kernel<bf16_t><<<T, 256, 0, s>>>(Y, ldy, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT,
+                                                  (bf16_t*)cqn, (bf16_t*)cn, (bf16_t*)cache, n_slots,
+                                                  slot_mapping, (bf16_t*)kbuf, d.H, d.dn);
+  return hipGetLastError();
+}
+
+// ===================================================================================
+// Query epilogue: per-head RoPE on the trailing dr dims and the cast to act.
+// ===================================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void q_epilogue_kernel(const float* __restrict__ Y, int64_t ldy,
+                                                         int H, int dn, int dr,
+                                                         const float* __restrict__ cosT,
+                                                         const float* __restrict__ sinT,
+                                                         T* __restrict__ q) {
+  const int t = blockIdx.x, dqk = dn + dr, half = dr >> 1;
+  const float* y = Y + (size_t)t * ldy;
+  for (int e = threadIdx.x; e < H * dqk; e += blockDim.x) {
+    const int h = e / dqk, dd = e - h * dqk;
+    float v;
+    if (dd < dn) {
+      v = y[e];
+    } else {
+      const int i = (dd - dn) >> 1;
+      const float c = cosT[(size_t)t * half + i], sn = sinT[(size_t)t * half + i];
+      const float x0 = y[h * dqk + dn + 2 * i], x1 = y[h * dqk + dn + 2 * i + 1];
+      v = ((dd - dn) & 1) ? (x0 * sn + x1 * c) : (x0 * c - x1 * sn);
+    }
+    Act<T>::st(q, (size_t)t * H * dqk + e, v);
+  }
+}
+
+hipError_t q_epilogue(const Dims& d, const float* Y, int64_t ldy, int T, const float* cosT,
+                      const float* sinT, void* q, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (d.act == 0)
+    q_epilogue_kernel<float><<<T, 256, 0, s>>>(Y, ldy, d.H, d.dn, d.dr, cosT, sinT, (float*)q);
+  else
+    q_epilogue_kernel<bf16_t><<<T, 256, 0, s>>>(Y, ldy, d.H, d.dn, d.dr, cosT, sinT, (bf16_t*)q);
+  return hipGetLastError();
+}
+
+// ===================================================================================
+// KV split: [k_nope | v] per head -> K[..., :dn], V.
+// ===================================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void kv_split_kernel(const float* __restrict__ KV, int H, int dn,
+                                                       int dr, int dv, T* __restrict__ k,
+                                                       T* __restrict__ v) {
+  const int t = blockIdx.x, w = dn + dv, dqk = dn + dr;
+  const float* y = KV + (size_t)t * H * w;
+  for (int e = threadIdx.x; e < H * w; e += blockDim.x) {
+    const int h = e / w, j = e - h * w;
+    if (j < dn) Act<T>::st(k, ((size_t)t * H + h) * dqk + j, y[e]);
+    else Act<T>::st(v, ((size_t)t * H + h) * dv + (j - dn), y[e]);
+  }
+}
+
+hipError_t kv_split(const Dims& d, const float* KV, int T, void* k, void* v, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (d.act == 0) kv_split_kernel<float><<<T, 256, 0, s>>>(KV, d.H, d.dn, d.dr, d.dv, (float*)k, (float*)v);
+  else kv_split_kernel<bf16_t><<<T, 256, 0, s>>>(KV, d.H, d.dn, d.dr, d.dv, (bf16_t*)k, (bf16_t*)v);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ Y, int64_t n, T* __restrict__ y) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    Act<T>::st(y, i, Y[i]);
+}
+
+hipError_t cast_rows(const Dims& d, const float* Y, int64_t n, void* y, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int grid = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  if (d.act == 0) cast_kernel<float><<<grid, 256, 0, s>>>(Y, n, (float*)y);
+  else cast_kernel<bf16_t><<<grid, 256, 0, s>>>(Y, n, (bf16_t*)y);
+  return hipGetLastError();
+}
+
+// ===================================================================================
+// Absorbed decode, general kernels.
+// ===================================================================================
+template <typename T, int WK>
+__global__ __launch_bounds__(256) void fold_simt_kernel(const T* __restrict__ q, int H, int dn, int dr,
+                                                        int dv, int Lkv, WeightView W,
+                                                        float* __restrict__ Qabs) {
+  extern __shared__ float qn[];
+  const int bh = blockIdx.x, h = bh % H;
+  const int dqk = dn + dr, R = Lkv + dr;
+  const T* qrow = q + (size_t)bh * dqk;
+  for (int p = threadIdx.x; p < dn; p += blockDim.x) qn[p] = Act<T>::ld(qrow, p);
+  __syncthreads();
+  const int64_t col0 = (int64_t)h * (dn + dv);
+  for (int c = threadIdx.x; c < Lkv; c += blockDim.x) {
+    float acc = 0.f;
+    for (int p = 0; p < dn; ++p) acc = fmaf(qn[p], load_w<WK>(W, c, col0 + p), acc);
+    Qabs[(size_t)bh * R + c] = acc;
+  }
+  for (int i = threadIdx.x; i < dr; i += blockDim.x) Qabs[(size_t)bh * R + Lkv + i] = Act<T>::ld(qrow, dn + i);
+}
+
+hipError_t fold_simt(const Dims& d, const void* q, int B, const WeightView& W, float* Qabs, hipStream_t s) {
+  const int grid = B * d.H;
+  const size_t sh = sizeof(float) * d.dn;
+#define FOLD_LAUNCH(T, WK) fold_simt_kernel<T, WK><<<grid, 256, sh, s>>>((const T*)q, d.H, d.dn, d.dr, d.dv, d.Lkv, W, Qabs)
+  if (d.act == 0) FOLD_LAUNCH(float, W_F32);
+  else if (d.wk == W_BF16) FOLD_LAUNCH(bf16_t, W_BF16);
+  else FOLD_LAUNCH(bf16_t, W_FP8);
+#undef FOLD_LAUNCH
+  return hipGetLastError();
+}
+
+// One block per (b, h, split); 256 threads; tokens processed in tiles of 256.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_attn_simt_kernel(
+    const float* __restrict__ Qabs, int H, int Lkv, int dr, float scale, const T* __restrict__ cache,
+    int64_t n_blocks, int bs, const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ ctx_lens, int nsplit, int chunk, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  extern __shared__ float sh[];
+  const int R = Lkv + dr;
+  float* Q = sh;             // [R]
+  float* P = sh + R;         // [256]
+  __shared__ float red[16];
+  __shared__ int64_t rowoff[256];
+  const int bh = blockIdx.x, sidx = blockIdx.y, b = bh / H;
+  for (int i = threadIdx.x; i < R; i += blockDim.x) Q[i] = Qabs[(size_t)bh * R + i];
+  const int ctx = ctx_lens[b];
+  const int t0 = sidx * chunk, t1 = min(ctx, t0 + chunk);
+  float m = -INFINITY, l = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};  // c = threadIdx.x + 256*j, Lkv <= 1024
+  __syncthreads();
+  for (int tb = t0; tb < t1; tb += 256) {
+    const int t = tb + threadIdx.x;
+    float sc = -INFINITY;
+    int64_t off = -1;
+    if (t < t1 && t / bs < max_blocks) {
+      const int blk = block_table[(size_t)b * max_blocks + t / bs];
+      if (blk >= 0 && blk < n_blocks) {
+        off = ((int64_t)blk * bs + (t % bs)) * R;
+        float acc = 0.f;
+        for (int dd = 0; dd < R; ++dd) acc = fmaf(Q[dd], Act<T>::ld(cache, off + dd), acc);
+        sc = acc * scale;
+      }
+    }
+    rowoff[threadIdx.x] = off;
+    const float tmax = block_max(sc, red);
+    const float mnew = fmaxf(m, tmax);
+    const float p = (sc == -INFINITY) ? 0.f : __expf(sc - mnew);
+    P[threadIdx.x] = p;
+    const float psum = block_sum(p, red);  // contains __syncthreads before reads of P / rowoff
+    const float corr = (m == -INFINITY) ? 0.f : __expf(m - mnew);
+    l = l * corr + psum;
+    m = mnew;
+    const int nt = min(256, t1 - tb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      if (c >= Lkv) break;
+      float acc = o[j] * corr;
+      for (int u = 0; u < nt; ++u) {
+        const int64_t ro = rowoff[u];
+        if (ro >= 0) acc = fmaf(P[u], Act<T>::ld(cache, ro + c), acc);
+      }
+      o[j] = acc;
+    }
+    __syncthreads();
+  }
+  const size_t pidx = (size_t)bh * nsplit + sidx;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < Lkv) part_o[pidx * Lkv + c] = o[j];
+  }
+  if (threadIdx.x == 0) {
+    part_ml[pidx * 2] = m;
+    part_ml[pidx * 2 + 1] = l;
+  }
+}
+
+hipError_t decode_attn_simt(const Dims& d, const float* Qabs, int B, const void* cache, int64_t n_blocks,
+                            const int32_t* block_table, int max_blocks, const int32_t* ctx, int nsplit,
+                            int chunk, float* part_o, float* part_ml, hipStream_t s) {
+  dim3 grid(B * d.H, nsplit);
+  const size_t sh = sizeof(float) * (d.R() + 256);
+  if (d.act == 0)
+    decode_attn_simt_kernel<float><<<grid, 256, sh, s>>>(Qabs, d.H, d.Lkv, d.dr, d.scale, (const float*)cache,
+                                                          n_blocks, d.bs, block_table, max_blocks, ctx, nsplit,
+                                                          chunk, part_o, part_ml);
+  else
+    decode_attn_simt_kernel<bf16_t><<<grid, 256, sh, s>>>(Qabs, d.H, d.Lkv, d.dr, d.scale, (const bf16_t*)cache,
+                                                           n_blocks, d.bs, block_table, max_blocks, ctx, nsplit,
+                                                           chunk, part_o, part_ml);
+  return hipGetLastError();
+}
+
+template <typename T, int WK>
+__global__ __launch_bounds__(256) void combine_simt_kernel(int H, int Lkv, int dn, int dv, int nsplit,
+                                                           const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           WeightView W, T* __restrict__ o) {
+  extern __shared__ float ol[];  // [Lkv]
+  const int bh = blockIdx.x, h = bh % H;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = part_ml[((size_t)bh * nsplit + s) * 2];
+    M = fmaxf(M, ms);
+  }
+  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = part_ml[((size_t)bh * nsplit + s) * 2], ls = part_ml[((size_t)bh * nsplit + s) * 2 + 1];
+    if (ms != -INFINITY) L += ls * __expf(ms - M);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int c = threadIdx.x; c < Lkv; c += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = part_ml[((size_t)bh * nsplit + s) * 2];
+      if (ms != -INFINITY) acc += part_o[((size_t)bh * nsplit + s) * Lkv + c] * __expf(ms - M);
+    }
+    ol[c] = acc * inv;
+  }
+  __syncthreads();
+  const int64_t col0 = (int64_t)h * (dn + dv) + dn;
+  for (int j = threadIdx.x; j < dv; j += blockDim.x) {
+    float acc = 0.f;
+    for (int c = 0; c < Lkv; ++c) acc = fmaf(ol[c], load_w<WK>(W, c, col0 + j), acc);
+    Act<T>::st(o, (size_t)bh * dv + j, acc);
+  }
+}
+
+hipError_t combine_simt(const Dims& d, int B, int nsplit, const float* part_o, const float* part_ml,
+                        const WeightView& W, void* o, hipStream_t s) {
+  const int grid = B * d.H;
+  const size_t sh = sizeof(float) * d.Lkv;
+#define COMB_LAUNCH(T, WK) combine_simt_kernel<T, WK><<<grid, 256, sh, s>>>(d.H, d.Lkv, d.dn, d.dv, nsplit, part_o, part_ml, W, (T*)o)
+  if (d.act == 0) COMB_LAUNCH(float, W_F32);
+  else if (d.wk == W_BF16) COMB_LAUNCH(bf16_t, W_BF16);
+  else COMB_LAUNCH(bf16_t, W_FP8);
+#undef COMB_LAUNCH
+  return hipGetLastError();
+}
+
+// ===================================================================================
+// Causal prefill attention, general version.  Block = 16 queries x 16 lanes of one
+// head; key tiles of 32 staged in LDS as fp32; online softmax.
+// ===================================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void prefill_attn_simt_kernel(const T* __restrict__ q,
+                                                                const T* __restrict__ k,
+                                                                const T* __restrict__ v, int T_, int H,
+                                                                int dqk, int dv, float scale,
+                                                                T* __restrict__ o) {
+  extern __shared__ float sh[];
+  float* Qs = sh;                    // [16][dqk]
+  float* Ks = Qs + 16 * dqk;         // [32][dqk + 1]
+  float* Vs = Ks + 32 * (dqk + 1);   // [32][dv]
+  float* Ps = Vs + 32 * dv;          // [16][32]
+  const int h = blockIdx.y, q0 = blockIdx.x * 16;
+  const int tid = threadIdx.x, qi = tid >> 4, lane = tid & 15;
+  const int tq = q0 + qi;
+  for (int e = tid; e < 16 * dqk; e += 256) {
+    const int r = e / dqk, c = e - r * dqk;
+    Qs[e] = (q0 + r < T_) ? Act<T>::ld(q, ((size_t)(q0 + r) * H + h) * dqk + c) : 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  const int kend = min(T_, q0 + 16);  // causal: keys < kend
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < 32 * dqk; e += 256) {
+      const int r = e / dqk, c = e - r * dqk;
+      Ks[r * (dqk + 1) + c] = (k0 + r < T_) ? Act<T>::ld(k, ((size_t)(k0 + r) * H + h) * dqk + c) : 0.f;
+    }
+    for (int e = tid; e < 32 * dv; e += 256) {
+      const int r = e / dv, c = e - r * dv;
+      Vs[e] = (k0 + r < T_) ? Act<T>::ld(v, ((size_t)(k0 + r) * H + h) * dv + c) : 0.f;
+    }
+    __syncthreads();
+    float s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kj = lane + 16 * u, tk = k0 + kj;
+      float a = 0.f;
+      for (int c = 0; c < dqk; ++c) a = fmaf(Qs[qi * dqk + c], Ks[kj * (dqk + 1) + c], a);
+      s[u] = (tk <= tq && tq < T_) ? a * scale : -INFINITY;
+    }
+    float tmax = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off, 16));
+    const float mnew = fmaxf(m, tmax);
+    float p0 = (s[0] == -INFINITY) ? 0.f : __expf(s[0] - mnew);
+    float p1 = (s[1] == -INFINITY) ? 0.f : __expf(s[1] - mnew);
+    Ps[qi * 32 + lane] = p0;
+    Ps[qi * 32 + lane + 16] = p1;
+    float ps = p0 + p1;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 16);
+    const float corr = (m == -INFINITY) ? 0.f : __expf(m - mnew);
+    l = l * corr + ps;
+    m = mnew;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = lane + 16 * j;
+      if (c < dv) {
+        float a = acc[j] * corr;
+        for (int kj = 0; kj < 32; ++kj) a = fmaf(Ps[qi * 32 + kj], Vs[kj * dv + c], a);
+        acc[j] = a;
+      }
+    }
+  }
+  if (tq < T_) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = lane + 16 * j;
+      if (c < dv) Act<T>::st(o, ((size_t)tq * H + h) * dv + c, acc[j] * inv);
+    }
+  }
+}
+
+hipError_t prefill_attn_simt(const Dims& d, const void* q, const void* k, const void* v, int T, void* o,
+                             hipStream_t s) {
+  dim3 grid((T + 15) / 16, d.H);
+  const int dqk = d.dqk();
+  const size_t sh = sizeof(float) * (16 * dqk + 32 * (dqk + 1) + 32 * d.dv + 16 * 32);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)prefill_attn_simt_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipFuncSetAttribute((const void*)prefill_attn_simt_kernel<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_set = true;
+  }
+  if (d.act == 0)
+    prefill_attn_simt_kernel<float><<<grid, 256, sh, s>>>((const float*)q, (const float*)k, (const float*)v, T,
+                                                           d.H, dqk, d.dv, d.scale, (float*)o);
+  else
+    prefill_attn_simt_kernel<bf16_t><<<grid, 256, sh, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                                                            T, d.H, dqk, d.dv, d.scale, (bf16_t*)o);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,182 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) multi-head latent attention (MLA) hot path.
+ *
+ * The layer is the DeepSeek-V2/V3 MLA described by:
+ *   [NeMo-MLA]   NVIDIA NeMo AutoModel, nemo_automodel.components.models.deepseek_v3.layers, class MLA
+ *   [Mla]        logicaffeine_compile, model::spec, Struct Mla
+ *   [MlaWeights] atlas docs, spark_model::layers::qwen3_attention, Struct MlaWeights
+ *   [NKI-Decode] AWS Neuron NKI, "MLA Decode QKV Kernel API Reference"
+ *   [NKI-CTE]    AWS Neuron NKI, "QKV CTE MLA Kernel API Reference"
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller.  The library keeps
+ *     no pointer after a call returns; buffers must stay alive until `stream`
+ *     reaches the enqueued work.
+ *   - Calls only enqueue work on `stream` (a hipStream_t passed as void*; NULL is
+ *     the null stream).  They never synchronise the host, never copy device to
+ *     host and never allocate device memory: scratch comes from the caller's
+ *     workspace `ws` of `ws_bytes` bytes (see mla_workspace_size).  Workspace
+ *     contents are undefined after a call.  Two calls that share a workspace must
+ *     be ordered on one stream.
+ *   - Tensors are dense row-major with the shapes given below.  "act" tensors
+ *     (x, q, k, v, o, y and the latent cache) have cfg->act_dtype; weights have
+ *     cfg->weight_dtype.  Supported (act, weight) pairs: (F32, F32), (BF16, BF16),
+ *     (BF16, FP8_E4M3).
+ *   - Dimension names: D = hidden, H = n_heads, Lq = q_lora_rank, Lkv = kv_lora_rank,
+ *     dn = qk_nope, dr = qk_rope, dv = v_dim, dqk = dn + dr, R = Lkv + dr (the width
+ *     of one latent-cache row), bs = block_size.
+ *   - Arguments are validated on the host before anything is enqueued; a failed
+ *     check returns a negative status and leaves every output untouched.  HIP
+ *     launch failures return MLA_ERR_HIP.  No C++ exception crosses this ABI.
+ *   - Paging indices (slot_mapping, block_table, context_lens) live on the device
+ *     and are not inspected by the host.  Kernels skip a slot outside
+ *     [0, n_blocks*bs) and treat a block id outside [0, n_blocks) as a row that
+ *     contributes nothing, so bad indices give wrong numbers, never a memory fault.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive or odd dimension, bad count */
+  MLA_ERR_UNSUPPORTED = -2,  /* dtype pair or shape the kernels do not implement      */
+  MLA_ERR_WORKSPACE = -3,    /* ws_bytes smaller than mla_workspace_size(...)         */
+  MLA_ERR_HIP = -4           /* a HIP launch or runtime call failed                   */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype;
+
+/* The layer's parameters, after the logicaffeine Mla struct (fields heads,
+ * q_lora_rank (optional), kv_lora_rank, qk_nope, qk_rope, v_dim, scale) and the
+ * NKI decode-QKV kernel's scalar parameters (n_heads, qk_nope_head_dim,
+ * qk_rope_head_dim, kv_lora_rank, norm_eps). */
+typedef struct {
+  int32_t hidden;         /* D                                                              */
+  int32_t n_heads;        /* H                                                              */
+  int32_t q_lora_rank;    /* Lq; 0 = no query latent, the query is x @ wq_b ([Mla] optional) */
+  int32_t kv_lora_rank;   /* Lkv                                                            */
+  int32_t qk_nope;        /* dn: per-head query/key dims that do not rotate                 */
+  int32_t qk_rope;        /* dr: trailing per-head dims that rotate; must be even           */
+  int32_t v_dim;          /* dv                                                             */
+  float softmax_scale;    /* score scale, normally 1/sqrt(dn + dr) ([NeMo-MLA] softmax_scale) */
+  float norm_eps;         /* RMSNorm epsilon, normally 1e-6 ([NKI-Decode] norm_eps)          */
+  int32_t block_size;     /* bs: rows per paged-cache block                                 */
+  int32_t act_dtype;      /* mla_dtype: MLA_F32 or MLA_BF16                                 */
+  int32_t weight_dtype;   /* mla_dtype: MLA_F32, MLA_BF16 or MLA_FP8_E4M3                   */
+} mla_config;
+
+/* One projection weight [K, N] row-major ("in, out" orientation, as the NKI
+ * kernels take wq_a [hidden, q_lora_rank] and wkv_a [hidden, kv_row_dim]).
+ * For MLA_FP8_E4M3, `w` holds one OCP E4M3FN byte per element and `scale` is
+ * fp32 [ceil(K/128), ceil(N/128)]: element (k, n) is code(k, n) * scale[k/128][n/128]
+ * (the 128x128 block scales of the [MlaWeights] fp8 fields).  Otherwise scale is NULL. */
+typedef struct {
+  const void* w;
+  const float* scale;
+} mla_weight;
+
+typedef struct {
+  mla_weight wq_a;   /* [D, Lq] query down-projection; unused when Lq == 0                     */
+  mla_weight wq_b;   /* [Lq, H*dqk] (or [D, H*dqk] when Lq == 0); per head [q_nope | q_pe]     */
+  mla_weight wkv_a;  /* [D, R] -> one cache row [c_kv | k_pe] per token                        */
+  mla_weight wkv_b;  /* [Lkv, H*(dn+dv)]; per head [k_nope | v].  Its per-head column blocks
+                        are the absorption weights W_UK (first dn) and W_UV (last dv)          */
+  mla_weight wo;     /* [H*dv, D] output projection                                            */
+  const float* q_norm_w;   /* [Lq]  fp32 RMSNorm gamma of the query latent; unused when Lq == 0 */
+  const float* kv_norm_w;  /* [Lkv] fp32 RMSNorm gamma of the KV latent                         */
+} mla_weights;
+
+/* Identifiers of the entry points, for mla_workspace_size. */
+enum {
+  MLA_FN_QKV_PREFILL = 0,
+  MLA_FN_PREFILL_ATTN = 1,
+  MLA_FN_DECODE_QKV = 2,
+  MLA_FN_DECODE_ATTN = 3,
+  MLA_FN_OUT_PROJ = 4
+};
+
+/* Context-encoding projections for T tokens at positions 0..T-1 of one sequence
+ * ([NKI-CTE] qkv_mla_mx, Notes: stage 1 x @ [wq_a | wkv_a], split, RMSNorm of both
+ * latents, stage 2 projections, final assembly).
+ *   x     [T, D] act.
+ *   cos, sin  fp32 [T, dr/2]: cos/sin of the angle of rope pair i at token t
+ *         ([NKI-Decode] cos/sin parameters).  Pair (2i, 2i+1) rotates as a complex number.
+ *   q     [T, H, dqk] act out: per head [q_nope | RoPE(q_pe)].
+ *   k     [T, H, dqk] act out: per head [k_nope | RoPE(k_pe)], the rope key shared by all heads.
+ *   v     [T, H, dv]  act out.
+ *   kv_cache  [n_blocks, 1, bs, R] act, updated in place: row t = [RMSNorm(c_kv) | RoPE(k_pe)]
+ *         is written to flat row slot_mapping[t] (block slot/bs, offset slot%bs); -1 skips.
+ *         kv_cache and slot_mapping may both be NULL (no cache write).
+ *   slot_mapping  int32 [T] or NULL.
+ * T >= 1. */
+mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const void* x, int32_t T,
+                           const float* cos, const float* sin, void* q, void* k, void* v,
+                           void* kv_cache, const int32_t* slot_mapping, int64_t n_blocks,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Causal softmax attention of one sequence's T tokens, per head:
+ *   o[t, h] = sum_{j <= t} softmax_j(scale * q[t,h] . k[j,h]) v[j,h]
+ * ([NeMo-MLA] forward with a causal attention_mask and softmax_scale).
+ *   q, k [T, H, dqk] act; v [T, H, dv] act; o [T, H, dv] act out.  T >= 1. */
+mla_status mla_prefill_attn(const mla_config* cfg, const void* q, const void* k, const void* v,
+                            int32_t T, void* o, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode front end for B sequences, one new token each ([NKI-Decode] mla_decode_qkv:
+ * both projections, both RMSNorms, interleaved RoPE, and the scatter of this step's
+ * row into the paged cache).  The query absorption that kernel also performs is done
+ * by mla_decode_attn_absorbed here.
+ *   x     [B, D] act.
+ *   cos, sin  fp32 [B, dr/2] at each token's position.
+ *   kv_cache  [n_blocks, 1, bs, R] act, updated: row b goes to flat row slot_mapping[b] (-1 skips).
+ *   slot_mapping  int32 [B].
+ *   q     [B, H, dqk] act out: per head [q_nope | RoPE(q_pe)] (not yet absorbed).
+ * B >= 1. */
+mla_status mla_decode_qkv_and_scatter(const mla_config* cfg, const mla_weights* w, const void* x,
+                                      int32_t B, const float* cos, const float* sin, void* kv_cache,
+                                      int64_t n_blocks, const int32_t* slot_mapping, void* q,
+                                      void* ws, size_t ws_bytes, void* stream);
+
+/* Absorbed decode attention over the paged latent cache ([NKI-Decode] background:
+ * the query is absorbed into the cache's latent space; [MlaWeights] w_uk_t / w_uv).
+ *   q_lat[b,h]  = q_nope[b,h] @ W_UK[h]    (W_UK[h][p][c] = wkv_b[c][h*(dn+dv) + p])
+ *   s[b,h,t]    = scale * (q_lat[b,h] . c_t + q_pe[b,h] . k_pe_t),   t < context_lens[b]
+ *   o[b,h]      = (sum_t softmax_t(s) c_t) @ W_UV[h]   (W_UV[h][c][j] = wkv_b[c][h*(dn+dv) + dn + j])
+ * where row t = [c_t | k_pe_t] of sequence b lives in block block_table[b][t/bs] at offset t%bs.
+ *   q        [B, H, dqk] act (as produced by mla_decode_qkv_and_scatter).
+ *   kv_cache [n_blocks, 1, bs, R] act (read only).
+ *   block_table  int32 [B, max_blocks]; entries past ceil(ctx/bs) are ignored.
+ *   context_lens int32 [B], each in [1, max_blocks*bs]; it counts the current token,
+ *                whose row must already be in the cache.
+ *   o        [B, H, dv] act out.
+ * B >= 1, max_blocks >= 1. */
+mla_status mla_decode_attn_absorbed(const mla_config* cfg, const mla_weights* w, const void* q,
+                                    int32_t B, const void* kv_cache, int64_t n_blocks,
+                                    const int32_t* block_table, int32_t max_blocks,
+                                    const int32_t* context_lens, void* o, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/* Output projection y = o @ wo ([NeMo-MLA] o_proj; [MlaWeights] wo).
+ *   o [M, H*dv] act; y [M, D] act out.  M >= 1. */
+mla_status mla_out_proj(const mla_config* cfg, const mla_weights* w, const void* o, int32_t M,
+                        void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes entry point `fn` (MLA_FN_*) needs for n rows (T or B or M) and,
+ * for MLA_FN_DECODE_ATTN, contexts up to max_context tokens.  Returns 0 for an
+ * invalid config or fn.  The value depends only on the arguments. */
+size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t max_context);
+
+/* Static, human-readable text of a status code. */
+const char* mla_status_string(mla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -38,7 +38,7 @@ import numpy as np
 
 __all__ = [
     "e4m3fn_value", "decode_tensor", "rms_norm", "rope_angles", "rope_interleaved",
-    "softmax_scale", "project", "expand_kv", "attention", "mla_prefill", "mla_decode",
+    "softmax_scale", "project", "project_rows", "expand_kv", "attention", "mla_prefill", "mla_decode", "decode_attention",
     "place_rows", "cache_read_dense", "decode_weights", "dims_of",
 ]
 
@@ -151,10 +151,21 @@ def project(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, dims
         q = x @ W["wq_b"]
     q = q.reshape(x.shape[0], H, dn + dr)
     q = np.concatenate([q[..., :dn], rope_interleaved(q[..., dn:], ang)], axis=-1)
+    return q, project_rows(W, x, positions, dims)
+
+
+def project_rows(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, dims: dict) -> np.ndarray:
+    """Latent-cache rows of tokens x [T, hidden]: [RMSNorm(c_kv) | RoPE(k_pe)].
+
+    x @ wkv_a gives one cache row per token split as [c_kv | k_pe] ([NKI-Decode]
+    wkv_a parameter; [NKI-CTE] stage-1 split); the latent is RMS-normed with
+    kv_norm_w, the rope key rotated at the token's position and not normed."""
+    Lkv, dr = dims["kv_lora_rank"], dims["qk_rope"]
+    ang = rope_angles(positions, dr, dims.get("rope_theta", 10000.0))
     kva = x @ W["wkv_a"]
-    c = rms_norm(kva[:, :Lkv], W["kv_norm_w"], eps)
+    c = rms_norm(kva[:, :Lkv], W["kv_norm_w"], dims["norm_eps"])
     p = rope_interleaved(kva[:, Lkv:], ang)
-    return q, np.concatenate([c, p], axis=-1)
+    return np.concatenate([c, p], axis=-1)
 
 
 def expand_kv(W: Dict[str, np.ndarray], rows: np.ndarray, dims: dict):
@@ -177,14 +188,14 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
     q [Tq, H, dqk], K [Tk, H, dqk], V [Tk, H, dv] -> [Tq, H, dv].  The softmax
     subtracts the row maximum before exponentiating ([NeMo-MLA] forward with a
     causal attention_mask; softmax_scale attribute)."""
-    s = np.einsum("ihd,jhd->hij", q, K) * scale
+    s = np.matmul(q.transpose(1, 0, 2), K.transpose(1, 2, 0)) * scale     # [H, Tq, Tk]
     j = np.arange(K.shape[0])
     mask = j[None, :] > np.asarray(q_positions)[:, None]
     s = np.where(mask[None], -np.inf, s)
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
     p = p / p.sum(axis=-1, keepdims=True)
-    return np.einsum("hij,jhd->ihd", p, V)
+    return np.matmul(p, V.transpose(1, 0, 2)).transpose(1, 0, 2)          # [Tq, H, dv]
 
 
 # ----------------------------------------------------------------------------- whole layer
@@ -211,21 +222,35 @@ def mla_decode(W: Dict[str, np.ndarray], x: np.ndarray, history: Sequence[np.nda
     attends to every row including its own.  Keys and values are expanded per
     head through wkv_b (head_chunk heads at a time to bound memory).
     Returns q [B, H, dqk], rows [B, R], o [B, H, dv], y [B, hidden]."""
-    H, dv = dims["n_heads"], dims["v_dim"]
     B = x.shape[0]
     pos = np.array([len(h) for h in history])
     q, rows = project(W, x, pos, dims)
+    seqs = [np.concatenate([np.asarray(history[b], dtype=np.float64).reshape(-1, rows.shape[1]),
+                            rows[b:b + 1]], axis=0) for b in range(B)]
+    o = decode_attention(W, q, seqs, dims, head_chunk)
+    y = o.reshape(B, -1) @ W["wo"]
+    return dict(q=q, rows=rows, o=o, y=y)
+
+
+def decode_attention(W: Dict[str, np.ndarray], q: np.ndarray, seqs: Sequence[np.ndarray], dims: dict,
+                     head_chunk: int = 16) -> np.ndarray:
+    """Attention of one query per sequence over all of that sequence's latent rows.
+
+    q [B, H, dqk] (q_pe already roped); seqs[b] = rows [n_b, R] of sequence b
+    (the query's own row last).  Keys and values are expanded per head through
+    wkv_b ([NKI-CTE] KV path stage 2 and final assembly), head_chunk heads at a
+    time.  Returns o [B, H, dv]."""
+    H, dv = dims["n_heads"], dims["v_dim"]
+    B = q.shape[0]
     o = np.zeros((B, H, dv))
     for b in range(B):
-        allrows = np.concatenate([np.asarray(history[b], dtype=np.float64).reshape(-1, rows.shape[1]),
-                                  rows[b:b + 1]], axis=0)
+        rows = np.asarray(seqs[b], dtype=np.float64)
         for h0 in range(0, H, head_chunk):
             hs = slice(h0, min(H, h0 + head_chunk))
             sub = _head_slice(W, dims, hs)
-            K, V = expand_kv(sub, allrows, dict(dims, n_heads=hs.stop - hs.start))
-            o[b, hs] = attention(q[b:b + 1, hs], K, V, dims["softmax_scale"], pos[b:b + 1])[0]
-    y = o.reshape(B, -1) @ W["wo"]
-    return dict(q=q, rows=rows, o=o, y=y)
+            K, V = expand_kv(sub, rows, dict(dims, n_heads=hs.stop - hs.start))
+            o[b, hs] = attention(q[b:b + 1, hs], K, V, dims["softmax_scale"], np.array([len(rows) - 1]))[0]
+    return o
 
 
 def _head_slice(W, dims, hs: slice) -> dict:

@@ -263,3 +263,21 @@ def fill_cache(cache: np.ndarray, p: Paging, b: int, rows: np.ndarray) -> None:
     slots = slots_for(p.block_table[b], np.arange(n), p.block_size).astype(np.int64)
     flat = cache.reshape(-1, cache.shape[-1])
     flat[slots] = rows
+
+
+# ----------------------------------------------------------------------------- per-entry-point inputs
+def make_normal(w: Workload, name: str, shape, std: float = 1.0) -> Tensor:
+    """N(0, std^2) activations of the given shape in the workload's activation format
+    (used for the q/k/v/o inputs of the attention and output-projection entry points)."""
+    x = rng(w.number, name).standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return encode(x, w.shape.act)
+
+
+def custom(base: Workload, number: int, name: str, **changes) -> Workload:
+    """A variant workload (edge-case sizes) with its own seed number."""
+    shape_keys = {f.name for f in dataclasses.fields(MlaShape)}
+    sh = dataclasses.replace(base.shape, **{k: v for k, v in changes.items() if k in shape_keys})
+    rest = {k: v for k, v in changes.items() if k not in shape_keys}
+    return dataclasses.replace(base, number=number, name=name, shape=sh, **rest)

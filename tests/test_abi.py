@@ -1,0 +1,79 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_latent_attention_amd as mla
+from head_latent_attention_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = mla.load()
+    names = _declared()
+    assert set(names) == set(B.SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    c = dict(hidden=256, n_heads=4, q_lora_rank=64, kv_lora_rank=64, qk_nope=32, qk_rope=16, v_dim=32,
+             act="f32", weight="f32", block_size=16)
+    c.update(kw)
+    return mla.config(**c)
+
+
+def test_status_strings():
+    lib = mla.load()
+    assert lib.mla_status_string(0) == b"ok"
+    assert lib.mla_status_string(-3) == b"workspace too small"
+
+
+def test_workspace_size_validation():
+    lib = mla.load()
+    good = _cfg()
+    for fn in range(5):
+        assert B.workspace_size(good, fn, 8, 64) > 0 or fn == B.FN_PREFILL_ATTN
+    assert B.workspace_size(good, 7, 8, 64) == 0
+    assert B.workspace_size(good, B.FN_DECODE_ATTN, 8, 0) == 0
+    assert B.workspace_size(_cfg(qk_rope=15), 0, 8) == 0
+    assert B.workspace_size(_cfg(act="f32", weight="bf16"), 0, 8) == 0
+    assert B.workspace_size(good, 0, 0) == 0
+
+
+def _call_decode_attn(cfg, ws_bytes=1 << 30, q=1, kv=1, bt=1, ctx=1, o=1, B_=1, max_blocks=1, n_blocks=1,
+                      wkv_b=1):
+    lib = mla.load()
+    W = B.MlaWeights()
+    W.wkv_b = B.MlaWeight(wkv_b, None)
+    return lib.mla_decode_attn_absorbed(ctypes.byref(cfg), ctypes.byref(W), q, B_, kv, n_blocks, bt, max_blocks,
+                                        ctx, o, 1, ws_bytes, None)
+
+
+def test_invalid_arguments_fail_before_launch():
+    cfg = _cfg()
+    assert _call_decode_attn(cfg, q=None) == -1
+    assert _call_decode_attn(cfg, B_=0) == -1
+    assert _call_decode_attn(cfg, max_blocks=0) == -1
+    assert _call_decode_attn(cfg, wkv_b=None) == -1
+    assert _call_decode_attn(_cfg(qk_rope=7)) == -1
+    assert _call_decode_attn(_cfg(act="bf16", weight="f32")) == -2
+    assert _call_decode_attn(_cfg(weight="fp8", act="bf16"), wkv_b=1) == -1  # fp8 weight without scales
+    assert _call_decode_attn(cfg, ws_bytes=16) == -3
+    lib = mla.load()
+    assert lib.mla_prefill_attn(ctypes.byref(cfg), 1, 1, 1, 0, 1, 1, 1 << 20, None) == -1
+    assert lib.mla_out_proj(ctypes.byref(cfg), None, 1, 4, 1, 1, 1 << 20, None) == -1
+    W = B.MlaWeights()
+    assert lib.mla_qkv_prefill(ctypes.byref(cfg), ctypes.byref(W), 1, 4, 1, 1, 1, 1, 1, None, None, 0, 1,
+                               1 << 20, None) == -1
+    assert lib.mla_decode_qkv_and_scatter(None, ctypes.byref(W), 1, 4, 1, 1, 1, 1, 1, 1, 1, 1 << 20, None) == -1

@@ -1,0 +1,196 @@
+"""Per-entry-point GPU parity against the float64 oracle.
+
+Each entry point gets seeded synthetic inputs of the workload's shape and value
+distribution; the oracle sees the same inputs decoded exactly to float64.  Small
+cases are compared element by element; full-size cases compare sampled rows
+(all heads) the oracle can afford, plus every cache row for the scatter."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import mla_oracle as O
+from synth import torch_io
+from helpers import assert_close, device_weights, lib_config, need_gpu, sentinel_cache
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+# small shapes with the V2/V3 per-head dims (kv_lora 512, nope 128, rope 64, v 128) and ragged sizes
+SMALL_V3 = synth.custom(W[4], 101, "small-v3-prefill", hidden=1024, n_heads=16, q_lora_rank=256, T=300)
+SMALL_V2 = synth.custom(W[2], 102, "small-v2-prefill", hidden=512, n_heads=16, T=177)
+EDGE_DEC16 = synth.custom(W[3], 103, "edge-decode-h16", hidden=1024, n_heads=16, q_lora_rank=256, B=6)
+EDGE_DEC128 = synth.custom(W[3], 104, "edge-decode-h128", B=6)
+EDGE_FP8 = synth.custom(W[5], 105, "edge-decode-fp8", B=6)
+EDGE_CTX = np.array([1, 63, 64, 65, 200, 1000], np.int32)
+
+_cache = {}
+
+
+def _weights(w):
+    if w.number not in _cache:
+        _cache.clear()
+        host = synth.make_weights(w)
+        _cache[w.number] = (host, O.decode_weights(host), device_weights(host))
+    return _cache[w.number]
+
+
+def _sample_rows(T, n_rand=12, seed=0):
+    base = {0, 1, 2, 63, 64, 65, 127, 128, T // 2, T - 2, T - 1}
+    r = np.random.default_rng(seed)
+    base |= set(r.integers(0, T, n_rand).tolist())
+    return np.array(sorted(t for t in base if 0 <= t < T))
+
+
+# ----------------------------------------------------------------------------- qkv prefill
+@pytest.mark.parametrize("w", [SMALL_V3, SMALL_V2, W[2], W[4]], ids=lambda w: w.name)
+def test_qkv_prefill(w):
+    need_gpu()
+    import head_latent_attention_amd as mla
+    s, T = w.shape, w.T
+    print(f"[qkv_prefill] {w.name} T={T}", flush=True)
+    host, Wd, dw = _weights(w)
+    cfg = lib_config(s)
+    xh = synth.make_x(w, T)
+    n_blocks = -(-T // s.block_size) + 3
+    perm = synth.shuffled_blocks(w.number, "blocks", n_blocks)
+    slots = synth.slots_for(perm, np.arange(T), s.block_size)
+    if T < 1000:
+        slots[5] = -1  # a skipped token
+    cache = sentinel_cache(s, n_blocks)
+    sentinel = torch_io.bits(cache).reshape(-1)[0]
+    cos, sin = mla.rope_cos_sin(np.arange(T), s.qk_rope)
+    q = torch_io.empty_act(s.act, (T, s.n_heads, s.qk_head))
+    k = torch_io.empty_act(s.act, (T, s.n_heads, s.qk_head))
+    v = torch_io.empty_act(s.act, (T, s.n_heads, s.v_dim))
+    mla.mla_qkv_prefill(cfg, dw, torch_io.to_device(xh), cos, sin, q, k, v, cache, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    dims = O.dims_of(s)
+    x64 = O.decode_tensor(s.act, xh.data)
+    rows = _sample_rows(T) if T > 1000 else np.arange(T)
+    qr, rr = O.project(Wd, x64[rows], rows, dims)
+    Kr, Vr = O.expand_kv(Wd, rr, dims)
+    assert_close(torch_io.to_f64(q)[rows], qr, s.act, "q")
+    assert_close(torch_io.to_f64(k)[rows], Kr, s.act, "k")
+    assert_close(torch_io.to_f64(v)[rows], Vr, s.act, "v")
+    # every cache row: the right row in the right slot, nothing else written
+    all_rows = O.project_rows(Wd, x64, np.arange(T), dims)
+    flat = torch_io.to_f64(cache).reshape(-1, s.row)
+    keep = slots >= 0
+    assert_close(flat[slots[keep]], all_rows[keep], s.act, "cache rows")
+    b = torch_io.bits(cache).reshape(-1, s.row)
+    untouched = np.setdiff1d(np.arange(b.shape[0]), slots[keep])
+    assert (b[untouched] == sentinel).all()
+
+
+# ----------------------------------------------------------------------------- causal attention
+PREFILL_ATTN_CASES = [(SMALL_V3, 1), (SMALL_V3, 17), (SMALL_V3, 300), (SMALL_V2, 129), (W[2], 4096), (W[4], 8192)]
+
+
+@pytest.mark.parametrize("w,T", PREFILL_ATTN_CASES, ids=lambda c: str(c) if isinstance(c, int) else c.name)
+def test_prefill_attn(w, T):
+    need_gpu()
+    import head_latent_attention_amd as mla
+    s = w.shape
+    print(f"[prefill_attn] {w.name} T={T}", flush=True)
+    cfg = lib_config(s)
+    qh = synth.make_normal(w, f"attn.q.{T}", (T, s.n_heads, s.qk_head))
+    kh = synth.make_normal(w, f"attn.k.{T}", (T, s.n_heads, s.qk_head))
+    vh = synth.make_normal(w, f"attn.v.{T}", (T, s.n_heads, s.v_dim))
+    o = torch_io.empty_act(s.act, (T, s.n_heads, s.v_dim))
+    mla.mla_prefill_attn(cfg, torch_io.to_device(qh), torch_io.to_device(kh), torch_io.to_device(vh), o)
+    torch.cuda.synchronize()
+    rows = _sample_rows(T) if T > 1000 else np.arange(T)
+    q64, k64, v64 = (O.decode_tensor(s.act, t.data) for t in (qh, kh, vh))
+    ref = O.attention(q64[rows], k64, v64, O.softmax_scale(s.qk_nope, s.qk_rope), rows)
+    assert_close(torch_io.to_f64(o)[rows], ref, s.act, "o")
+
+
+# ----------------------------------------------------------------------------- decode front end
+@pytest.mark.parametrize("w", [EDGE_DEC16, W[3], W[5]], ids=lambda w: w.name)
+def test_decode_qkv_and_scatter(w):
+    need_gpu()
+    import head_latent_attention_amd as mla
+    s = w.shape
+    print(f"[decode_qkv] {w.name} B={w.B}", flush=True)
+    host, Wd, dw = _weights(w)
+    cfg = lib_config(s)
+    ctx = EDGE_CTX if w.B == 6 else synth.context_lengths(w)
+    pg = synth.make_paging(w.number, ctx, s.block_size)
+    slots = synth.decode_slot_mapping(pg)
+    cache = sentinel_cache(s, pg.n_blocks)
+    sentinel = torch_io.bits(cache[:1]).reshape(-1)[0]
+    xh = synth.make_x(w, w.B, "x.decode")
+    pos = ctx.astype(np.int64) - 1
+    cos, sin = mla.rope_cos_sin(pos, s.qk_rope)
+    q = torch_io.empty_act(s.act, (w.B, s.n_heads, s.qk_head))
+    mla.mla_decode_qkv_and_scatter(cfg, dw, torch_io.to_device(xh), cos, sin, cache,
+                                   torch.from_numpy(slots).cuda(), q)
+    torch.cuda.synchronize()
+    qr, rr = O.project(Wd, O.decode_tensor(s.act, xh.data), pos, O.dims_of(s))
+    assert_close(torch_io.to_f64(q), qr, s.act, "q")
+    flat = cache.view(-1, s.row)
+    got_rows = torch_io.to_f64(flat[torch.from_numpy(slots.astype(np.int64)).cuda()])
+    assert_close(got_rows, rr, s.act, "cache rows")
+    # nothing but the B slots was written
+    mask = torch.ones(flat.shape[0], dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(slots.astype(np.int64)).cuda()] = False
+    rest = flat[mask]
+    assert bool((rest.view(torch.int16 if s.act == "bf16" else torch.int32) == int(sentinel)).all())
+
+
+# ----------------------------------------------------------------------------- absorbed decode attention
+def _paged_cache(w, ctx):
+    s = w.shape
+    pg = synth.make_paging(w.number, ctx, s.block_size)
+    host = np.zeros((pg.n_blocks, s.block_size, s.row), np.uint16 if s.act == "bf16" else np.float32)
+    for b, n in enumerate(ctx):
+        synth.fill_cache(host, pg, b, synth.history_rows(w, b, int(n)).data)
+    kind = synth.BF16 if s.act == "bf16" else synth.F32
+    dev = torch_io.to_device(synth.Tensor(kind, host)).view(pg.n_blocks, 1, s.block_size, s.row)
+    return pg, dev
+
+
+@pytest.mark.parametrize("w", [EDGE_DEC16, EDGE_DEC128, EDGE_FP8, W[3], W[5]], ids=lambda w: w.name)
+def test_decode_attn_absorbed(w):
+    need_gpu()
+    import head_latent_attention_amd as mla
+    s = w.shape
+    print(f"[decode_attn] {w.name} B={w.B}", flush=True)
+    host, Wd, dw = _weights(w)
+    cfg = lib_config(s)
+    ctx = EDGE_CTX if w.B == 6 else synth.context_lengths(w)
+    pg, cache = _paged_cache(w, ctx)
+    qh = synth.make_normal(w, "decode.q", (w.B, s.n_heads, s.qk_head), std=0.8)
+    o = torch_io.empty_act(s.act, (w.B, s.n_heads, s.v_dim))
+    mla.mla_decode_attn_absorbed(cfg, dw, torch_io.to_device(qh), cache, torch.from_numpy(pg.block_table).cuda(),
+                                 torch.from_numpy(ctx).cuda(), o)
+    torch.cuda.synchronize()
+    if w.B <= 8:
+        bs_ = np.arange(w.B)
+    else:
+        order = np.argsort(ctx)
+        bs_ = np.array(sorted({int(order[0]), int(order[1]), int(order[len(order) // 2])}))
+    q64 = O.decode_tensor(s.act, qh.data)
+    seqs = [O.decode_tensor(s.act, synth.history_rows(w, int(b), int(ctx[b])).data) for b in bs_]
+    ref = O.decode_attention(Wd, q64[bs_], seqs, O.dims_of(s))
+    assert_close(torch_io.to_f64(o)[bs_], ref, s.act, f"o (sequences {bs_.tolist()})")
+
+
+# ----------------------------------------------------------------------------- output projection
+@pytest.mark.parametrize("w,M", [(SMALL_V3, 300), (EDGE_FP8, 7), (W[2], 4096), (W[3], 64), (W[4], 8192), (W[5], 256)],
+                         ids=lambda c: str(c) if isinstance(c, int) else c.name)
+def test_out_proj(w, M):
+    need_gpu()
+    import head_latent_attention_amd as mla
+    s = w.shape
+    print(f"[out_proj] {w.name} M={M}", flush=True)
+    host, Wd, dw = _weights(w)
+    cfg = lib_config(s)
+    oh = synth.make_normal(w, f"oproj.o.{M}", (M, s.n_heads * s.v_dim), std=0.5)
+    y = torch_io.empty_act(s.act, (M, s.hidden))
+    mla.mla_out_proj(cfg, dw, torch_io.to_device(oh), y)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M) if M > 1000 else np.arange(M)
+    ref = O.decode_tensor(s.act, oh.data)[rows] @ Wd["wo"]
+    assert_close(torch_io.to_f64(y)[rows], ref, s.act, "y")
