@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Throughput of the MLA hot path on one MI355X.
+
+One step = one decode step of a DeepSeek-V3-shaped MLA layer for a batch of 64
+sequences (bf16, context lengths uniform in [1024, 8192], paged latent cache of
+576-wide rows, block_size 64): mla_decode_qkv_and_scatter ->
+mla_decode_attn_absorbed -> mla_out_proj.  Inputs are seeded synthetic data
+resident in HBM before the timed region.  The JSON line also carries the V3
+causal prefill (8192 tokens) TFLOP/s, the latent-cache GB/s, the roofline of the
+dominant kernel (the absorbed decode attention) and the CPU oracle baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_setup(w, device="cuda"):
+    import torch
+    import synth
+    from synth import torch_io
+    import head_latent_attention_amd as mla
+    s = w.shape
+    host = synth.make_weights(w)
+    tens = {k: torch_io.to_device(v, device) for k, v in host.items()}
+    scales = {k: torch_io.scale_to_device(v, device) for k, v in host.items() if v.scale is not None}
+    dw = mla.Weights(tens, scales)
+    cfg = mla.config(s.hidden, s.n_heads, s.q_lora_rank, s.kv_lora_rank, s.qk_nope, s.qk_rope, s.v_dim,
+                     act=s.act, weight=s.weight, block_size=s.block_size)
+    ctx = synth.context_lengths(w)
+    pg = synth.make_paging(w.number, ctx, s.block_size)
+    cache = torch.empty((pg.n_blocks, 1, s.block_size, s.row), dtype=torch.bfloat16, device=device)
+    flat = cache.view(-1, s.row)
+    for b, n in enumerate(ctx):
+        rows = torch_io.to_device(synth.history_rows(w, b, int(n)), device)
+        slots = synth.slots_for(pg.block_table[b], np.arange(int(n)), s.block_size).astype(np.int64)
+        flat[torch.from_numpy(slots).to(device)] = rows
+    x = torch_io.to_device(synth.make_x(w, w.B, "x.decode"), device)
+    pos = ctx.astype(np.int64) - 1
+    cos, sin = mla.rope_cos_sin(pos, s.qk_rope, device=device)
+    slot = torch.from_numpy(synth.decode_slot_mapping(pg)).to(device)
+    bt = torch.from_numpy(pg.block_table).to(device)
+    cl = torch.from_numpy(ctx).to(device)
+    q = torch.empty((w.B, s.n_heads, s.qk_head), dtype=torch.bfloat16, device=device)
+    o = torch.empty((w.B, s.n_heads, s.v_dim), dtype=torch.bfloat16, device=device)
+    y = torch.empty((w.B, s.hidden), dtype=torch.bfloat16, device=device)
+    max_ctx = pg.block_table.shape[1] * s.block_size
+    ws = {
+        "qkv": mla.workspace(cfg, 2, w.B),
+        "attn": mla.workspace(cfg, 3, w.B, max_ctx),
+        "out": mla.workspace(cfg, 4, w.B),
+    }
+    return dict(mla=mla, cfg=cfg, dw=dw, host=host, ctx=ctx, pg=pg, cache=cache, x=x, cos=cos, sin=sin,
+                slot=slot, bt=bt, cl=cl, q=q, o=o, y=y, ws=ws)
+
+
+def decode_step(S, ev=None):
+    mla = S["mla"]
+    if ev:
+        ev[0].record()
+    mla.mla_decode_qkv_and_scatter(S["cfg"], S["dw"], S["x"], S["cos"], S["sin"], S["cache"], S["slot"], S["q"],
+                                   ws=S["ws"]["qkv"])
+    if ev:
+        ev[1].record()
+    mla.mla_decode_attn_absorbed(S["cfg"], S["dw"], S["q"], S["cache"], S["bt"], S["cl"], S["o"],
+                                 ws=S["ws"]["attn"])
+    if ev:
+        ev[2].record()
+    mla.mla_out_proj(S["cfg"], S["dw"], S["o"], S["y"], ws=S["ws"]["out"])
+    if ev:
+        ev[3].record()
+
+
+def weight_bytes(s, names):
+    import synth
+    shapes = synth.weight_shapes(s)
+    per = 1 if s.weight == "fp8" else (2 if s.weight == "bf16" else 4)
+    total = 0
+    for n in names:
+        if n not in shapes:
+            continue
+        K, N = shapes[n]
+        total += K * N * per
+        if s.weight == "fp8":
+            total += 4 * (-(-K // 128)) * (-(-N // 128))
+    return total
+
+
+def attn_algorithmic_bytes(s, ctx, B):
+    """Absorbed decode attention: each cache row once, W_UK and W_UV once, q in, o out."""
+    act = 2 if s.act == "bf16" else 4
+    wb = 1 if s.weight == "fp8" else act
+    cache = int(ctx.sum()) * s.row * act
+    w_ukuv = s.kv_lora_rank * s.n_heads * (s.qk_nope + s.v_dim) * wb
+    if s.weight == "fp8":
+        w_ukuv += 4 * (-(-s.kv_lora_rank // 128)) * (-(-s.n_heads * (s.qk_nope + s.v_dim) // 128))
+    io = B * s.n_heads * (s.qk_head + s.v_dim) * act
+    return cache, cache + w_ukuv + io
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "head_latent_attention_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(name, launches_per_step=1):
+    """HBM bytes per launch from committed FETCH_SIZE / WRITE_SIZE counter runs, or None
+    when the kernels changed since the counters were taken."""
+    p = os.path.join(PROFILES, f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_prefill(w, reps):
+    import torch
+    import synth
+    from synth import torch_io
+    import head_latent_attention_amd as mla
+    s, T = w.shape, w.T
+    host = synth.make_weights(w)
+    dw = mla.Weights({k: torch_io.to_device(v) for k, v in host.items()},
+                     {k: torch_io.scale_to_device(v) for k, v in host.items() if v.scale is not None})
+    cfg = mla.config(s.hidden, s.n_heads, s.q_lora_rank, s.kv_lora_rank, s.qk_nope, s.qk_rope, s.v_dim,
+                     act=s.act, weight=s.weight, block_size=s.block_size)
+    x = torch_io.to_device(synth.make_x(w, T))
+    cos, sin = mla.rope_cos_sin(np.arange(T), s.qk_rope)
+    n_blocks = -(-T // s.block_size)
+    perm = synth.shuffled_blocks(w.number, "blocks", n_blocks)
+    slots = torch.from_numpy(synth.slots_for(perm, np.arange(T), s.block_size)).cuda()
+    cache = torch.empty((n_blocks, 1, s.block_size, s.row), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((T, s.n_heads, s.qk_head), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((T, s.n_heads, s.v_dim), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(v)
+    y = torch.empty((T, s.hidden), dtype=torch.bfloat16, device="cuda")
+    ws_q, ws_a, ws_o = mla.workspace(cfg, 0, T), mla.workspace(cfg, 1, T), mla.workspace(cfg, 4, T)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def once(rec):
+        if rec:
+            ev[0].record()
+        mla.mla_qkv_prefill(cfg, dw, x, cos, sin, q, k, v, cache, slots, ws=ws_q)
+        if rec:
+            ev[1].record()
+        mla.mla_prefill_attn(cfg, q, k, v, o, ws=ws_a)
+        if rec:
+            ev[2].record()
+        mla.mla_out_proj(cfg, dw, o, y, ws=ws_o)
+        if rec:
+            ev[3].record()
+
+    once(False)
+    torch.cuda.synchronize()
+    tq = ta = to = 0.0
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        once(True)
+        torch.cuda.synchronize()
+        tq += ev[0].elapsed_time(ev[1])
+        ta += ev[1].elapsed_time(ev[2])
+        to += ev[2].elapsed_time(ev[3])
+    wall = (time.perf_counter() - t0) / reps
+    D, H, Lq, Lkv, dn, dr, dv = s.hidden, s.n_heads, s.q_lora_rank, s.kv_lora_rank, s.qk_nope, s.qk_rope, s.v_dim
+    pairs = T * (T + 1) // 2
+    f_qkv = 2 * T * D * (Lq + Lkv + dr) + 2 * T * Lq * H * (dn + dr) + 2 * T * Lkv * H * (dn + dv)
+    f_attn = 2 * pairs * H * (dn + dr + dv)
+    f_out = 2 * T * H * dv * D
+    tq, ta, to = tq / reps, ta / reps, to / reps
+    return dict(tflops=(f_qkv + f_attn + f_out) / ((tq + ta + to) * 1e-3) / 1e12,
+                attn_tflops=f_attn / (ta * 1e-3) / 1e12, ms=tq + ta + to, ms_qkv=tq, ms_attn=ta, ms_out=to,
+                wall_ms=wall * 1e3, flops=f_qkv + f_attn + f_out)
+
+
+def cpu_baseline(w, S, budget_s=12.0):
+    """The float64 oracle on a bounded sample of the same decode batch."""
+    from threadpoolctl import threadpool_info
+    import synth
+    from oracle import mla_oracle as O
+    s = w.shape
+    W = O.decode_weights(S["host"])
+    dims = O.dims_of(s)
+    ctx = S["ctx"]
+    x64 = O.decode_tensor(s.act, synth.make_x(w, w.B, "x.decode").data)
+    order = np.random.default_rng(0).permutation(w.B)
+    done, rows_done = [], 0
+    t0 = time.perf_counter()
+    for b in order:
+        hist = O.decode_tensor(s.act, synth.history_rows(w, int(b), int(ctx[b]) - 1).data)
+        O.mla_decode(W, x64[b:b + 1], [hist], dims)
+        done.append(int(b))
+        rows_done += int(ctx[b])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    t_full = el * float(ctx.sum()) / rows_done
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(w.B / t_full, 3), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} of {w.B} sequences ({rows_done} of {int(ctx.sum())} cached rows), "
+                      f"{el:.1f} s of float64 numpy; time scaled by total rows to the full batch"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+                                   "not an implemented path", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import synth
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+    w = synth.WORKLOADS[3]
+    s = w.shape
+    log(f"[bench] setting up {w.name}")
+    S = decode_setup(w)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        decode_step(S)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} decode steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        decode_step(S, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_qkv = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    t_attn = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    t_out = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    ms_step = wall * 1e3 / args.steps
+    cache_b, attn_b = attn_algorithmic_bytes(s, S["ctx"], w.B)
+    step_bytes = attn_b + weight_bytes(s, ["wq_a", "wkv_a", "wq_b", "wo"])
+    achieved = attn_b / (t_attn * 1e-3) / 1e9
+    traffic = traffic_from_profiles("decode_attn")
+    out = {
+        "metric": "decode tok/s (V3-shaped MLA layer, B=64)",
+        "value": round(w.B / (ms_step * 1e-3), 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init weights N(0,0.02); cache rows c~N(0,1), k_pe~N(0,1.7^2))",
+        "config": {"workload": "v3-decode-b64: DeepSeek-V3-shaped MLA decode step, bf16, B=64, "
+                               "ctx~U[1024,8192], paged cache block_size 64",
+                   "batch": w.B, "context_tokens": int(S["ctx"].sum()), "hidden": s.hidden, "heads": s.n_heads,
+                   "q_lora_rank": s.q_lora_rank, "kv_lora_rank": s.kv_lora_rank, "qk_nope": s.qk_nope,
+                   "qk_rope": s.qk_rope, "v_dim": s.v_dim, "block_size": s.block_size},
+        "ms_decode_qkv": round(float(t_qkv), 4),
+        "ms_decode_attn": round(float(t_attn), 4),
+        "ms_out_proj": round(float(t_out), 4),
+        "latent_cache_GBps": round(cache_b / (t_attn * 1e-3) / 1e9, 1),
+        "step_algorithmic_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "mla_decode_attn_absorbed", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": attn_b},
+    }
+    if not args.no_prefill:
+        log("[bench] V3 prefill, T=8192")
+        pf = run_prefill(synth.WORKLOADS[4], args.prefill_reps)
+        out["prefill_TFLOPs"] = round(pf["tflops"], 2)
+        out["prefill"] = {"workload": "v3-prefill-8192", "ms": round(pf["ms"], 3),
+                          "ms_qkv": round(pf["ms_qkv"], 3), "ms_attn": round(pf["ms_attn"], 3),
+                          "ms_out_proj": round(pf["ms_out"], 3), "attn_TFLOPs": round(pf["attn_tflops"], 2),
+                          "frac_bf16_peak": round(pf["tflops"] / BF16_PEAK_TFLOPS, 4),
+                          "causal_counted_flops": pf["flops"]}
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(w, S)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
