@@ -1,0 +1,530 @@
+// Absorbed MLA decode attention on CDNA4 matrix cores (gfx950), for the
+// DeepSeek-V2/V3 head geometry: 128 heads, kv_lora 512, qk_rope 64, qk_nope 128,
+// v_dim 128, bf16 activations and cache, bf16 or block-scaled E4M3FN weights.
+//
+// Three kernels plus a one-block planner:
+//   plan     prefix sums of 64-token tiles over the batch (the work list).
+//   fold     q_lat[b,h] = q_nope[b,h] @ W_UK[h], W_UK read straight out of wkv_b
+//            (AWS NKI "MLA Decode QKV Kernel API Reference": the query is absorbed
+//            into the cache's latent space; atlas "Struct MlaWeights": w_uk_t).
+//   attn     split-context attention: the concatenated tile list is cut into 256
+//            equal shares, one workgroup each.  A workgroup streams its rows of
+//            [c_kv | k_pe] (576 bf16) into LDS once (direct global->LDS copies,
+//            double buffered) for all 128 heads and keeps an unnormalised latent
+//            output, running max and sum per head.
+//   combine  log-sum-exp merge of the shares of each sequence, then the value
+//            extraction o = o_lat @ W_UV[h] (atlas "Struct MlaWeights": w_uv).
+//
+// Matrix-core layout of the attention (8 waves, 16 heads each):
+//   S^T = K Q^T with tokens as the M dimension (A operand read from LDS with
+//   ds_read_b128) and heads as N (Q^T held in registers for the whole segment).
+//   The S^T accumulator already has the lane layout of the B operand of
+//   O^T = V^T P^T, so probabilities go from the softmax straight into the PV
+//   matrix op; V^T comes from the same row-major LDS tile with the gfx950
+//   transposing read ds_read_b64_tr_b16.  Rows are XOR-swizzled in 16-byte
+//   chunks so both read patterns are bank-conflict free.
+#include "mla_fast.h"
+
+namespace mla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int kH = 128, kLkv = 512, kDr = 64, kR = 576, kDn = 128, kDv = 128;
+constexpr int kChunks = kR / 8;   // 16-byte chunks per cache row
+constexpr int kTile = 64;         // tokens per work-list tile
+constexpr int kAttnWGs = 256;     // workgroups of the attention kernel (one per CU on MI355X)
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^(s - m) <= 256 between rescales
+
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Eight consecutive weight elements (k fixed, n..n+7) as bf16; fp8 codes are
+// converted exactly (E4M3FN value times a power-of-two block scale).
+template <int WK>
+__device__ __forceinline__ uint4 load_w8(const WeightView& W, int64_t k, int64_t n) {
+  if constexpr (WK == W_BF16) {
+    return *(const uint4*)((const bf16_t*)W.w + k * W.ld + n);
+  } else {
+    const uint2 raw = *(const uint2*)((const uint8_t*)W.w + k * W.ld + n);
+    const float s = W.scale[(k >> 7) * W.scale_ld + (n >> 7)];
+    uint32_t out[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t word = h ? raw.y : raw.x;
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+      out[2 * h] = pack_bf16x2(lo[0] * s, lo[1] * s);
+      out[2 * h + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+  }
+}
+
+// ------------------------------------------------------------------------------ plan
+// P[b] = number of 64-token tiles of sequences 0..b-1; P[B] = total.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ ctx, int B, int32_t* __restrict__ P,
+                                                    bf16_t* __restrict__ zero_row) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  if (tid < kR) zero_row[tid] = 0;
+  const int per = (B + 1023) / 1024;
+  const int lo = min(B, tid * per), hi = min(B, lo + per);
+  int s = 0;
+  for (int b = lo; b < hi; ++b) {
+    const int c = ctx[b];
+    s += c > 0 ? (c + kTile - 1) / kTile : 0;
+  }
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int base = tid ? part[tid - 1] : 0;
+  for (int b = lo; b < hi; ++b) {
+    P[b] = base;
+    const int c = ctx[b];
+    base += c > 0 ? (c + kTile - 1) / kTile : 0;
+  }
+  if (tid == 1023) P[B] = part[1023];
+}
+
+// ------------------------------------------------------------------------------ fold
+// Qabs[b][h] = [q_nope[b][h] @ W_UK[h] | q_pe[b][h]] in bf16, W_UK[h][p][c] = wkv_b[c][h*256 + p].
+// Grid (H, ceil(B/64)); wave w computes latent columns [128w, 128w + 128) for 64 rows.
+template <int WK>
+__global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q, int B, WeightView W,
+                                                   bf16_t* __restrict__ Qabs) {
+  const int h = blockIdx.x, b0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int qs = kH * (kDn + kDr);
+#pragma unroll
+  for (int ks = 0; ks < kDn / 32; ++ks) {
+    bf16x8 a[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int b = b0 + 16 * mt + j;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (b < B) v = *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + 32 * ks + 8 * g);
+      a[mt] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int c = 128 * w + 16 * nt + j;
+      const bf16x8 bop = as_bf16x8(load_w8<WK>(W, c, (int64_t)h * (kDn + kDv) + 32 * ks + 8 * g));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], bop, acc[mt][nt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = b0 + 16 * mt + 4 * g + i;
+      if (b >= B) continue;
+      bf16_t* dst = Qabs + ((size_t)b * kH + h) * kR;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) dst[128 * w + 16 * nt + j] = f32_to_bf16(acc[mt][nt][i]);
+    }
+  // rope part of the query is carried over unchanged
+  for (int e = tid; e < 64 * kDr; e += 256) {
+    const int r = e / kDr, d = e - r * kDr, b = b0 + r;
+    if (b < B) Qabs[((size_t)b * kH + h) * kR + kLkv + d] = q[(size_t)b * qs + h * (kDn + kDr) + kDn + d];
+  }
+}
+
+// ------------------------------------------------------------------------------ attention
+// LDS tile of 64 tokens: region C holds the 512 latent values of each token as
+// 64 chunks of 16 bytes (token t, chunk c at slot 64*t + (c ^ swz_c(t))), region
+// PE the 64 rope values as 8 chunks (slot 8*t + (c ^ swz_pe(t))).  swz_c is a
+// bijection of the token's low 4 bits chosen so that both the 16-token reads of
+// the score operand and the 4-token transposing reads of the value operand hit
+// 16 distinct 16-byte bank groups.
+constexpr int kCSlots = kTile * 64, kPeSlots = kTile * 8, kBufSlots = kCSlots + kPeSlots;
+
+__device__ __forceinline__ int swz_c(int t) {
+  return ((t >> 2) & 1) | ((t & 1) << 1) | (((t >> 1) & 1) << 2) | (((t >> 3) & 1) << 3);
+}
+__device__ __forceinline__ int swz_pe(int t) { return (t >> 1) & 7; }
+
+struct AttnArgs {
+  const bf16_t* Qabs;
+  const bf16_t* cache;
+  const bf16_t* zero_row;  // kR zeros: source of rows past the context or with an invalid block id
+  int64_t n_blocks;
+  int bs;
+  const int32_t* bt;
+  int max_blocks;
+  const int32_t* ctx;
+  const int32_t* P;
+  int B;
+  float scale_log2;
+  float* part_o;   // [(G + B)][H][Lkv]
+  float* part_ml;  // [(G + B)][H][2]   (running max in log2 units, sum)
+};
+
+// Wave-uniform load through the scalar cache (the value is read-only for the kernel's lifetime).
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// Row of token `tok` of sequence b (wave-uniform), or the zero row.
+__device__ __forceinline__ const bf16_t* row_ptr(const AttnArgs& A, int b, int tok, int tok_hi) {
+  if (tok < tok_hi) {
+    const int lb = tok / A.bs;
+    if (lb < A.max_blocks) {
+      const int blk = sload(A.bt + (size_t)b * A.max_blocks + lb);
+      if (blk >= 0 && blk < A.n_blocks) return A.cache + ((int64_t)blk * A.bs + (tok - lb * A.bs)) * kR;
+    }
+  }
+  return A.zero_row;
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Direct global->LDS copies of one 64-token tile: wave w copies tokens [8w, 8w + 8):
+// one 64-lane copy per token for its latent part and one copy for the 8 tokens' rope parts.
+// All row addresses are resolved (scalar loads of the block table) before the first copy
+// is issued, so the copies are in flight together.
+__device__ __forceinline__ void issue_tile_copy(const AttnArgs& A, int b, int tok0, int tok_hi,
+                                                uint4* __restrict__ buf, int w, int lane) {
+  const bf16_t* rows[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rows[i] = row_ptr(A, b, tok0 + 8 * w + i, tok_hi);
+  // The lane index is made opaque so the per-copy offsets are recomputed here
+  // (one XOR each) instead of being hoisted into long-lived registers.
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  const int tp = l >> 3;
+  const bf16_t* prow = rows[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) prow = tp == i ? rows[i] : prow;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = 8 * w + i;
+    dma16(rows[i] + 8 * (l ^ swz_c(t)), buf + 64 * t);
+  }
+  dma16(prow + kLkv + 8 * ((l & 7) ^ swz_pe(8 * w + tp)), buf + kCSlots + 64 * w);
+}
+
+// One 64-token tile: prefetch the next tile into `nxt`, scores, online softmax, PV.
+// `buf` and `nxt` are restrict-qualified: once inlined, the copies into `nxt` carry
+// alias scopes disjoint from the reads of `buf`, so the compiler does not make those
+// reads wait for the copies and the prefetch stays in flight during the compute.
+__device__ __forceinline__ void attn_tile(const AttnArgs& A, int b, int tok0, int tok_hi,
+                                          const uint4* __restrict__ buf, uint4* __restrict__ nxt,
+                                          const bf16x8 (&qf)[kR / 32], f32x4 (&o)[kLkv / 16], float& m_run,
+                                          float& l_run, const int (&sbase)[4], const int (&pbase)[2],
+                                          const int (&tbase)[8], int w, int lane, int g) {
+  if (tok0 + kTile < tok_hi) issue_tile_copy(A, b, tok0 + kTile, tok_hi, nxt, w, lane);
+  const char* bbase = (const char*)buf;
+  // ---- scores S^T[token][head], 4 token tiles of 16; k-steps 0..15 latent, 16..17 rope
+  f32x4 s[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kR / 32; ++ks) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const char* pa = ks < 16 ? bbase + sbase[ks & 3] + (16 * mt * 64 + 16 * (ks >> 2)) * 16
+                               : bbase + pbase[ks - 16] + (16 * mt * 8) * 16;
+      const bf16x8 a = as_bf16x8(*(const uint4*)pa);
+      s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[mt], 0, 0, 0);
+    }
+  }
+  // ---- online softmax (log2 domain); this lane's head is `head`
+  float x[4][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok0 + 16 * mt + 4 * g + i;
+      x[mt][i] = tok < tok_hi ? s[mt][i] * A.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[mt][i]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = (m_run == -INFINITY || mx > m_run + kRescaleThreshold) ? mx : m_run;
+  const float corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+  float sum = 0.f;
+  bf16x8 pb[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2f(x[2 * kk][i] - m_new);
+      p[4 + i] = exp2f(x[2 * kk + 1][i] - m_new);
+      sum += p[i] + p[4 + i];
+    }
+    pb[kk] = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                  pack_bf16x2(p[6], p[7])));
+  }
+  sum += __shfl_xor(sum, 16, 64);
+  sum += __shfl_xor(sum, 32, 64);
+  l_run = l_run * corr + sum;
+  m_run = m_new;
+  if (__any(corr != 1.f)) {
+#pragma unroll
+    for (int mt = 0; mt < kLkv / 16; ++mt) o[mt] *= corr;
+  }
+  // ---- O^T[latent][head] += V^T P^T, two k-steps of 32 tokens
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int mt = 0; mt < kLkv / 16; ++mt) {
+      const char* pa = bbase + tbase[mt & 7] + (32 * kk * 64 + 16 * (mt >> 3)) * 16;
+      const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
+      const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + 16 * 64 * 16));
+      const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kk], o[mt], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// 512 threads = 8 waves; wave w owns heads [16w, 16w + 16).
+__global__ __launch_bounds__(512, 1) void decode_attn_kernel(AttnArgs A) {
+  __shared__ __attribute__((aligned(16))) uint4 kv[2][kBufSlots];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = sload(A.P + A.B);
+  const int wg = blockIdx.x;
+  const int t_lo = (int)((int64_t)wg * N / kAttnWGs), t_hi = (int)((int64_t)(wg + 1) * N / kAttnWGs);
+  if (t_lo >= t_hi) return;
+  // sequence holding tile t_lo: the largest b with P[b] <= t_lo
+  int lo = 0, hi = A.B;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sload(A.P + mid) <= t_lo) lo = mid;
+    else hi = mid - 1;
+  }
+  int b = lo;
+  int tile = t_lo;
+  const int head = 16 * w + j;
+  // Lane-dependent byte offsets inside a tile buffer; every LDS address below is
+  // one of these plus a compile-time offset.  Token 16*mt + j has the swizzle
+  // of j; token 32*kk + {0,16} + 4*g + j/4 has the swizzle of 4*g + j/4.
+  int sbase[4], pbase[2], tbase[8];
+  {
+    const int sj = swz_c(j), pj = swz_pe(j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sbase[e] = (64 * j + ((4 * e + g) ^ sj)) * 16;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) pbase[e] = (kCSlots + 8 * j + ((4 * e + g) ^ pj)) * 16;
+    const int tA = 4 * g + (j >> 2), sA = swz_c(tA), half = (j >> 1) & 1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) tbase[q] = (64 * tA + ((2 * q + half) ^ sA)) * 16 + (j & 1) * 8;
+  }
+  while (tile < t_hi) {
+    while (sload(A.P + b + 1) <= tile) ++b;
+    const int pb0 = sload(A.P + b);
+    const int seg_end = min(t_hi, sload(A.P + b + 1));
+    const int tok_lo = (tile - pb0) * kTile;
+    const int tok_hi = min(sload(A.ctx + b), (seg_end - pb0) * kTile);
+    tile = seg_end;
+
+    issue_tile_copy(A, b, tok_lo, tok_hi, kv[0], w, lane);
+    // Q^T fragments of this wave's 16 heads (B operand of S^T = K Q^T)
+    bf16x8 qf[kR / 32];
+    {
+      const bf16_t* qrow = A.Qabs + ((size_t)b * kH + head) * kR + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < kR / 32; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qrow + 32 * ks));
+    }
+    f32x4 o[kLkv / 16];
+#pragma unroll
+    for (int mt = 0; mt < kLkv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int cur = 0;
+    for (int tok0 = tok_lo; tok0 < tok_hi; tok0 += kTile) {
+      attn_tile(A, b, tok0, tok_hi, kv[cur], kv[cur ^ 1], qf, o, m_run, l_run, sbase, pbase, tbase, w, lane, g);
+      cur ^= 1;
+    }
+    // ---- partial result of (this workgroup, sequence b)
+    const size_t ps = (size_t)wg + b;
+    float* dst = A.part_o + (ps * kH + head) * kLkv + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < kLkv / 16; ++mt) *(f32x4*)(dst + 16 * mt) = o[mt];
+    if (g == 0) {
+      A.part_ml[(ps * kH + head) * 2] = m_run;
+      A.part_ml[(ps * kH + head) * 2 + 1] = l_run;
+    }
+  }
+}
+
+// Work-list share of attention workgroup w: tiles [w*N/G, (w+1)*N/G).
+__device__ __forceinline__ bool wg_nonempty(int w, int N) {
+  return (int64_t)w * N / kAttnWGs < (int64_t)(w + 1) * N / kAttnWGs;
+}
+
+// ------------------------------------------------------------------------------ combine + W_UV
+// Grid (H, ceil(B/16)).  Merges the partials of 16 sequences for one head, then
+// o[b][h] = o_lat[b][h] @ W_UV[h] on the matrix cores (W_UV[h][c][j] = wkv_b[c][h*256 + 128 + j]).
+template <int WK>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                      const int32_t* __restrict__ P, int B, WeightView W,
+                                                      bf16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[16][kLkv + 8];
+  __shared__ __attribute__((aligned(16))) bf16_t Ws[128][kDv + 16];
+  const int h = blockIdx.x, b0 = blockIdx.y * 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
+  const int N = P[B];
+  // ---- merge: wave w handles local rows 4w..4w+3, each lane 8 latent columns
+  for (int r = 0; r < 4; ++r) {
+    const int lb = 4 * w + r, b = b0 + lb;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (b < B && P[b + 1] > P[b]) {
+      const int wf = (int)(((int64_t)(P[b] + 1) * kAttnWGs - 1) / N);
+      const int wl = (int)(((int64_t)P[b + 1] * kAttnWGs - 1) / N);
+      float M = -INFINITY;
+      for (int wq = wf; wq <= wl; ++wq)
+        if (wg_nonempty(wq, N)) M = fmaxf(M, part_ml[(((size_t)wq + b) * kH + h) * 2]);
+      float L = 0.f;
+      for (int wq = wf; wq <= wl; ++wq) {
+        if (!wg_nonempty(wq, N)) continue;
+        const float* ml = part_ml + (((size_t)wq + b) * kH + h) * 2;
+        const float f = exp2f(ml[0] - M);
+        L += f * ml[1];
+        const float* src = part_o + (((size_t)wq + b) * kH + h) * kLkv + 8 * lane;
+        const f32x4 v0 = *(const f32x4*)src, v1 = *(const f32x4*)(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += f * v0[e];
+          acc[4 + e] += f * v1[e];
+        }
+      }
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    }
+    *(uint4*)&As[lb][8 * lane] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                           pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  }
+  // ---- o[16 x 128] = As[16 x 512] @ W_UV[512 x 128]; wave w owns columns [32w, 32w + 32)
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const int64_t col0 = (int64_t)h * (kDn + kDv) + kDn;
+  for (int cc = 0; cc < kLkv / 128; ++cc) {
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
+      *(uint4*)&Ws[r][8 * ch] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = as_bf16x8(*(const uint4*)&As[j][128 * cc + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int col = 32 * w + 16 * nt + 4 * (j & 3);
+        const int row = 32 * ks + 8 * g + (j >> 2);
+        const bf16x4 b0v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&Ws[row][col]);
+        const bf16x4 b1v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&Ws[row + 4][col]);
+        const bf16x8 bop = __builtin_shufflevector(b0v, b1v, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop, acc[nt], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = b0 + 4 * g + i;
+      if (b < B) out[((size_t)b * kH + h) * kDv + 32 * w + 16 * nt + j] = f32_to_bf16(acc[nt][i]);
+    }
+}
+
+struct DecodeLayout {
+  bf16_t* Qabs;
+  int32_t* P;
+  bf16_t* zero_row;
+  float* part_o;
+  float* part_ml;
+  size_t bytes;
+};
+
+size_t al(size_t v) { return (v + 255) / 256 * 256; }
+
+DecodeLayout layout(int B, void* base) {
+  DecodeLayout L;
+  char* p = (char*)base;
+  size_t off = 0;
+  L.Qabs = (bf16_t*)(p + off);
+  off += al((size_t)B * kH * kR * sizeof(bf16_t));
+  L.P = (int32_t*)(p + off);
+  off += al((size_t)(B + 1) * sizeof(int32_t));
+  L.zero_row = (bf16_t*)(p + off);
+  off += al((size_t)kR * sizeof(bf16_t));
+  L.part_o = (float*)(p + off);
+  off += al((size_t)(kAttnWGs + B) * kH * kLkv * sizeof(float));
+  L.part_ml = (float*)(p + off);
+  off += al((size_t)(kAttnWGs + B) * kH * 2 * sizeof(float));
+  L.bytes = off;
+  return L;
+}
+
+}  // namespace
+
+bool fast_decode_supported(const Dims& d) {
+  return d.act == 1 && (d.wk == W_BF16 || d.wk == W_FP8) && d.H == kH && d.Lkv == kLkv && d.dr == kDr &&
+         d.dn == kDn && d.dv == kDv;
+}
+
+size_t fast_decode_ws_bytes(const Dims& d, int B, int) { return layout(B, nullptr).bytes; }
+
+hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cache, int64_t n_blocks,
+                            const int32_t* block_table, int max_blocks, const int32_t* ctx,
+                            const WeightView& wkv_b, void* o, const FastDecodeWs& ws, hipStream_t s) {
+  const DecodeLayout L = layout(B, ws.base);
+  plan_kernel<<<1, 1024, 0, s>>>(ctx, B, L.P, L.zero_row);
+  dim3 fgrid(kH, (B + 63) / 64);
+  if (d.wk == W_BF16) fold_kernel<W_BF16><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs);
+  else fold_kernel<W_FP8><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs);
+  AttnArgs A;
+  A.Qabs = L.Qabs;
+  A.cache = (const bf16_t*)cache;
+  A.zero_row = L.zero_row;
+  A.n_blocks = n_blocks;
+  A.bs = d.bs;
+  A.bt = block_table;
+  A.max_blocks = max_blocks;
+  A.ctx = ctx;
+  A.P = L.P;
+  A.B = B;
+  A.scale_log2 = d.scale * 1.4426950408889634f;
+  A.part_o = L.part_o;
+  A.part_ml = L.part_ml;
+  decode_attn_kernel<<<kAttnWGs, 512, 0, s>>>(A);
+  dim3 cgrid(kH, (B + 15) / 16);
+  if (d.wk == W_BF16) combine_kernel<W_BF16><<<cgrid, 256, 0, s>>>(L.part_o, L.part_ml, L.P, B, wkv_b, (bf16_t*)o);
+  else combine_kernel<W_FP8><<<cgrid, 256, 0, s>>>(L.part_o, L.part_ml, L.P, B, wkv_b, (bf16_t*)o);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -8,12 +8,6 @@ hipError_t fast_gemm(const Dims&, const void*, int64_t, const WeightView&, float
                      hipStream_t) {
   return hipErrorInvalidValue;
 }
-bool fast_decode_supported(const Dims&) { return false; }
-size_t fast_decode_ws_bytes(const Dims&, int, int) { return 0; }
-hipError_t fast_decode_attn(const Dims&, const void*, int, const void*, int64_t, const int32_t*, int,
-                            const int32_t*, const WeightView&, void*, const FastDecodeWs&, hipStream_t) {
-  return hipErrorInvalidValue;
-}
 bool fast_prefill_attn_supported(const Dims&) { return false; }
 size_t fast_prefill_attn_ws_bytes(const Dims&, int) { return 0; }
 hipError_t fast_prefill_attn(const Dims&, const void*, const void*, const void*, int, void*, void*,
