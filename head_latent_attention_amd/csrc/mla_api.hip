@@ -2,6 +2,7 @@
 // dispatch.  Nothing here synchronises the host or allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstdio>
@@ -83,7 +84,17 @@ struct QkvWs {
   void* cqn;     // [n, Lq]       RMSNorm(q latent) * gamma (act)
   void* cn;      // [n, Lkv]      RMSNorm(c_kv) * gamma (act), prefill only
   float* KVraw;  // [n, H*(dn+dv)] prefill only
+  void* gscratch;  // split-K partial sums of the projection GEMMs
 };
+
+size_t gemm_scratch(const Dims& d, int n, bool prefill) {
+  if (!fast_proj_supported(d)) return 0;
+  const int HQ = d.H * d.dqk();
+  size_t s = std::max(fast_gemm_ws_bytes(n, d.R(), d.D), fast_gemm_ws_bytes(n, HQ, d.Lq > 0 ? d.Lq : d.D));
+  if (d.Lq > 0) s = std::max(s, fast_gemm_ws_bytes(n, d.Lq, d.D));
+  if (prefill) s = std::max(s, fast_gemm_ws_bytes(n, d.H * (d.dn + d.dv), d.Lkv));
+  return s;
+}
 
 size_t qkv_ws(const Dims& d, int n, bool prefill, void* base, QkvWs* out) {
   Carver c(base);
@@ -93,6 +104,7 @@ size_t qkv_ws(const Dims& d, int n, bool prefill, void* base, QkvWs* out) {
   w.cqn = c.take<char>((size_t)n * (d.Lq > 0 ? d.Lq : 1) * act_bytes(d));
   w.cn = prefill ? c.take<char>((size_t)n * d.Lkv * act_bytes(d)) : nullptr;
   w.KVraw = prefill ? c.take<float>((size_t)n * d.H * (d.dn + d.dv)) : nullptr;
+  w.gscratch = c.take<char>(gemm_scratch(d, n, prefill));
   if (out) *out = w;
   return c.used;
 }
@@ -133,10 +145,12 @@ size_t decode_attn_ws(const Dims& d, int B, int max_context, void* base, DecodeA
   return c.used;
 }
 
-size_t out_proj_ws(const Dims& d, int M, void* base, float** Y) {
+size_t out_proj_ws(const Dims& d, int M, void* base, float** Y, void** scratch) {
   Carver c(base);
   float* y = c.take<float>((size_t)M * d.D);
+  void* sc = c.take<char>(fast_proj_supported(d) ? fast_gemm_ws_bytes(M, d.D, d.H * d.dv) : 0);
   if (Y) *Y = y;
+  if (scratch) *scratch = sc;
   return c.used;
 }
 
@@ -163,11 +177,11 @@ mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, 
   const int HQ = d.H * d.dqk();
   if (fast_proj_supported(d)) {
     if (d.Lq > 0) {
-      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wq_a, d.Lq), ws.Y1, ldy, n, d.Lq, d.D, s));
-      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1 + d.Lq, ldy, n, d.R(), d.D, s));
+      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wq_a, d.Lq), ws.Y1, ldy, n, d.Lq, d.D, ws.gscratch, s));
+      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1 + d.Lq, ldy, n, d.R(), d.D, ws.gscratch, s));
     } else {
-      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.D, s));
-      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1, ldy, n, d.R(), d.D, s));
+      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.D, ws.gscratch, s));
+      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1, ldy, n, d.R(), d.D, ws.gscratch, s));
     }
   } else {
     if (d.Lq > 0) {
@@ -182,7 +196,7 @@ mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, 
                       ws.cn, kv_cache, n_slots, slot_mapping, kbuf, s));
   if (d.Lq > 0) {
     if (fast_proj_supported(d))
-      HIP_TRY(fast_gemm(d, ws.cqn, d.Lq, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.Lq, s));
+      HIP_TRY(fast_gemm(d, ws.cqn, d.Lq, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.Lq, ws.gscratch, s));
     else
       HIP_TRY(gemm_simt(d, ws.cqn, d.Lq, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.Lq, s));
   }
@@ -221,7 +235,7 @@ size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t 
     case MLA_FN_DECODE_ATTN:
       if (max_context <= 0) return 0;
       return decode_attn_ws(d, n, max_context, nullptr, nullptr);
-    case MLA_FN_OUT_PROJ: return out_proj_ws(d, n, nullptr, nullptr);
+    case MLA_FN_OUT_PROJ: return out_proj_ws(d, n, nullptr, nullptr, nullptr);
   }
   return 0;
 }
@@ -245,7 +259,7 @@ mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const vo
   if (st != MLA_OK) return st;
   const int NKV = d.H * (d.dn + d.dv);
   if (fast_proj_supported(d))
-    HIP_TRY(fast_gemm(d, L.cn, d.Lkv, view(d, w->wkv_b, NKV), L.KVraw, NKV, T, NKV, d.Lkv, s));
+    HIP_TRY(fast_gemm(d, L.cn, d.Lkv, view(d, w->wkv_b, NKV), L.KVraw, NKV, T, NKV, d.Lkv, L.gscratch, s));
   else
     HIP_TRY(gemm_simt(d, L.cn, d.Lkv, view(d, w->wkv_b, NKV), L.KVraw, NKV, T, NKV, d.Lkv, s));
   HIP_TRY(kv_split(d, L.KVraw, T, k, v, s));
@@ -322,12 +336,13 @@ mla_status mla_out_proj(const mla_config* cfg, const mla_weights* w, const void*
   if (st != MLA_OK) return st;
   if (M <= 0 || !w || !o || !y || !check_weight(d, w->wo)) return MLA_ERR_INVALID_ARG;
   float* Y = nullptr;
-  const size_t need = out_proj_ws(d, M, ws, &Y);
+  void* scratch = nullptr;
+  const size_t need = out_proj_ws(d, M, ws, &Y, &scratch);
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int K = d.H * d.dv;
   if (fast_proj_supported(d))
-    HIP_TRY(fast_gemm(d, o, K, view(d, w->wo, d.D), Y, d.D, M, d.D, K, s));
+    HIP_TRY(fast_gemm(d, o, K, view(d, w->wo, d.D), Y, d.D, M, d.D, K, scratch, s));
   else
     HIP_TRY(gemm_simt(d, o, K, view(d, w->wo, d.D), Y, d.D, M, d.D, K, s));
   HIP_TRY(cast_rows(d, Y, (int64_t)M * d.D, y, s));

@@ -11,10 +11,12 @@ struct FastDecodeWs {
   size_t bytes = 0;
 };
 
-// Projection GEMM / GEMV: C[M, N] fp32 = A[M, K] (act) @ W[K, N].
+// Projection GEMM / GEMV: C[M, N] fp32 = A[M, K] (act) @ W[K, N].  `scratch` holds
+// the split-K partial sums, fast_gemm_ws_bytes(M, N, K) bytes (0 when not split).
 bool fast_proj_supported(const Dims& d);
+size_t fast_gemm_ws_bytes(int M, int N, int K);
 hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C, int64_t ldc,
-                     int M, int N, int K, hipStream_t s);
+                     int M, int N, int K, void* scratch, hipStream_t s);
 
 // Absorbed decode: fold, split-context attention over the paged cache, combine with W_UV.
 bool fast_decode_supported(const Dims& d);

@@ -3,11 +3,6 @@
 
 namespace mla {
 
-bool fast_proj_supported(const Dims&) { return false; }
-hipError_t fast_gemm(const Dims&, const void*, int64_t, const WeightView&, float*, int64_t, int, int, int,
-                     hipStream_t) {
-  return hipErrorInvalidValue;
-}
 bool fast_prefill_attn_supported(const Dims&) { return false; }
 size_t fast_prefill_attn_ws_bytes(const Dims&, int) { return 0; }
 hipError_t fast_prefill_attn(const Dims&, const void*, const void*, const void*, int, void*, void*,

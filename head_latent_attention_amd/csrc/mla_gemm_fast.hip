@@ -1,0 +1,260 @@
+// Projection GEMM / GEMV on CDNA4 matrix cores (gfx950):
+//   C[M, N] (fp32) = A[M, K] (bf16, row-major) @ W[K, N] (bf16, or E4M3FN bytes with
+//   fp32 128x128 block scales), W in the [in, out] orientation the NKI projection
+//   kernels take.
+//
+// One workgroup (4 waves) owns a BM x 128 output tile and a K range; K advances in
+// steps of 64 through double-buffered LDS tiles loaded via registers.  A is read
+// with ds_read_b128 (row-contiguous k); W is stored row-major [k][n] and the B
+// operand (k-contiguous per lane) comes from the gfx950 transposing read
+// ds_read_b64_tr_b16.  fp8 weights are decoded to bf16 while being staged: the
+// E4M3FN value times a power-of-two block scale is exact in bf16, so the matrix
+// op sees the same numbers the block-scaled weight represents (atlas "Struct
+// MlaWeights", fp8 fields: the GEMV reads one byte per weight and dequantises in
+// the kernel).  Skinny decode shapes split K over extra workgroups; the partial
+// sums are added in a fixed order by a second kernel, so results are bitwise
+// reproducible.
+#include "mla_fast.h"
+
+namespace mla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int BK = 64;   // k per LDS stage
+constexpr int BN = 128;  // output columns per workgroup
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// A tile: [BM][64] bf16, 8 chunks of 16 B per row; chunk c of row r at slot 8r + (c ^ ((r >> 1) & 7)).
+__device__ __forceinline__ int a_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
+// W tile: [64][128] bf16, 16 chunks per row; chunk c of row k at slot 16k + (c ^ (2 * (k & 3))).
+__device__ __forceinline__ int w_slot(int k, int c) { return 16 * k + (c ^ (2 * (k & 3))); }
+
+template <int BM, int WM, int WN, int WK>
+struct Gemm {
+  static constexpr int MT = BM / WM / 16;   // 16-row tiles per wave
+  static constexpr int NT = BN / WN / 16;   // 16-col tiles per wave
+  static constexpr int A_LOADS = BM * 8 / 256;  // 16-byte chunks of A per thread
+  static constexpr int W_LOADS = 4;             // bf16 chunks of W per thread (fp8: 2 loads, 4 chunks after decode)
+  static constexpr int A_SLOTS = BM * 8, W_SLOTS = BK * 16;
+  static_assert(WM * WN == 4, "4 waves");
+};
+
+template <int BM, int WM, int WN, int WK>
+__global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda, WeightView W,
+                                                   float* __restrict__ C, int64_t ldc, int M, int N, int K,
+                                                   int k_split, int64_t split_stride) {
+  using G = Gemm<BM, WM, WN, WK>;
+  __shared__ __attribute__((aligned(16))) uint4 As[2][G::A_SLOTS];
+  __shared__ __attribute__((aligned(16))) uint4 Ws[2][G::W_SLOTS];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, j = lane & 15;
+  const int wm = wv / WN, wn = wv % WN;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int kbeg = blockIdx.z * k_split, kend = min(K, kbeg + k_split);
+  C += (int64_t)blockIdx.z * split_stride;
+
+  uint4 ra[G::A_LOADS], rw[G::W_LOADS];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < G::A_LOADS; ++it) {
+      const int e = it * 256 + tid, r = e >> 3, c = e & 7;
+      const int m = m0 + r, k = k0 + 8 * c;
+      ra[it] = (m < M && k < kend) ? *(const uint4*)(A + (int64_t)m * lda + k) : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (WK == W_BF16) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int e = it * 256 + tid, kr = e >> 4, c = e & 15;
+        const int k = k0 + kr, n = n0 + 8 * c;
+        rw[it] = (k < kend && n < N) ? *(const uint4*)((const bf16_t*)W.w + (int64_t)k * W.ld + n)
+                                     : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      // 64 x 128 bytes = 512 chunks of 16 B; thread takes 2, each becomes 2 bf16 chunks
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int e = it * 256 + tid, kr = e >> 3, c = e & 7;
+        const int k = k0 + kr, n = n0 + 16 * c;
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        float s = 0.f;
+        if (k < kend && n < N) {
+          raw = *(const uint4*)((const uint8_t*)W.w + (int64_t)k * W.ld + n);
+          s = W.scale[(k >> 7) * W.scale_ld + (n >> 7)];
+        }
+        uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t out[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[q], false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[q], true);
+          out[2 * q] = pack2(lo[0] * s, lo[1] * s);
+          out[2 * q + 1] = pack2(hi[0] * s, hi[1] * s);
+        }
+        rw[2 * it] = make_uint4(out[0], out[1], out[2], out[3]);
+        rw[2 * it + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+      }
+    }
+  };
+  auto store = [&](uint4* __restrict__ as, uint4* __restrict__ ws) {
+#pragma unroll
+    for (int it = 0; it < G::A_LOADS; ++it) {
+      const int e = it * 256 + tid;
+      as[a_slot(e >> 3, e & 7)] = ra[it];
+    }
+    if constexpr (WK == W_BF16) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int e = it * 256 + tid;
+        ws[w_slot(e >> 4, e & 15)] = rw[it];
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int e = it * 256 + tid, kr = e >> 3, c = e & 7;
+        ws[w_slot(kr, 2 * c)] = rw[2 * it];
+        ws[w_slot(kr, 2 * c + 1)] = rw[2 * it + 1];
+      }
+    }
+  };
+
+  f32x4 acc[G::MT][G::NT];
+#pragma unroll
+  for (int a = 0; a < G::MT; ++a)
+#pragma unroll
+    for (int b = 0; b < G::NT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // lane parts of the LDS addresses
+  const int arow0 = wm * (BM / WM) + j;                  // + 16*mt
+  const int wcol0 = wn * (BN / WN);                      // + 16*nt
+  if (kbeg < kend) {
+    load(kbeg);
+    store(As[0], Ws[0]);
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+    const bool next = k0 + BK < kend;
+    if (next) load(k0 + BK);
+    const uint4* as = As[cur];
+    const char* wsb = (const char*)Ws[cur];
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8 af[G::MT], bfr[G::NT];
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) af[mt] = as_bf16x8(as[a_slot(arow0 + 16 * mt, 4 * ks + g)]);
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) {
+        const int col = wcol0 + 16 * nt + 4 * (j & 3);
+        const int c = col >> 3, byte_in = (col & 7) * 2;
+        const int k = 32 * ks + 8 * g + (j >> 2);
+        const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k, c) * 16 + byte_in));
+        const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k + 4, c) * 16 + byte_in));
+        bfr[nt] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+    }
+    if (next) store(As[cur ^ 1], Ws[cur ^ 1]);
+    __syncthreads();
+    cur ^= 1;
+  }
+#pragma unroll
+  for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * (BM / WM) + 16 * mt + 4 * g + i;
+      if (m >= M) continue;
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) {
+        const int n = n0 + wcol0 + 16 * nt + j;
+        if (n < N) C[(int64_t)m * ldc + n] = acc[mt][nt][i];
+      }
+    }
+}
+
+// C[m, n] = sum_z P[z][m, n], z in fixed order.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ P, int splits, int64_t stride,
+                                                           int M, int N, float* __restrict__ C, int64_t ldc) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / N, n = i - m * N;
+    float s = 0.f;
+    for (int z = 0; z < splits; ++z) s += P[z * stride + m * N + n];
+    C[m * ldc + n] = s;
+  }
+}
+
+struct Plan {
+  int bm, splits, k_split;
+};
+
+Plan plan(int M, int N, int K) {
+  Plan p;
+  p.bm = M <= 64 ? 64 : 128;
+  const int tiles = ((N + BN - 1) / BN) * ((M + p.bm - 1) / p.bm);
+  int splits = 1;
+  // skinny shapes: spread K over more workgroups until every CU has one, keeping >= 256 k per split
+  while (tiles * splits < 256 && K / (splits * 2) >= 256) splits *= 2;
+  p.k_split = ((K + splits - 1) / splits + BK - 1) / BK * BK;
+  p.splits = (K + p.k_split - 1) / p.k_split;
+  return p;
+}
+
+template <int BM, int WM, int WN>
+hipError_t launch(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C, int64_t ldc, int M, int N,
+                  int K, int k_split, int splits, int64_t split_stride, hipStream_t s) {
+  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, splits);
+  if (d.wk == W_FP8)
+    gemm_kernel<BM, WM, WN, W_FP8><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W, C, ldc, M, N, K, k_split, split_stride);
+  else
+    gemm_kernel<BM, WM, WN, W_BF16><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W, C, ldc, M, N, K, k_split, split_stride);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fast_proj_supported(const Dims& d) {
+  // every K and N is a multiple of the 16-byte load width (16 columns for fp8 bytes)
+  const int q = d.wk == W_FP8 ? 16 : 8;
+  return d.act == 1 && (d.wk == W_BF16 || d.wk == W_FP8) && d.D % q == 0 && d.Lq % q == 0 && d.Lkv % 8 == 0 &&
+         (d.Lkv + d.dr) % q == 0 && (d.H * (d.dn + d.dr)) % q == 0 && (d.H * (d.dn + d.dv)) % q == 0 &&
+         (d.H * d.dv) % 8 == 0;
+}
+
+size_t fast_gemm_ws_bytes(int M, int N, int K) {
+  const Plan p = plan(M, N, K);
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+}
+
+hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C, int64_t ldc, int M,
+                     int N, int K, void* scratch, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  const Plan p = plan(M, N, K);
+  float* out = C;
+  int64_t ld = ldc, stride = 0;
+  if (p.splits > 1) {
+    out = (float*)scratch;
+    ld = N;
+    stride = (int64_t)M * N;
+  }
+  hipError_t e = p.bm == 64 ? launch<64, 1, 4>(d, A, lda, W, out, ld, M, N, K, p.k_split, p.splits, stride, s)
+                            : launch<128, 2, 2>(d, A, lda, W, out, ld, M, N, K, p.k_split, p.splits, stride, s);
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t total = (int64_t)M * N;
+  const int grid = (int)std::min<int64_t>((total + 255) / 256, 2048);
+  split_reduce_kernel<<<grid, 256, 0, s>>>(out, p.splits, stride, M, N, C, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace mla
