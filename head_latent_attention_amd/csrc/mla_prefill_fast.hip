@@ -1,0 +1,260 @@
+// Causal prefill attention on CDNA4 matrix cores (gfx950) for the V2/V3 head
+// shape: q, k [T, H, 192] and v [T, H, 128] in bf16, o [T, H, 128].
+//   o[t, h] = sum_{j <= t} softmax_j(scale * q[t,h] . k[j,h]) v[j,h]
+// (NeMo "MLA" module: forward with a causal attention mask and softmax_scale).
+//
+// Flash-style: a workgroup owns 32*NW queries of one head and streams 64-key tiles
+// of K and V through double-buffered LDS (direct global->LDS copies).  Each wave
+// keeps 32 queries: S^T = K Q^T with keys as the M dimension, so the softmax
+// probabilities are already in the B-operand layout of O^T = V^T P^T; V^T is read
+// with the transposing LDS read.  Online softmax in the log2 domain with a lazy
+// rescale (the running max only moves when a tile exceeds it by 2^8).
+// Workgroups are ordered heaviest first (latest query tiles) and grouped so that
+// the query tiles of one head run on one XCD and share its L2.
+#include "mla_fast.h"
+
+namespace mla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int DQK = 192, DV = 128;
+constexpr int KC = DQK / 8, VC = DV / 8;   // 16-byte chunks per key / value row
+constexpr int KT = 64;                     // keys per tile
+constexpr int K_SLOTS = KT * KC, V_SLOTS = KT * VC;
+constexpr float kRescaleThreshold = 8.0f;
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// K tile: key t, chunk c at slot KC*t + (c ^ ks_swz(t)) (XOR inside aligned groups of 8).
+__device__ __forceinline__ int k_swz(int t) {
+  const int i = (t >> 1) & 7;
+  return ((i << 1) + (i >> 2)) & 7;
+}
+// V tile: key t, chunk c at slot VC*t + (c ^ (2 * (t & 3))).
+__device__ __forceinline__ int v_swz(int t) { return 2 * (t & 3); }
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+struct PrefillArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  bf16_t* o;
+  int T, H;
+  float scale_log2;
+  int n_qtiles;
+};
+
+// Copies of key tile kt: NW waves share K_SLOTS + V_SLOTS 16-byte slots.
+template <int NW>
+__device__ __forceinline__ void issue_kv_copy(const PrefillArgs& P, int h, int kt, uint4* __restrict__ kb,
+                                              uint4* __restrict__ vb, int w, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  constexpr int KI = K_SLOTS / 64 / NW, VI = V_SLOTS / 64 / NW;
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int p = 64 * (KI * w + i) + l;
+    const int t = p / KC, c = (p - t * KC) ^ k_swz(t);
+    const int key = min(kt * KT + t, P.T - 1);
+    dma16(P.k + ((int64_t)key * P.H + h) * DQK + 8 * c, kb + 64 * (KI * w + i));
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int p = 64 * (VI * w + i) + l;
+    const int t = p / VC, c = (p - t * VC) ^ v_swz(t);
+    const int key = min(kt * KT + t, P.T - 1);
+    dma16(P.v + ((int64_t)key * P.H + h) * DV + 8 * c, vb + 64 * (VI * w + i));
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& P, int h, int kt, int n_kt, int qw0,
+                                             const uint4* __restrict__ kb, const uint4* __restrict__ vb,
+                                             uint4* __restrict__ kn, uint4* __restrict__ vn,
+                                             const bf16x8 (&qf)[2][DQK / 32], f32x4 (&o)[DV / 16][2],
+                                             float (&m_run)[2], float (&l_run)[2], const int (&kbase)[2],
+                                             const int (&vbase)[4], int w, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  if (kt + 1 < n_kt) issue_kv_copy<NW>(P, h, kt + 1, kn, vn, w, lane);
+  const int k0 = kt * KT;
+  if (k0 <= qw0 + 31) {  // this wave has queries that see keys of the tile
+    // ---- S^T[key][query]
+    f32x4 s[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DQK / 32; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        // slot KC*(16*mt + j) + ((4*ks + g) ^ k_swz(j)), lane part in kbase[ks & 1]
+        const bf16x8 a = as_bf16x8(*(const uint4*)((const char*)kb + kbase[ks & 1] + (KC * 16 * mt + 8 * (ks >> 1)) * 16));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nt][ks], s[mt][nt], 0, 0, 0);
+      }
+    }
+    // ---- online softmax per query (lane's query: qw0 + 16*nt + j)
+    const bool diag = k0 + KT - 1 > qw0;
+    bf16x8 pb[2][2];  // [nt][kk]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int qi = qw0 + 16 * nt + j;
+      float x[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * mt + 4 * g + i;
+          const float v = s[mt][nt][i] * P.scale_log2;
+          x[mt][i] = (diag && key > qi) ? -INFINITY : v;
+          mx = fmaxf(mx, x[mt][i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = (m_run[nt] == -INFINITY || mx > m_run[nt] + kRescaleThreshold) ? mx : m_run[nt];
+      const float corr = (m_run[nt] == -INFINITY || m_new == -INFINITY) ? (m_run[nt] == m_new ? 1.f : 0.f)
+                                                                         : exp2f(m_run[nt] - m_new);
+      float sum = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = m_new == -INFINITY ? 0.f : exp2f(x[2 * kk][i] - m_new);
+          p[4 + i] = m_new == -INFINITY ? 0.f : exp2f(x[2 * kk + 1][i] - m_new);
+          sum += p[i] + p[4 + i];
+        }
+        pb[nt][kk] = as_bf16x8(make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])));
+      }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      l_run[nt] = l_run[nt] * corr + sum;
+      m_run[nt] = m_new;
+      if (__any(corr != 1.f)) {
+#pragma unroll
+        for (int mt = 0; mt < DV / 16; ++mt) o[mt][nt] *= corr;
+      }
+    }
+    // ---- O^T[d][query] += V^T P^T
+    const char* vbb = (const char*)vb;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < DV / 16; ++mt) {
+        // keys 32*kk + {0,16} + 4*g + j/4, chunk 2*mt + half; lane part in vbase[mt & 3]
+        const char* pa = vbb + vbase[mt & 3] + (VC * 32 * kk + 8 * (mt >> 2)) * 16;
+        const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
+        const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + VC * 16 * 16));
+        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nt][kk], o[mt][nt], 0, 0, 0);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P) {
+  __shared__ __attribute__((aligned(16))) uint4 kbuf[2][K_SLOTS];
+  __shared__ __attribute__((aligned(16))) uint4 vbuf[2][V_SLOTS];
+  constexpr int BQ = 32 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // block -> (head, query tile): one XCD per group of heads, heaviest query tiles first
+  const int bid = blockIdx.x;
+  const int per_xcd = (P.H * P.n_qtiles + kXcds - 1) / kXcds;
+  const int lin = (bid % kXcds) * per_xcd + bid / kXcds;
+  if (lin >= P.H * P.n_qtiles) return;
+  const int h = lin / P.n_qtiles;
+  const int qt = P.n_qtiles - 1 - (lin - h * P.n_qtiles);
+  const int q0 = qt * BQ, qw0 = q0 + 32 * w;
+  const int q_last = min(P.T, q0 + BQ) - 1;
+  const int n_kt = q_last / KT + 1;
+
+  int kbase[2], vbase[4];
+  {
+    const int sj = k_swz(j);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) kbase[e] = (KC * j + ((4 * e + g) ^ sj)) * 16;
+    const int tA = 4 * g + (j >> 2), u = (j >> 2) & 3, half = (j >> 1) & 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vbase[q] = (VC * tA + 2 * (q ^ u) + half) * 16 + (j & 1) * 8;
+  }
+  issue_kv_copy<NW>(P, h, 0, kbuf[0], vbuf[0], w, lane);
+  bf16x8 qf[2][DQK / 32];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int qi = min(qw0 + 16 * nt + j, P.T - 1);
+    const bf16_t* qrow = P.q + ((int64_t)qi * P.H + h) * DQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < DQK / 32; ++ks) qf[nt][ks] = as_bf16x8(*(const uint4*)(qrow + 32 * ks));
+  }
+  f32x4 o[DV / 16][2];
+#pragma unroll
+  for (int mt = 0; mt < DV / 16; ++mt) o[mt][0] = o[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int cur = 0;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    prefill_tile<NW>(P, h, kt, n_kt, qw0, kbuf[cur], vbuf[cur], kbuf[cur ^ 1], vbuf[cur ^ 1], qf, o, m_run, l_run,
+                     kbase, vbase, w, lane);
+    cur ^= 1;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int qi = qw0 + 16 * nt + j;
+    if (qi >= P.T) continue;
+    const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
+    bf16_t* dst = P.o + ((int64_t)qi * P.H + h) * DV + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < DV / 16; ++mt) {
+      const f32x4 v = o[mt][nt] * inv;
+      *(uint2*)(dst + 16 * mt) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+    }
+  }
+}
+
+}  // namespace
+
+bool fast_prefill_attn_supported(const Dims& d) { return d.act == 1 && d.dn + d.dr == DQK && d.dv == DV; }
+
+size_t fast_prefill_attn_ws_bytes(const Dims&, int) { return 0; }
+
+hipError_t fast_prefill_attn(const Dims& d, const void* q, const void* k, const void* v, int T, void* o, void*,
+                             hipStream_t s) {
+  PrefillArgs P;
+  P.q = (const bf16_t*)q;
+  P.k = (const bf16_t*)k;
+  P.v = (const bf16_t*)v;
+  P.o = (bf16_t*)o;
+  P.T = T;
+  P.H = d.H;
+  P.scale_log2 = d.scale * 1.4426950408889634f;
+  // 256 queries per workgroup when that still gives every CU work, else 128
+  const bool big = (int64_t)d.H * ((T + 255) / 256) >= 1024;
+  const int BQ = big ? 256 : 128;
+  P.n_qtiles = (T + BQ - 1) / BQ;
+  const int total = d.H * P.n_qtiles;
+  const int grid = (total + kXcds - 1) / kXcds * kXcds;
+  if (big) prefill_attn_kernel<8><<<grid, 512, 0, s>>>(P);
+  else prefill_attn_kernel<4><<<grid, 256, 0, s>>>(P);
+  return hipGetLastError();
+}
+
+}  // namespace mla
