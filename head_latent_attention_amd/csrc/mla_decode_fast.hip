@@ -151,17 +151,23 @@ __global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q,
 }
 
 // ------------------------------------------------------------------------------ attention
-// LDS tile of 64 tokens: region C holds the 512 latent values of each token as
+// LDS tile of 32 tokens: region C holds the 512 latent values of each token as
 // 64 chunks of 16 bytes (token t, chunk c at slot 64*t + (c ^ swz_c(t))), region
-// PE the 64 rope values as 8 chunks (slot 8*t + (c ^ swz_pe(t))).  swz_c is a
-// bijection of the token's low 4 bits chosen so that both the 16-token reads of
-// the score operand and the 4-token transposing reads of the value operand hit
-// 16 distinct 16-byte bank groups.
-constexpr int kCSlots = kTile * 64, kPeSlots = kTile * 8, kBufSlots = kCSlots + kPeSlots;
+// PE the 64 rope values as 8 chunks (slot 8*t + (c ^ swz_pe(t))).  gfx950 serves a
+// 64-lane ds_read_b128 in four passes of 16 lanes, the lanes of a pass being the
+// lane quads of equal bit parity within each half wave, and a ds_read_b64_tr_b16
+// in two passes of 32 lanes; a pass is conflict-free when its lanes hit distinct
+// 4-byte banks.  swz_c (linear in the token's low 4 bits) satisfies both the
+// 16-token score reads and the 4-token transposing value reads; swz_pe the score
+// reads of the rope chunks.  Four such buffers rotate: three tiles of
+// copies are in flight while the fourth is being consumed.
+constexpr int kSub = 32;                                  // tokens per LDS buffer
+constexpr int kCSlots = kSub * 64, kPeSlots = kSub * 8, kBufSlots = kCSlots + kPeSlots;
+constexpr int kNBuf = 4;
+constexpr int kAttnWaves = 8;
+static_assert(kTile % kSub == 0, "work-list tiles are whole LDS buffers");
 
-__device__ __forceinline__ int swz_c(int t) {
-  return ((t >> 2) & 1) | ((t & 1) << 1) | (((t >> 1) & 1) << 2) | (((t >> 3) & 1) << 3);
-}
+__device__ __forceinline__ int swz_c(int t) { return ((t & 7) << 1) ^ (((t >> 3) & 1) * 9); }
 __device__ __forceinline__ int swz_pe(int t) { return (t >> 1) & 7; }
 
 struct AttnArgs {
@@ -186,129 +192,156 @@ __device__ __forceinline__ T sload(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
-// Row of token `tok` of sequence b (wave-uniform), or the zero row.
-__device__ __forceinline__ const bf16_t* row_ptr(const AttnArgs& A, int b, int tok, int tok_hi) {
-  if (tok < tok_hi) {
-    const int lb = tok / A.bs;
-    if (lb < A.max_blocks) {
-      const int blk = sload(A.bt + (size_t)b * A.max_blocks + lb);
-      if (blk >= 0 && blk < A.n_blocks) return A.cache + ((int64_t)blk * A.bs + (tok - lb * A.bs)) * kR;
-    }
-  }
-  return A.zero_row;
-}
-
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-// Direct global->LDS copies of one 64-token tile: wave w copies tokens [8w, 8w + 8):
-// one 64-lane copy per token for its latent part and one copy for the 8 tokens' rope parts.
-// All row addresses are resolved (scalar loads of the block table) before the first copy
-// is issued, so the copies are in flight together.
-__device__ __forceinline__ void issue_tile_copy(const AttnArgs& A, int b, int tok0, int tok_hi,
-                                                uint4* __restrict__ buf, int w, int lane) {
-  const bf16_t* rows[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) rows[i] = row_ptr(A, b, tok0 + 8 * w + i, tok_hi);
-  // The lane index is made opaque so the per-copy offsets are recomputed here
-  // (one XOR each) instead of being hoisted into long-lived registers.
-  int l = lane;
-  asm volatile("" : "+v"(l));
-  const int tp = l >> 3;
-  const bf16_t* prow = rows[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) prow = tp == i ? rows[i] : prow;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = 8 * w + i;
-    dma16(rows[i] + 8 * (l ^ swz_c(t)), buf + 64 * t);
-  }
-  dma16(prow + kLkv + 8 * ((l & 7) ^ swz_pe(8 * w + tp)), buf + kCSlots + 64 * w);
+// Block id of the (block-size aligned) 32-token sub-tile starting at token tok0, or -1.
+__device__ __forceinline__ int sub_tile_block(const AttnArgs& A, int b, int tok0, int tok_hi) {
+  if (tok0 >= tok_hi) return -1;
+  const int lb = tok0 / A.bs;
+  return lb < A.max_blocks ? sload(A.bt + (size_t)b * A.max_blocks + lb) : -1;
 }
 
-// One 64-token tile: prefetch the next tile into `nxt`, scores, online softmax, PV.
-// `buf` and `nxt` are restrict-qualified: once inlined, the copies into `nxt` carry
-// alias scopes disjoint from the reads of `buf`, so the compiler does not make those
-// reads wait for the copies and the prefetch stays in flight during the compute.
-__device__ __forceinline__ void attn_tile(const AttnArgs& A, int b, int tok0, int tok_hi,
-                                          const uint4* __restrict__ buf, uint4* __restrict__ nxt,
-                                          const bf16x8 (&qf)[kR / 32], f32x4 (&o)[kLkv / 16], float& m_run,
-                                          float& l_run, const int (&sbase)[4], const int (&pbase)[2],
-                                          const int (&tbase)[8], int w, int lane, int g) {
-  if (tok0 + kTile < tok_hi) issue_tile_copy(A, b, tok0 + kTile, tok_hi, nxt, w, lane);
-  const char* bbase = (const char*)buf;
-  // ---- scores S^T[token][head], 4 token tiles of 16; k-steps 0..15 latent, 16..17 rope
-  f32x4 s[4];
+// Direct global->LDS copies of one 32-token sub-tile of block `blk`.  The block size is a
+// multiple of 32, so the sub-tile's rows are 32 consecutive rows of one cache block.  Wave
+// w copies the latent parts of tokens [4w, 4w + 4) (one 64-lane copy each); waves 0..3
+// also copy the rope parts of tokens [8w, 8w + 8) (8 lanes per token).  Rows past the
+// context or in an invalid block come from the zero row.
+__device__ __forceinline__ void issue_tile_copy(const AttnArgs& A, int blk, int tok0, int tok_hi,
+                                                uint4* __restrict__ buf, int w, int lane) {
+  const bool blk_ok = blk >= 0 && blk < A.n_blocks;
+  const bf16_t* base = A.cache + ((int64_t)blk * A.bs + (tok0 % A.bs)) * kR;
+  int l = lane;
+  asm volatile("" : "+v"(l));
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < kR / 32; ++ks) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const char* pa = ks < 16 ? bbase + sbase[ks & 3] + (16 * mt * 64 + 16 * (ks >> 2)) * 16
-                               : bbase + pbase[ks - 16] + (16 * mt * 8) * 16;
-      const bf16x8 a = as_bf16x8(*(const uint4*)pa);
-      s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[mt], 0, 0, 0);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * w + i;
+    const bf16_t* row = (blk_ok && tok0 + t < tok_hi) ? base + t * kR : A.zero_row;  // wave-uniform
+    dma16(row + 8 * (l ^ swz_c(t)), buf + 64 * t);
   }
-  // ---- online softmax (log2 domain); this lane's head is `head`
-  float x[4][4];
+  if (w < 4) {
+    const int t = 8 * w + (l >> 3);
+    const bf16_t* row = (blk_ok && tok0 + t < tok_hi) ? base + t * kR : A.zero_row;
+    dma16(row + kLkv + 8 * ((l & 7) ^ swz_pe(t)), buf + kCSlots + 64 * w);
+  }
+}
+
+// Reductions over the lanes that share (lane & 15): the gfx950 row-swap permutes
+// (v_permlane16_swap / v_permlane32_swap) leave {x[l], x[l ^ 16]} (resp. 32) in the
+// two results of every lane.
+__device__ __forceinline__ float xmax16_32(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float xsum16_32(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Waits until this wave's copies of the oldest in-flight sub-tile have landed, given
+// that `later` further sub-tiles' copies were issued after it.
+__device__ __forceinline__ void wait_copies(int w, int later) {
+  // copies per sub-tile per wave: 5 for waves 0..3, 4 for waves 4..7
+  if (w < 4) {
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 10);
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 5);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  } else {
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+}
+
+// One 32-token sub-tile.  `nxt` (the buffer three sub-tiles ahead) is refilled and,
+// when `compute` is set, `buf` is consumed.  Both are restrict-qualified so that, once
+// inlined, the copies into `nxt` carry alias scopes disjoint from the reads of `buf`;
+// every copy of a segment (also the first three) is issued by this one inlined call
+// site, so the compiler never makes the score/value reads wait for copies in flight.
+__device__ __forceinline__ void attn_sub_tile(const AttnArgs& A, int tok0, int tok_hi, int tok_pf, int blk_pf,
+                                              bool compute, const uint4* __restrict__ buf, uint4* __restrict__ nxt,
+                                              const bf16x8 (&qf)[kR / 32], f32x4 (&o)[kLkv / 16], float& m_run,
+                                              float& l_run, int w, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  if (tok_pf < tok_hi) issue_tile_copy(A, blk_pf, tok_pf, tok_hi, nxt, w, lane);
+  if (!compute) return;
+  const char* bbase = (const char*)buf;
+  // ---- scores S^T[token][head]: 2 token tiles of 16; k-steps 0..15 latent, 16..17 rope
+  // lane address parts: token 16*mt + j has the swizzle of j
+  const int sj = swz_c(j), pj = swz_pe(j);
+  const int srow = 64 * j * 16, prow = (kCSlots + 8 * j) * 16;
+  auto s_addr = [&](int ks, int mt) -> const uint4* {
+    if (ks < 16) return (const uint4*)(bbase + srow + 16 * 64 * 16 * mt + ((4 * ks + g) ^ sj) * 16);
+    return (const uint4*)(bbase + prow + 16 * 8 * 16 * mt + ((4 * (ks - 16) + g) ^ pj) * 16);
+  };
+  f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  bf16x8 a_nx = as_bf16x8(*s_addr(0, 0));
+#pragma unroll
+  for (int it = 0; it < 2 * (kR / 32); ++it) {
+    const int ks = it >> 1, mt = it & 1;
+    const bf16x8 a = a_nx;
+    if (it + 1 < 2 * (kR / 32)) a_nx = as_bf16x8(*s_addr((it + 1) >> 1, (it + 1) & 1));
+    s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[mt], 0, 0, 0);
+  }
+  // ---- online softmax (log2 domain); the lane's head is 16*w + j
+  float x[2][4];
   float mx = -INFINITY;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = tok0 + 16 * mt + 4 * g + i;
       x[mt][i] = tok < tok_hi ? s[mt][i] * A.scale_log2 : -INFINITY;
       mx = fmaxf(mx, x[mt][i]);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = xmax16_32(mx);
   const float m_new = (m_run == -INFINITY || mx > m_run + kRescaleThreshold) ? mx : m_run;
-  const float corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+  const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+  float p[8];
   float sum = 0.f;
-  bf16x8 pb[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    float p[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = exp2f(x[2 * kk][i] - m_new);
-      p[4 + i] = exp2f(x[2 * kk + 1][i] - m_new);
-      sum += p[i] + p[4 + i];
-    }
-    pb[kk] = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                  pack_bf16x2(p[6], p[7])));
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(x[0][i] - m_new);
+    p[4 + i] = __builtin_amdgcn_exp2f(x[1][i] - m_new);
+    sum += p[i] + p[4 + i];
   }
-  sum += __shfl_xor(sum, 16, 64);
-  sum += __shfl_xor(sum, 32, 64);
+  const bf16x8 pb = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                         pack_bf16x2(p[6], p[7])));
+  sum = xsum16_32(sum);
   l_run = l_run * corr + sum;
   m_run = m_new;
   if (__any(corr != 1.f)) {
 #pragma unroll
     for (int mt = 0; mt < kLkv / 16; ++mt) o[mt] *= corr;
   }
-  // ---- O^T[latent][head] += V^T P^T, two k-steps of 32 tokens
+  // ---- O^T[latent][head] += V^T P^T over the 32 tokens (one k-step)
+  // tokens {0,16} + 4*g + j/4 share the swizzle of 4*g + j/4; chunk 2*mt + half
+  const int tA = 4 * g + (j >> 2);
+  const int vU = ((j >> 1) & 1) ^ swz_c(tA);
+  const int vrow = 64 * tA * 16 + (j & 1) * 8;
+  auto v_addr = [&](int mt) -> const char* { return bbase + vrow + ((2 * mt) ^ vU) * 16; };
+  bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)v_addr(0));
+  bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v_addr(0) + 16 * 64 * 16));
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-    for (int mt = 0; mt < kLkv / 16; ++mt) {
-      const char* pa = bbase + tbase[mt & 7] + (32 * kk * 64 + 16 * (mt >> 3)) * 16;
-      const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
-      const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + 16 * 64 * 16));
-      const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kk], o[mt], 0, 0, 0);
+  for (int mt = 0; mt < kLkv / 16; ++mt) {
+    const bf16x8 a = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    if (mt + 1 < kLkv / 16) {
+      b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)v_addr(mt + 1));
+      b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v_addr(mt + 1) + 16 * 64 * 16));
     }
+    o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
 }
 
 // 512 threads = 8 waves; wave w owns heads [16w, 16w + 16).
-__global__ __launch_bounds__(512, 1) void decode_attn_kernel(AttnArgs A) {
-  __shared__ __attribute__((aligned(16))) uint4 kv[2][kBufSlots];
+__global__ __launch_bounds__(64 * kAttnWaves, 1) void decode_attn_kernel(AttnArgs A) {
+  __shared__ __attribute__((aligned(16))) uint4 kv[kNBuf][kBufSlots];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = sload(A.P + A.B);
@@ -325,20 +358,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(AttnArgs A) {
   int b = lo;
   int tile = t_lo;
   const int head = 16 * w + j;
-  // Lane-dependent byte offsets inside a tile buffer; every LDS address below is
-  // one of these plus a compile-time offset.  Token 16*mt + j has the swizzle
-  // of j; token 32*kk + {0,16} + 4*g + j/4 has the swizzle of 4*g + j/4.
-  int sbase[4], pbase[2], tbase[8];
-  {
-    const int sj = swz_c(j), pj = swz_pe(j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sbase[e] = (64 * j + ((4 * e + g) ^ sj)) * 16;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) pbase[e] = (kCSlots + 8 * j + ((4 * e + g) ^ pj)) * 16;
-    const int tA = 4 * g + (j >> 2), sA = swz_c(tA), half = (j >> 1) & 1;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) tbase[q] = (64 * tA + ((2 * q + half) ^ sA)) * 16 + (j & 1) * 8;
-  }
   while (tile < t_hi) {
     while (sload(A.P + b + 1) <= tile) ++b;
     const int pb0 = sload(A.P + b);
@@ -346,8 +365,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(AttnArgs A) {
     const int tok_lo = (tile - pb0) * kTile;
     const int tok_hi = min(sload(A.ctx + b), (seg_end - pb0) * kTile);
     tile = seg_end;
-
-    issue_tile_copy(A, b, tok_lo, tok_hi, kv[0], w, lane);
+    const int n_sub = (tok_hi - tok_lo + kSub - 1) / kSub;
     // Q^T fragments of this wave's 16 heads (B operand of S^T = K Q^T)
     bf16x8 qf[kR / 32];
     {
@@ -355,17 +373,27 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(AttnArgs A) {
 #pragma unroll
       for (int ks = 0; ks < kR / 32; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qrow + 32 * ks));
     }
+    // nothing but cache-row copies may be in flight inside the loop below
+    __builtin_amdgcn_s_waitcnt(0);
     f32x4 o[kLkv / 16];
 #pragma unroll
     for (int mt = 0; mt < kLkv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    // iterations st < 0 only put the first kNBuf - 1 sub-tiles in flight
+    for (int st = -(kNBuf - 1); st < n_sub; ++st) {
+      const int tok_pf = tok_lo + (st + kNBuf - 1) * kSub;
+      const int blk_pf = sub_tile_block(A, b, tok_pf, tok_hi);  // scalar load, overlaps the barrier
+      if (st >= 0) {
+        // copies issued after sub-tile st's: those of st+1 and st+2 (when they exist)
+        wait_copies(w, min(n_sub - 1 - st, kNBuf - 2));
+        __syncthreads();
+      }
+      const int sb = st < 0 ? 0 : st % kNBuf;
+      attn_sub_tile(A, tok_lo + st * kSub, tok_hi, tok_pf, blk_pf, st >= 0, kv[sb], kv[(st + 2 * kNBuf - 1) % kNBuf], qf,
+                    o, m_run, l_run, w, lane);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int cur = 0;
-    for (int tok0 = tok_lo; tok0 < tok_hi; tok0 += kTile) {
-      attn_tile(A, b, tok0, tok_hi, kv[cur], kv[cur ^ 1], qf, o, m_run, l_run, sbase, pbase, tbase, w, lane, g);
-      cur ^= 1;
-    }
     // ---- partial result of (this workgroup, sequence b)
     const size_t ps = (size_t)wg + b;
     float* dst = A.part_o + (ps * kH + head) * kLkv + 4 * g;
@@ -493,7 +521,7 @@ DecodeLayout layout(int B, void* base) {
 
 bool fast_decode_supported(const Dims& d) {
   return d.act == 1 && (d.wk == W_BF16 || d.wk == W_FP8) && d.H == kH && d.Lkv == kLkv && d.dr == kDr &&
-         d.dn == kDn && d.dv == kDv;
+         d.dn == kDn && d.dv == kDv && d.bs % kSub == 0;
 }
 
 size_t fast_decode_ws_bytes(const Dims& d, int B, int) { return layout(B, nullptr).bytes; }
@@ -520,7 +548,7 @@ hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cac
   A.scale_log2 = d.scale * 1.4426950408889634f;
   A.part_o = L.part_o;
   A.part_ml = L.part_ml;
-  decode_attn_kernel<<<kAttnWGs, 512, 0, s>>>(A);
+  decode_attn_kernel<<<kAttnWGs, 64 * kAttnWaves, 0, s>>>(A);
   dim3 cgrid(kH, (B + 15) / 16);
   if (d.wk == W_BF16) combine_kernel<W_BF16><<<cgrid, 256, 0, s>>>(L.part_o, L.part_ml, L.P, B, wkv_b, (bf16_t*)o);
   else combine_kernel<W_FP8><<<cgrid, 256, 0, s>>>(L.part_o, L.part_ml, L.P, B, wkv_b, (bf16_t*)o);

@@ -35,8 +35,10 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 // A tile: [BM][64] bf16, 8 chunks of 16 B per row; chunk c of row r at slot 8r + (c ^ ((r >> 1) & 7)).
 __device__ __forceinline__ int a_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
-// W tile: [64][128] bf16, 16 chunks per row; chunk c of row k at slot 16k + (c ^ (2 * (k & 3))).
-__device__ __forceinline__ int w_slot(int k, int c) { return 16 * k + (c ^ (2 * (k & 3))); }
+// W tile: [64][128] bf16, 16 chunks per row; chunk c of row k at slot 16k + (c ^ ws(k)).  The XOR
+// patterns keep the 16-lane passes of ds_read_b128 and the 32-lane passes of the transposing
+// ds_read_b64_tr_b16 on distinct banks.
+__device__ __forceinline__ int w_slot(int k, int c) { return 16 * k + (c ^ (((k & 3) << 1) ^ (((k >> 3) & 1) << 3))); }
 
 template <int BM, int WM, int WN, int WK>
 struct Gemm {

@@ -34,13 +34,12 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
-// K tile: key t, chunk c at slot KC*t + (c ^ ks_swz(t)) (XOR inside aligned groups of 8).
-__device__ __forceinline__ int k_swz(int t) {
-  const int i = (t >> 1) & 7;
-  return ((i << 1) + (i >> 2)) & 7;
-}
-// V tile: key t, chunk c at slot VC*t + (c ^ (2 * (t & 3))).
-__device__ __forceinline__ int v_swz(int t) { return 2 * (t & 3); }
+// K tile: key t, chunk c at slot KC*t + (c ^ k_swz(t)) (XOR inside aligned groups of 8).
+// V tile: key t, chunk c at slot VC*t + (c ^ v_swz(t)).  Both keep the 16-lane passes of
+// ds_read_b128 (score operand) and the 32-lane passes of ds_read_b64_tr_b16 (value
+// operand) on distinct banks.
+__device__ __forceinline__ int k_swz(int t) { return (t >> 1) & 7; }
+__device__ __forceinline__ int v_swz(int t) { return 2 * (t & 7); }
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
@@ -154,8 +153,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& P, int h, int kt
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int mt = 0; mt < DV / 16; ++mt) {
-        // keys 32*kk + {0,16} + 4*g + j/4, chunk 2*mt + half; lane part in vbase[mt & 3]
-        const char* pa = vbb + vbase[mt & 3] + (VC * 32 * kk + 8 * (mt >> 2)) * 16;
+        // keys 32*kk + {0,16} + 4*g + j/4 (same swizzle), chunk 2*mt + half = (2*mt) ^ half
+        const char* pa = vbb + vbase[0] + (VC * 32 * kk) * 16 + ((2 * mt) ^ vbase[1]) * 16;
         const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
         const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + VC * 16 * 16));
         const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -191,9 +190,10 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
     const int sj = k_swz(j);
 #pragma unroll
     for (int e = 0; e < 2; ++e) kbase[e] = (KC * j + ((4 * e + g) ^ sj)) * 16;
-    const int tA = 4 * g + (j >> 2), u = (j >> 2) & 3, half = (j >> 1) & 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) vbase[q] = (VC * tA + 2 * (q ^ u) + half) * 16 + (j & 1) * 8;
+    const int tA = 4 * g + (j >> 2), half = (j >> 1) & 1;
+    vbase[0] = VC * tA * 16 + (j & 1) * 8;   // row part
+    vbase[1] = half ^ v_swz(tA);            // chunk XOR
+    vbase[2] = vbase[3] = 0;
   }
   issue_kv_copy<NW>(P, h, 0, kbuf[0], vbuf[0], w, lane);
   bf16x8 qf[2][DQK / 32];
