@@ -126,7 +126,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(name, launches_per_step=1):
+def traffic_from_profiles(name):
     """HBM bytes per launch from committed FETCH_SIZE / WRITE_SIZE counter runs, or None
     when the kernels changed since the counters were taken."""
     p = os.path.join(PROFILES, f"{name}_traffic.json")
@@ -135,7 +135,7 @@ def traffic_from_profiles(name, launches_per_step=1):
     rec = json.load(open(p))
     if rec.get("kernel_src_sha") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return round(rec.get("bytes_per_launch"))
 
 
 def run_prefill(w, reps):
@@ -234,6 +234,8 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration for HBM traffic)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
@@ -244,6 +246,13 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4}))
+        return
     w = synth.WORKLOADS[3]
     s = w.shape
     log(f"[bench] setting up {w.name}")

@@ -1,0 +1,110 @@
+"""Summaries of rocprofv3 CSV output: per-kernel time statistics and HBM traffic per
+launch of an entry point (FETCH_SIZE / WRITE_SIZE counters scaled by a plain copy of
+known size).
+
+Usage:
+  python -m head_latent_attention_amd.profiling stats RUN_kernel_stats.csv
+  python -m head_latent_attention_amd.profiling summary RUN_kernel_stats.csv "TITLE" "COMMAND" > OUT.md
+  python -m head_latent_attention_amd.profiling traffic FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR OUT.json
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+# kernels launched once by each mla_decode_attn_absorbed call (MFMA path)
+DECODE_ATTN_KERNELS = ("plan_kernel", "fold_kernel", "decode_attn_kernel", "combine_kernel")
+COPY_BYTES = 1 << 30
+
+
+def kernel_stats(path: str):
+    rows = list(csv.DictReader(open(path)))
+    out = []
+    for r in rows:
+        out.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
+    return out
+
+
+def _counter_rows(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def per_kernel_counter(d: str, counter: str):
+    """{kernel short name: mean counter value per dispatch}"""
+    acc = {}
+    for r in _counter_rows(d):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _largest(d: str, counter: str) -> float:
+    vals = per_kernel_counter(d, counter)
+    return max(vals.values())
+
+
+def source_hash(csrc: str) -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir, out_json, kernels=DECODE_ATTN_KERNELS):
+    # the copy reads and writes COPY_BYTES once; its counters give KiB -> bytes factors
+    f_copy = _largest(calib_fetch_dir, "FETCH_SIZE") * 1024.0
+    w_copy = _largest(calib_write_dir, "WRITE_SIZE") * 1024.0
+    f_factor, w_factor = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    fetch = per_kernel_counter(fetch_dir, "FETCH_SIZE")
+    write = per_kernel_counter(write_dir, "WRITE_SIZE")
+    parts = {}
+    total = 0.0
+    for short in kernels:
+        fk = [v for k, v in fetch.items() if short in k]
+        wk = [v for k, v in write.items() if short in k]
+        if not fk or not wk:
+            raise KeyError(f"kernel {short} missing from the counter runs")
+        b = fk[0] * 1024.0 * f_factor + wk[0] * 1024.0 * w_factor
+        parts[short] = {"fetch_bytes": fk[0] * 1024.0 * f_factor, "write_bytes": wk[0] * 1024.0 * w_factor}
+        total += b
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    rec = {"kernel_src_sha": source_hash(csrc), "bytes_per_launch": total, "kernels": parts,
+           "copy_calibration": {"copy_bytes": COPY_BYTES, "fetch_factor": f_factor, "write_factor": w_factor}}
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
+def summary_md(stats_csv: str, title: str, command: str) -> str:
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp", command, "```", "",
+             "| kernel | calls | average (us) | share of GPU time |", "|---|---:|---:|---:|"]
+    for name, calls, avg_us, pct in kernel_stats(stats_csv):
+        short = name.replace("(anonymous namespace)::", "").split("(")[0]
+        short = short[5:] if short.startswith("void ") else short
+        short = short if len(short) <= 80 else short[:77] + "..."
+        lines.append(f"| `{short}` | {calls} | {avg_us:.1f} | {pct:.2f}% |")
+    lines.append("")
+    return "\n".join(lines)
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "summary":
+        print(summary_md(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif sys.argv[1] == "stats":
+        for name, calls, avg_us, pct in kernel_stats(sys.argv[2]):
+            print(f"{avg_us:10.1f} us  {calls:6d}  {pct:6.2f}%  {name[:110]}")
+    elif sys.argv[1] == "traffic":
+        print(json.dumps(traffic(*sys.argv[2:7]), indent=1))
