@@ -78,33 +78,33 @@ WeightView view(const Dims& d, const mla_weight& w, int64_t N) {
 }
 
 // ---- workspace layouts (the single source of truth for sizes and pointers) ----------
-struct QkvWs {
-  float* Y1;     // [n, Lq + R]   stage-1 outputs (fp32)
-  float* Qraw;   // [n, H*dqk]    stage-2 query (fp32)
-  void* cqn;     // [n, Lq]       RMSNorm(q latent) * gamma (act)
-  void* cn;      // [n, Lkv]      RMSNorm(c_kv) * gamma (act), prefill only
-  float* KVraw;  // [n, H*(dn+dv)] prefill only
-  void* gscratch;  // split-K partial sums of the projection GEMMs
-};
-
-size_t gemm_scratch(const Dims& d, int n, bool prefill) {
-  if (!fast_proj_supported(d)) return 0;
-  const int HQ = d.H * d.dqk();
-  size_t s = std::max(fast_gemm_ws_bytes(n, d.R(), d.D), fast_gemm_ws_bytes(n, HQ, d.Lq > 0 ? d.Lq : d.D));
-  if (d.Lq > 0) s = std::max(s, fast_gemm_ws_bytes(n, d.Lq, d.D));
-  if (prefill) s = std::max(s, fast_gemm_ws_bytes(n, d.H * (d.dn + d.dv), d.Lkv));
-  return s;
+// Every projection result is kept as fp32 split-K partial sums (one part on the general
+// path) and summed by the kernel that consumes it.
+size_t proj_out_bytes(const Dims& d, int M, int N, int K) {
+  if (fast_proj_supported(d)) return fast_gemm_out_bytes(M, N, K);
+  return (size_t)M * N * sizeof(float);
 }
+
+// output columns of the stage-1 projection: [q latent (Lq) or query (H*dqk) | c_kv | k_pe]
+int stage1_q_cols(const Dims& d) { return d.Lq > 0 ? d.Lq : d.H * d.dqk(); }
+
+struct QkvWs {
+  float* P1;   // [n, stage1_q_cols + R]  stage-1 projection
+  float* P2;   // [n, H*dqk]              query up-projection (Lq > 0)
+  void* cqn;   // [n, Lq]                 RMSNorm(q latent) * gamma (act)
+  void* cn;    // [n, Lkv]                RMSNorm(c_kv) * gamma (act), prefill only
+  float* PKV;  // [n, H*(dn+dv)]          kv up-projection, prefill only
+};
 
 size_t qkv_ws(const Dims& d, int n, bool prefill, void* base, QkvWs* out) {
   Carver c(base);
   QkvWs w;
-  w.Y1 = c.take<float>((size_t)n * (d.Lq + d.R()));
-  w.Qraw = c.take<float>((size_t)n * d.H * d.dqk());
-  w.cqn = c.take<char>((size_t)n * (d.Lq > 0 ? d.Lq : 1) * act_bytes(d));
+  const int HQ = d.H * d.dqk();
+  w.P1 = (float*)c.take<char>(proj_out_bytes(d, n, stage1_q_cols(d) + d.R(), d.D));
+  w.P2 = d.Lq > 0 ? (float*)c.take<char>(proj_out_bytes(d, n, HQ, d.Lq)) : nullptr;
+  w.cqn = d.Lq > 0 ? c.take<char>((size_t)n * d.Lq * act_bytes(d)) : nullptr;
   w.cn = prefill ? c.take<char>((size_t)n * d.Lkv * act_bytes(d)) : nullptr;
-  w.KVraw = prefill ? c.take<float>((size_t)n * d.H * (d.dn + d.dv)) : nullptr;
-  w.gscratch = c.take<char>(gemm_scratch(d, n, prefill));
+  w.PKV = prefill ? (float*)c.take<char>(proj_out_bytes(d, n, d.H * (d.dn + d.dv), d.Lkv)) : nullptr;
   if (out) *out = w;
   return c.used;
 }
@@ -145,12 +145,10 @@ size_t decode_attn_ws(const Dims& d, int B, int max_context, void* base, DecodeA
   return c.used;
 }
 
-size_t out_proj_ws(const Dims& d, int M, void* base, float** Y, void** scratch) {
+size_t out_proj_ws(const Dims& d, int M, void* base, float** Y) {
   Carver c(base);
-  float* y = c.take<float>((size_t)M * d.D);
-  void* sc = c.take<char>(fast_proj_supported(d) ? fast_gemm_ws_bytes(M, d.D, d.H * d.dv) : 0);
+  float* y = (float*)c.take<char>(proj_out_bytes(d, M, d.D, d.H * d.dv));
   if (Y) *Y = y;
-  if (scratch) *scratch = sc;
   return c.used;
 }
 
@@ -168,39 +166,41 @@ mla_status hip_status(hipError_t e) {
     if (e_ != hipSuccess) return hip_status(e_);          \
   } while (0)
 
-// Shared front end of prefill and decode: stage-1 GEMMs, row builder, query.
+// C = A @ [W0 | W1] (W0: output columns [0, n_split)), left as partial sums in `out`.
+mla_status project(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split, const WeightView& W1,
+                   int M, int N, int K, float* out, Partials* res, hipStream_t s) {
+  if (fast_proj_supported(d)) {
+    HIP_TRY(fast_gemm(d, A, lda, W0, n_split, W1, M, N, K, out, res, s));
+    return MLA_OK;
+  }
+  const int n0 = std::min(n_split, N);
+  HIP_TRY(gemm_simt(d, A, lda, W0, out, N, M, n0, K, s));
+  if (n0 < N) HIP_TRY(gemm_simt(d, A, lda, W1, out + n0, N, M, N - n0, K, s));
+  *res = Partials{out, 1, 0, N};
+  return MLA_OK;
+}
+
+// Shared front end of prefill and decode: one projection of x by [wq_a | wkv_a] (by
+// [wq_b | wkv_a] without a query latent), row builder, query up-projection and RoPE.
 mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, const float* cosT,
                      const float* sinT, void* q, void* kbuf, void* kv_cache, int64_t n_blocks,
                      const int32_t* slot_mapping, const QkvWs& ws, hipStream_t s) {
-  const int ldy = d.Lq + d.R();
   const int64_t n_slots = kv_cache ? n_blocks * d.bs : 0;
   const int HQ = d.H * d.dqk();
-  if (fast_proj_supported(d)) {
-    if (d.Lq > 0) {
-      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wq_a, d.Lq), ws.Y1, ldy, n, d.Lq, d.D, ws.gscratch, s));
-      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1 + d.Lq, ldy, n, d.R(), d.D, ws.gscratch, s));
-    } else {
-      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.D, ws.gscratch, s));
-      HIP_TRY(fast_gemm(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1, ldy, n, d.R(), d.D, ws.gscratch, s));
-    }
-  } else {
-    if (d.Lq > 0) {
-      HIP_TRY(gemm_simt(d, x, d.D, view(d, w->wq_a, d.Lq), ws.Y1, ldy, n, d.Lq, d.D, s));
-      HIP_TRY(gemm_simt(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1 + d.Lq, ldy, n, d.R(), d.D, s));
-    } else {
-      HIP_TRY(gemm_simt(d, x, d.D, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.D, s));
-      HIP_TRY(gemm_simt(d, x, d.D, view(d, w->wkv_a, d.R()), ws.Y1, ldy, n, d.R(), d.D, s));
-    }
-  }
-  HIP_TRY(row_builder(d, ws.Y1, ldy, n, w->q_norm_w, w->kv_norm_w, cosT, sinT, d.Lq > 0 ? ws.cqn : nullptr,
-                      ws.cn, kv_cache, n_slots, slot_mapping, kbuf, s));
+  const int NQ1 = stage1_q_cols(d);
+  Partials P1;
+  const WeightView w1q = d.Lq > 0 ? view(d, w->wq_a, d.Lq) : view(d, w->wq_b, HQ);
+  mla_status st = project(d, x, d.D, w1q, NQ1, view(d, w->wkv_a, d.R()), n, NQ1 + d.R(), d.D, ws.P1, &P1, s);
+  if (st != MLA_OK) return st;
+  HIP_TRY(row_builder(d, P1, P1.offset(NQ1), n, w->q_norm_w, w->kv_norm_w, cosT, sinT, ws.cqn, ws.cn, kv_cache,
+                      n_slots, slot_mapping, kbuf, s));
+  Partials PQ = P1;
   if (d.Lq > 0) {
-    if (fast_proj_supported(d))
-      HIP_TRY(fast_gemm(d, ws.cqn, d.Lq, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.Lq, ws.gscratch, s));
-    else
-      HIP_TRY(gemm_simt(d, ws.cqn, d.Lq, view(d, w->wq_b, HQ), ws.Qraw, HQ, n, HQ, d.Lq, s));
+    const WeightView wqb = view(d, w->wq_b, HQ);
+    st = project(d, ws.cqn, d.Lq, wqb, HQ, wqb, n, HQ, d.Lq, ws.P2, &PQ, s);
+    if (st != MLA_OK) return st;
   }
-  HIP_TRY(q_epilogue(d, ws.Qraw, HQ, n, cosT, sinT, q, s));
+  HIP_TRY(q_epilogue(d, PQ, n, cosT, sinT, q, s));
   return MLA_OK;
 }
 
@@ -235,7 +235,7 @@ size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t 
     case MLA_FN_DECODE_ATTN:
       if (max_context <= 0) return 0;
       return decode_attn_ws(d, n, max_context, nullptr, nullptr);
-    case MLA_FN_OUT_PROJ: return out_proj_ws(d, n, nullptr, nullptr, nullptr);
+    case MLA_FN_OUT_PROJ: return out_proj_ws(d, n, nullptr, nullptr);
   }
   return 0;
 }
@@ -258,11 +258,11 @@ mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const vo
   st = front_end(d, w, x, T, cos, sin, q, k, kv_cache, n_blocks, slot_mapping, L, s);
   if (st != MLA_OK) return st;
   const int NKV = d.H * (d.dn + d.dv);
-  if (fast_proj_supported(d))
-    HIP_TRY(fast_gemm(d, L.cn, d.Lkv, view(d, w->wkv_b, NKV), L.KVraw, NKV, T, NKV, d.Lkv, L.gscratch, s));
-  else
-    HIP_TRY(gemm_simt(d, L.cn, d.Lkv, view(d, w->wkv_b, NKV), L.KVraw, NKV, T, NKV, d.Lkv, s));
-  HIP_TRY(kv_split(d, L.KVraw, T, k, v, s));
+  const WeightView wkvb = view(d, w->wkv_b, NKV);
+  Partials PKV;
+  st = project(d, L.cn, d.Lkv, wkvb, NKV, wkvb, T, NKV, d.Lkv, L.PKV, &PKV, s);
+  if (st != MLA_OK) return st;
+  HIP_TRY(kv_split(d, PKV, T, k, v, s));
   return MLA_OK;
 }
 
@@ -336,16 +336,15 @@ mla_status mla_out_proj(const mla_config* cfg, const mla_weights* w, const void*
   if (st != MLA_OK) return st;
   if (M <= 0 || !w || !o || !y || !check_weight(d, w->wo)) return MLA_ERR_INVALID_ARG;
   float* Y = nullptr;
-  void* scratch = nullptr;
-  const size_t need = out_proj_ws(d, M, ws, &Y, &scratch);
+  const size_t need = out_proj_ws(d, M, ws, &Y);
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int K = d.H * d.dv;
-  if (fast_proj_supported(d))
-    HIP_TRY(fast_gemm(d, o, K, view(d, w->wo, d.D), Y, d.D, M, d.D, K, scratch, s));
-  else
-    HIP_TRY(gemm_simt(d, o, K, view(d, w->wo, d.D), Y, d.D, M, d.D, K, s));
-  HIP_TRY(cast_rows(d, Y, (int64_t)M * d.D, y, s));
+  const WeightView wo = view(d, w->wo, d.D);
+  Partials P;
+  st = project(d, o, K, wo, d.D, wo, M, d.D, K, Y, &P, s);
+  if (st != MLA_OK) return st;
+  HIP_TRY(cast_rows(d, P, M, d.D, y, s));
   return MLA_OK;
 }
 

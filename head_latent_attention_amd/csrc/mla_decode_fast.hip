@@ -102,51 +102,60 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 
 // ------------------------------------------------------------------------------ fold
 // Qabs[b][h] = [q_nope[b][h] @ W_UK[h] | q_pe[b][h]] in bf16, W_UK[h][p][c] = wkv_b[c][h*256 + p].
-// Grid (H, ceil(B/64)); wave w computes latent columns [128w, 128w + 128) for 64 rows.
+// Grid (H, 4, ceil(B/64)): workgroup (h, cg) covers latent columns [128cg, 128cg + 128) of 64
+// rows, wave w the 32 columns [128cg + 32w, 128cg + 32w + 32).  Every operand load of a wave is
+// issued before its first matrix op.
 template <int WK>
 __global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q, int B, WeightView W,
                                                    bf16_t* __restrict__ Qabs) {
-  const int h = blockIdx.x, b0 = blockIdx.y * 64;
+  const int h = blockIdx.x, cg = blockIdx.y, b0 = blockIdx.z * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int qs = kH * (kDn + kDr);
+  const int c0 = 128 * cg + 32 * w;
+  uint4 a[kDn / 32][4], bw[kDn / 32][2];
 #pragma unroll
   for (int ks = 0; ks < kDn / 32; ++ks) {
-    bf16x8 a[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int b = b0 + 16 * mt + j;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (b < B) v = *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + 32 * ks + 8 * g);
-      a[mt] = as_bf16x8(v);
+      a[ks][mt] = b < B ? *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + 32 * ks + 8 * g)
+                        : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int c = 128 * w + 16 * nt + j;
-      const bf16x8 bop = as_bf16x8(load_w8<WK>(W, c, (int64_t)h * (kDn + kDv) + 32 * ks + 8 * g));
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], bop, acc[mt][nt], 0, 0, 0);
-    }
+    for (int nt = 0; nt < 2; ++nt)
+      bw[ks][nt] = load_w8<WK>(W, c0 + 16 * nt + j, (int64_t)h * (kDn + kDv) + 32 * ks + 8 * g);
   }
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kDn / 32; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks][mt]), as_bf16x8(bw[ks][nt]),
+                                                              acc[mt][nt], 0, 0, 0);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = b0 + 16 * mt + 4 * g + i;
       if (b >= B) continue;
-      bf16_t* dst = Qabs + ((size_t)b * kH + h) * kR;
+      bf16_t* dst = Qabs + ((size_t)b * kH + h) * kR + c0 + j;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) dst[128 * w + 16 * nt + j] = f32_to_bf16(acc[mt][nt][i]);
+      for (int nt = 0; nt < 2; ++nt) dst[16 * nt] = f32_to_bf16(acc[mt][nt][i]);
     }
   // rope part of the query is carried over unchanged
-  for (int e = tid; e < 64 * kDr; e += 256) {
-    const int r = e / kDr, d = e - r * kDr, b = b0 + r;
-    if (b < B) Qabs[((size_t)b * kH + h) * kR + kLkv + d] = q[(size_t)b * qs + h * (kDn + kDr) + kDn + d];
+  if (cg == 0) {
+    for (int e = tid; e < 64 * kDr / 8; e += 256) {
+      const int r = e / (kDr / 8), c = e - r * (kDr / 8), b = b0 + r;
+      if (b < B)
+        *(uint4*)(Qabs + ((size_t)b * kH + h) * kR + kLkv + 8 * c) =
+            *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + kDn + 8 * c);
+    }
   }
 }
 
@@ -182,8 +191,8 @@ struct AttnArgs {
   const int32_t* P;
   int B;
   float scale_log2;
-  float* part_o;   // [(G + B)][H][Lkv]
-  float* part_ml;  // [(G + B)][H][2]   (running max in log2 units, sum)
+  bf16_t* part_o;  // [(G + B)][H][Lkv]  latent output of a share, normalised by its own sum
+  float* part_ml;  // [(G + B)][H][2]    (running max in log2 units, sum)
 };
 
 // Wave-uniform load through the scalar cache (the value is read-only for the kernel's lifetime).
@@ -396,9 +405,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void decode_attn_kernel(AttnArg
     __syncthreads();
     // ---- partial result of (this workgroup, sequence b)
     const size_t ps = (size_t)wg + b;
-    float* dst = A.part_o + (ps * kH + head) * kLkv + 4 * g;
+    bf16_t* dst = A.part_o + (ps * kH + head) * kLkv + 4 * g;
+    const float inv_l = 1.f / l_run;
 #pragma unroll
-    for (int mt = 0; mt < kLkv / 16; ++mt) *(f32x4*)(dst + 16 * mt) = o[mt];
+    for (int mt = 0; mt < kLkv / 16; ++mt)
+      *(uint2*)(dst + 16 * mt) = make_uint2(pack_bf16x2(o[mt][0] * inv_l, o[mt][1] * inv_l),
+                                            pack_bf16x2(o[mt][2] * inv_l, o[mt][3] * inv_l));
     if (g == 0) {
       A.part_ml[(ps * kH + head) * 2] = m_run;
       A.part_ml[(ps * kH + head) * 2 + 1] = l_run;
@@ -414,10 +426,11 @@ __device__ __forceinline__ bool wg_nonempty(int w, int N) {
 // ------------------------------------------------------------------------------ combine + W_UV
 // Grid (H, ceil(B/16)).  Merges the partials of 16 sequences for one head, then
 // o[b][h] = o_lat[b][h] @ W_UV[h] on the matrix cores (W_UV[h][c][j] = wkv_b[c][h*256 + 128 + j]).
+// A share's weight in the merge is 2^(m - M) * l (its normalised output times its own sum).
 template <int WK>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                                      const int32_t* __restrict__ P, int B, WeightView W,
-                                                      bf16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml, const int32_t* __restrict__ P,
+                                                      int B, WeightView W, bf16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) bf16_t As[16][kLkv + 8];
   __shared__ __attribute__((aligned(16))) bf16_t Ws[128][kDv + 16];
   const int h = blockIdx.x, b0 = blockIdx.y * 16;
@@ -434,17 +447,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       for (int wq = wf; wq <= wl; ++wq)
         if (wg_nonempty(wq, N)) M = fmaxf(M, part_ml[(((size_t)wq + b) * kH + h) * 2]);
       float L = 0.f;
-      for (int wq = wf; wq <= wl; ++wq) {
-        if (!wg_nonempty(wq, N)) continue;
-        const float* ml = part_ml + (((size_t)wq + b) * kH + h) * 2;
-        const float f = exp2f(ml[0] - M);
-        L += f * ml[1];
-        const float* src = part_o + (((size_t)wq + b) * kH + h) * kLkv + 8 * lane;
-        const f32x4 v0 = *(const f32x4*)src, v1 = *(const f32x4*)(src + 4);
+      // four shares per round, all loads of a round issued together
+      for (int wq0 = wf; wq0 <= wl; wq0 += 4) {
+        float f[4];
+        uint4 v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] += f * v0[e];
-          acc[4 + e] += f * v1[e];
+        for (int u = 0; u < 4; ++u) {
+          const int wq = wq0 + u;
+          const bool ok = wq <= wl && wg_nonempty(wq, N);
+          const size_t ps = ((size_t)(ok ? wq : wf) + b) * kH + h;
+          const float2 ml = *(const float2*)(part_ml + ps * 2);
+          const uint4 x = *(const uint4*)(part_o + ps * kLkv + 8 * lane);
+          v[u] = ok ? x : make_uint4(0, 0, 0, 0);  // an empty share's slot was never written
+          f[u] = ok ? exp2f(ml.x - M) * ml.y : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          L += f[u];
+          const uint32_t wds[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += f[u] * __uint_as_float(wds[e] << 16);
+            acc[2 * e + 1] += f[u] * __uint_as_float(wds[e] & 0xFFFF0000u);
+          }
         }
       }
       const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -492,7 +517,7 @@ struct DecodeLayout {
   bf16_t* Qabs;
   int32_t* P;
   bf16_t* zero_row;
-  float* part_o;
+  bf16_t* part_o;
   float* part_ml;
   size_t bytes;
 };
@@ -509,8 +534,8 @@ DecodeLayout layout(int B, void* base) {
   off += al((size_t)(B + 1) * sizeof(int32_t));
   L.zero_row = (bf16_t*)(p + off);
   off += al((size_t)kR * sizeof(bf16_t));
-  L.part_o = (float*)(p + off);
-  off += al((size_t)(kAttnWGs + B) * kH * kLkv * sizeof(float));
+  L.part_o = (bf16_t*)(p + off);
+  off += al((size_t)(kAttnWGs + B) * kH * kLkv * sizeof(bf16_t));
   L.part_ml = (float*)(p + off);
   off += al((size_t)(kAttnWGs + B) * kH * 2 * sizeof(float));
   L.bytes = off;
@@ -531,7 +556,7 @@ hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cac
                             const WeightView& wkv_b, void* o, const FastDecodeWs& ws, hipStream_t s) {
   const DecodeLayout L = layout(B, ws.base);
   plan_kernel<<<1, 1024, 0, s>>>(ctx, B, L.P, L.zero_row);
-  dim3 fgrid(kH, (B + 63) / 64);
+  dim3 fgrid(kH, kLkv / 128, (B + 63) / 64);
   if (d.wk == W_BF16) fold_kernel<W_BF16><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs);
   else fold_kernel<W_FP8><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs);
   AttnArgs A;

@@ -11,12 +11,13 @@ struct FastDecodeWs {
   size_t bytes = 0;
 };
 
-// Projection GEMM / GEMV: C[M, N] fp32 = A[M, K] (act) @ W[K, N].  `scratch` holds
-// the split-K partial sums, fast_gemm_ws_bytes(M, N, K) bytes (0 when not split).
+// Projection GEMM / GEMV: C[M, N] = A[M, K] (act) @ [W0 | W1], W0 giving output columns
+// [0, n_split) and W1 columns [n_split, N) (n_split >= N: W0 only).  C is left in `out`
+// (fast_gemm_out_bytes(M, N, K) bytes) as split-K partial sums, described by *res.
 bool fast_proj_supported(const Dims& d);
-size_t fast_gemm_ws_bytes(int M, int N, int K);
-hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C, int64_t ldc,
-                     int M, int N, int K, void* scratch, hipStream_t s);
+size_t fast_gemm_out_bytes(int M, int N, int K);
+hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split,
+                     const WeightView& W1, int M, int N, int K, float* out, Partials* res, hipStream_t s);
 
 // Absorbed decode: fold, split-context attention over the paged cache, combine with W_UV.
 bool fast_decode_supported(const Dims& d);

@@ -1,7 +1,9 @@
 // Projection GEMM / GEMV on CDNA4 matrix cores (gfx950):
-//   C[M, N] (fp32) = A[M, K] (bf16, row-major) @ W[K, N] (bf16, or E4M3FN bytes with
-//   fp32 128x128 block scales), W in the [in, out] orientation the NKI projection
-//   kernels take.
+//   C[M, N] (fp32) = A[M, K] (bf16, row-major) @ [W0 | W1] (bf16, or E4M3FN bytes with
+//   fp32 128x128 block scales), weights in the [in, out] orientation the NKI projection
+//   kernels take.  Two weights that read the same activations (the query and kv
+//   down-projections) run as one launch: W0 feeds output columns [0, n_split), W1 the
+//   rest.
 //
 // One workgroup (4 waves) owns a BM x 128 output tile and a K range; K advances in
 // steps of 64 through double-buffered LDS tiles loaded via registers.  A is read
@@ -11,9 +13,9 @@
 // E4M3FN value times a power-of-two block scale is exact in bf16, so the matrix
 // op sees the same numbers the block-scaled weight represents (atlas "Struct
 // MlaWeights", fp8 fields: the GEMV reads one byte per weight and dequantises in
-// the kernel).  Skinny decode shapes split K over extra workgroups; the partial
-// sums are added in a fixed order by a second kernel, so results are bitwise
-// reproducible.
+// the kernel).  Skinny decode shapes split K over extra workgroups; the result is
+// handed on as the split-K partial sums, which the consuming kernel adds in a fixed
+// order, so results are bitwise reproducible.
 #include "mla_fast.h"
 
 namespace mla {
@@ -51,9 +53,9 @@ struct Gemm {
 };
 
 template <int BM, int WM, int WN, int WK>
-__global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda, WeightView W,
-                                                   float* __restrict__ C, int64_t ldc, int M, int N, int K,
-                                                   int k_split, int64_t split_stride) {
+__global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda, WeightView W0,
+                                                   WeightView W1, int n_split, float* __restrict__ C, int64_t ldc,
+                                                   int M, int N, int K, int k_split, int64_t split_stride) {
   using G = Gemm<BM, WM, WN, WK>;
   __shared__ __attribute__((aligned(16))) uint4 As[2][G::A_SLOTS];
   __shared__ __attribute__((aligned(16))) uint4 Ws[2][G::W_SLOTS];
@@ -62,6 +64,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int kbeg = blockIdx.z * k_split, kend = min(K, kbeg + k_split);
   C += (int64_t)blockIdx.z * split_stride;
+  // weight segment of this column tile (n_split is a multiple of BN, so a tile never straddles it)
+  const bool seg1 = n0 >= n_split;
+  const WeightView W = seg1 ? W1 : W0;
+  const int wn0 = seg1 ? n0 - n_split : n0, WN_ = seg1 ? N - n_split : n_split;
 
   uint4 ra[G::A_LOADS], rw[G::W_LOADS];
   auto load = [&](int k0) {
@@ -75,8 +81,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int e = it * 256 + tid, kr = e >> 4, c = e & 15;
-        const int k = k0 + kr, n = n0 + 8 * c;
-        rw[it] = (k < kend && n < N) ? *(const uint4*)((const bf16_t*)W.w + (int64_t)k * W.ld + n)
+        const int k = k0 + kr, n = wn0 + 8 * c;
+        rw[it] = (k < kend && n < WN_) ? *(const uint4*)((const bf16_t*)W.w + (int64_t)k * W.ld + n)
                                      : make_uint4(0, 0, 0, 0);
       }
     } else {
@@ -84,10 +90,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int e = it * 256 + tid, kr = e >> 3, c = e & 7;
-        const int k = k0 + kr, n = n0 + 16 * c;
+        const int k = k0 + kr, n = wn0 + 16 * c;
         uint4 raw = make_uint4(0, 0, 0, 0);
         float s = 0.f;
-        if (k < kend && n < N) {
+        if (k < kend && n < WN_) {
           raw = *(const uint4*)((const uint8_t*)W.w + (int64_t)k * W.ld + n);
           s = W.scale[(k >> 7) * W.scale_ld + (n >> 7)];
         }
@@ -185,18 +191,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
     }
 }
 
-// C[m, n] = sum_z P[z][m, n], z in fixed order.
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ P, int splits, int64_t stride,
-                                                           int M, int N, float* __restrict__ C, int64_t ldc) {
-  const int64_t total = (int64_t)M * N;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = i / N, n = i - m * N;
-    float s = 0.f;
-    for (int z = 0; z < splits; ++z) s += P[z * stride + m * N + n];
-    C[m * ldc + n] = s;
-  }
-}
-
 struct Plan {
   int bm, splits, k_split;
 };
@@ -214,14 +208,24 @@ Plan plan(int M, int N, int K) {
 }
 
 template <int BM, int WM, int WN>
-hipError_t launch(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C, int64_t ldc, int M, int N,
-                  int K, int k_split, int splits, int64_t split_stride, hipStream_t s) {
+hipError_t launch(const Dims& d, const void* A, int64_t lda, const WeightView& W0, const WeightView& W1, int n_split,
+                  float* C, int64_t ldc, int M, int N, int K, int k_split, int splits, int64_t split_stride,
+                  hipStream_t s) {
   dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, splits);
   if (d.wk == W_FP8)
-    gemm_kernel<BM, WM, WN, W_FP8><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W, C, ldc, M, N, K, k_split, split_stride);
+    gemm_kernel<BM, WM, WN, W_FP8><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W0, W1, n_split, C, ldc, M, N, K,
+                                                        k_split, split_stride);
   else
-    gemm_kernel<BM, WM, WN, W_BF16><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W, C, ldc, M, N, K, k_split, split_stride);
+    gemm_kernel<BM, WM, WN, W_BF16><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W0, W1, n_split, C, ldc, M, N, K,
+                                                         k_split, split_stride);
   return hipGetLastError();
+}
+
+hipError_t launch_plan(const Plan& p, const Dims& d, const void* A, int64_t lda, const WeightView& W0,
+                       const WeightView& W1, int n_split, float* C, int64_t ldc, int M, int N, int K, int64_t stride,
+                       hipStream_t s) {
+  return p.bm == 64 ? launch<64, 1, 4>(d, A, lda, W0, W1, n_split, C, ldc, M, N, K, p.k_split, p.splits, stride, s)
+                    : launch<128, 2, 2>(d, A, lda, W0, W1, n_split, C, ldc, M, N, K, p.k_split, p.splits, stride, s);
 }
 
 }  // namespace
@@ -234,29 +238,23 @@ bool fast_proj_supported(const Dims& d) {
          (d.H * d.dv) % 8 == 0;
 }
 
-size_t fast_gemm_ws_bytes(int M, int N, int K) {
-  const Plan p = plan(M, N, K);
-  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+size_t fast_gemm_out_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return (size_t)plan(M, N, K).splits * M * N * sizeof(float);
 }
 
-hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C, int64_t ldc, int M,
-                     int N, int K, void* scratch, hipStream_t s) {
-  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split, const WeightView& W1,
+                     int M, int N, int K, float* out, Partials* res, hipStream_t s) {
   const Plan p = plan(M, N, K);
-  float* out = C;
-  int64_t ld = ldc, stride = 0;
-  if (p.splits > 1) {
-    out = (float*)scratch;
-    ld = N;
-    stride = (int64_t)M * N;
-  }
-  hipError_t e = p.bm == 64 ? launch<64, 1, 4>(d, A, lda, W, out, ld, M, N, K, p.k_split, p.splits, stride, s)
-                            : launch<128, 2, 2>(d, A, lda, W, out, ld, M, N, K, p.k_split, p.splits, stride, s);
-  if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t total = (int64_t)M * N;
-  const int grid = (int)std::min<int64_t>((total + 255) / 256, 2048);
-  split_reduce_kernel<<<grid, 256, 0, s>>>(out, p.splits, stride, M, N, C, ldc);
-  return hipGetLastError();
+  const int64_t stride = (int64_t)M * N;
+  *res = Partials{out, p.splits, stride, N};
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (n_split >= N || n_split % BN == 0)
+    return launch_plan(p, d, A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, stride, s);
+  // segments not aligned to the column tile: one launch each, same split plan and partial layout
+  hipError_t e = launch_plan(p, d, A, lda, W0, W0, n_split, out, N, M, n_split, K, stride, s);
+  if (e != hipSuccess) return e;
+  return launch_plan(p, d, A, lda, W1, W1, N - n_split, out + n_split, N, M, N - n_split, K, stride, s);
 }
 
 }  // namespace mla

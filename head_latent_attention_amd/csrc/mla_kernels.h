@@ -18,30 +18,47 @@ struct Dims {
   int R() const { return Lkv + dr; }
 };
 
+// fp32 matrix given as a sum of split-K partial products:
+//   value(m, n) = sum_{z < splits} p[z * stride + m * ld + n]
+struct Partials {
+  const float* p;
+  int splits;
+  int64_t stride;
+  int64_t ld;
+  Partials offset(int64_t cols) const { return Partials{p + cols, splits, stride, ld}; }
+};
+
+__device__ __forceinline__ float part_ld(const Partials& P, int64_t m, int64_t n) {
+  const float* q = P.p + m * P.ld + n;
+  float v = q[0];
+  for (int z = 1; z < P.splits; ++z) v += q[z * P.stride];
+  return v;
+}
+
 // ---- general (any shape) kernels: SIMT fp32 arithmetic ------------------------------
 // C[M, N] fp32 (row stride ldc) = A[M, K] (act, row stride lda) @ W[K, N]
 hipError_t gemm_simt(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C,
                      int64_t ldc, int M, int N, int K, hipStream_t s);
 
-// Row builder.  Y [T, ldy] fp32 holds [cq (Lq) | c_kv (Lkv) | k_pe (dr)] starting at column 0
-// (cq absent when Lq == 0).  Writes cqn = RMSNorm(cq)*gq (act [T, Lq], if non-null),
+// Row builder.  Yq [T, *] holds cq (Lq columns, absent when Lq == 0), Ykv [T, *] holds
+// [c_kv (Lkv) | k_pe (dr)].  Writes cqn = RMSNorm(cq)*gq (act [T, Lq], if non-null),
 // cn = RMSNorm(c_kv)*gkv (act [T, Lkv], if non-null), the cache row [cn | RoPE(k_pe)] at
 // slot_mapping[t] (if cache and slot_mapping are non-null), and K[t, h, dn:] = RoPE(k_pe)
 // for every head (if kbuf is non-null).
-hipError_t row_builder(const Dims& d, const float* Y, int64_t ldy, int T, const float* gq,
+hipError_t row_builder(const Dims& d, const Partials& Yq, const Partials& Ykv, int T, const float* gq,
                        const float* gkv, const float* cosT, const float* sinT, void* cqn, void* cn,
                        void* cache, int64_t n_slots, const int32_t* slot_mapping, void* kbuf,
                        hipStream_t s);
 
 // q[t, h, :] (act) = [Y[t, h*dqk : h*dqk+dn] | RoPE(Y[t, h*dqk+dn : (h+1)*dqk])]
-hipError_t q_epilogue(const Dims& d, const float* Y, int64_t ldy, int T, const float* cosT,
-                      const float* sinT, void* q, hipStream_t s);
+hipError_t q_epilogue(const Dims& d, const Partials& Y, int T, const float* cosT, const float* sinT, void* q,
+                      hipStream_t s);
 
-// KV[t, h*(dn+dv) + j] fp32 -> K[t, h, j] (j < dn) and V[t, h, j - dn] (act)
-hipError_t kv_split(const Dims& d, const float* KV, int T, void* k, void* v, hipStream_t s);
+// KV[t, h*(dn+dv) + j] -> K[t, h, j] (j < dn) and V[t, h, j - dn] (act)
+hipError_t kv_split(const Dims& d, const Partials& KV, int T, void* k, void* v, hipStream_t s);
 
-// y (act, [M, N]) = Y (fp32, [M, N])
-hipError_t cast_rows(const Dims& d, const float* Y, int64_t n, void* y, hipStream_t s);
+// y (act, [M, N]) = Y
+hipError_t cast_rows(const Dims& d, const Partials& Y, int M, int N, void* y, hipStream_t s);
 
 // Absorbed decode, general version.  Qabs fp32 [B, H, R] = [q_nope @ W_UK | q_pe].
 hipError_t fold_simt(const Dims& d, const void* q, int B, const WeightView& wkv_b, float* Qabs,

@@ -79,27 +79,36 @@ hipError_t gemm_simt(const Dims& d, const void* A, int64_t lda, const WeightView
 
 // ===================================================================================
 // Row builder: RMSNorm of both latents, RoPE of k_pe, cache-row scatter, k_pe broadcast.
-// One block of 256 threads per token.
+// Grid (tokens, 2): y = 0 normalises the query latent, y = 1 builds the kv row.
 // ===================================================================================
 template <typename T>
 __global__ __launch_bounds__(256) void row_builder_kernel(
-    const float* __restrict__ Y, int64_t ldy, int Lq, int Lkv, int dr, const float* __restrict__ gq,
-    const float* __restrict__ gkv, float eps, const float* __restrict__ cosT,
-    const float* __restrict__ sinT, T* __restrict__ cqn, T* __restrict__ cn, T* __restrict__ cache,
-    int64_t n_slots, const int32_t* __restrict__ slot_mapping, T* __restrict__ kbuf, int H, int dn) {
+    Partials Yq, Partials Ykv, int Lq, int Lkv, int dr, const float* __restrict__ gq, const float* __restrict__ gkv, float eps,
+    const float* __restrict__ cosT, const float* __restrict__ sinT, T* __restrict__ cqn, T* __restrict__ cn,
+    T* __restrict__ cache, int64_t n_slots, const int32_t* __restrict__ slot_mapping, T* __restrict__ kbuf, int H,
+    int dn) {
   __shared__ float red[16];
   const int t = blockIdx.x;
-  const float* y = Y + (size_t)t * ldy;
   const int R = Lkv + dr, dqk = dn + dr;
-  if (Lq > 0 && cqn != nullptr) {
+  // the partial sums are re-read for the second pass (it hits L2)
+  if (blockIdx.y == 0) {
+    // query latent: RMSNorm(cq) * gq
+    if (Lq == 0 || cqn == nullptr) return;
     float ss = 0.f;
-    for (int i = threadIdx.x; i < Lq; i += blockDim.x) ss += y[i] * y[i];
-    float r = rsqrtf(block_sum(ss, red) / (float)Lq + eps);
-    for (int i = threadIdx.x; i < Lq; i += blockDim.x) Act<T>::st(cqn, (size_t)t * Lq + i, y[i] * r * gq[i]);
+    for (int i = threadIdx.x; i < Lq; i += blockDim.x) {
+      const float v = part_ld(Yq, t, i);
+      ss += v * v;
+    }
+    const float r = rsqrtf(block_sum(ss, red) / (float)Lq + eps);
+    for (int i = threadIdx.x; i < Lq; i += blockDim.x) Act<T>::st(cqn, (size_t)t * Lq + i, part_ld(Yq, t, i) * r * gq[i]);
+    return;
   }
-  const float* ckv = y + Lq;
+  // kv latent: RMSNorm(c_kv) * gkv, RoPE(k_pe), cache row, k_pe broadcast
   float ss = 0.f;
-  for (int i = threadIdx.x; i < Lkv; i += blockDim.x) ss += ckv[i] * ckv[i];
+  for (int i = threadIdx.x; i < Lkv; i += blockDim.x) {
+    const float v = part_ld(Ykv, t, i);
+    ss += v * v;
+  }
   const float r = rsqrtf(block_sum(ss, red) / (float)Lkv + eps);
   int64_t slot = -1;
   if (cache != nullptr && slot_mapping != nullptr) {
@@ -107,23 +116,22 @@ __global__ __launch_bounds__(256) void row_builder_kernel(
     if (slot >= n_slots) slot = -1;
   }
   for (int i = threadIdx.x; i < Lkv; i += blockDim.x) {
-    float v = Act<T>::round(ckv[i] * r * gkv[i]);
+    const float v = Act<T>::round(part_ld(Ykv, t, i) * r * gkv[i]);
     if (cn) Act<T>::st(cn, (size_t)t * Lkv + i, v);
     if (slot >= 0) Act<T>::st(cache, (size_t)slot * R + i, v);
   }
-  const float* pe = ckv + Lkv;
   const int half = dr >> 1;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    float c = cosT[(size_t)t * half + i], sn = sinT[(size_t)t * half + i];
-    float x0 = pe[2 * i], x1 = pe[2 * i + 1];
-    float y0 = Act<T>::round(x0 * c - x1 * sn), y1 = Act<T>::round(x0 * sn + x1 * c);
+    const float c = cosT[(size_t)t * half + i], sn = sinT[(size_t)t * half + i];
+    const float x0 = part_ld(Ykv, t, Lkv + 2 * i), x1 = part_ld(Ykv, t, Lkv + 2 * i + 1);
+    const float y0 = Act<T>::round(x0 * c - x1 * sn), y1 = Act<T>::round(x0 * sn + x1 * c);
     if (slot >= 0) {
       Act<T>::st(cache, (size_t)slot * R + Lkv + 2 * i, y0);
       Act<T>::st(cache, (size_t)slot * R + Lkv + 2 * i + 1, y1);
     }
     if (kbuf) {
       for (int h = 0; h < H; ++h) {
-        size_t base = ((size_t)t * H + h) * dqk + dn + 2 * i;
+        const size_t base = ((size_t)t * H + h) * dqk + dn + 2 * i;
         Act<T>::st(kbuf, base, y0);
         Act<T>::st(kbuf, base + 1, y1);
       }
@@ -131,19 +139,19 @@ __global__ __launch_bounds__(256) void row_builder_kernel(
   }
 }
 
-hipError_t row_builder(const Dims& d, const float* Y, int64_t ldy, int T, const float* gq,
-                       const float* gkv, const float* cosT, const float* sinT, void* cqn, void* cn,
-                       void* cache, int64_t n_slots, const int32_t* slot_mapping, void* kbuf,
-                       hipStream_t s) {
+hipError_t row_builder(const Dims& d, const Partials& Yq, const Partials& Ykv, int T, const float* gq, const float* gkv, const float* cosT,
+                       const float* sinT, void* cqn, void* cn, void* cache, int64_t n_slots,
+                       const int32_t* slot_mapping, void* kbuf, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  dim3 grid(T, 2);
   if (d.act == 0)
-    row_builder_kernel<float><<<T, 256, 0, s>>>(Y, ldy, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT,
-                                                 (float*)cqn, (float*)cn, (float*)cache, n_slots,
-                                                 slot_mapping, (float*)kbuf, d.H, d.dn);
+    row_builder_kernel<float><<<grid, 256, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT, (float*)cqn,
+                                                    (float*)cn, (float*)cache, n_slots, slot_mapping, (float*)kbuf,
+                                                    d.H, d.dn);
   else
-    row_builder_kernel<bf16_t><<<T, 256, 0, s>>>(Y, ldy, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT,
-                                                  (bf16_t*)cqn, (bf16_t*)cn, (bf16_t*)cache, n_slots,
-                                                  slot_mapping, (bf16_t*)kbuf, d.H, d.dn);
+    row_builder_kernel<bf16_t><<<grid, 256, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT, (bf16_t*)cqn,
+                                                     (bf16_t*)cn, (bf16_t*)cache, n_slots, slot_mapping,
+                                                     (bf16_t*)kbuf, d.H, d.dn);
   return hipGetLastError();
 }
 
@@ -151,35 +159,32 @@ hipError_t row_builder(const Dims& d, const float* Y, int64_t ldy, int T, const 
 // Query epilogue: per-head RoPE on the trailing dr dims and the cast to act.
 // ===================================================================================
 template <typename T>
-__global__ __launch_bounds__(256) void q_epilogue_kernel(const float* __restrict__ Y, int64_t ldy,
-                                                         int H, int dn, int dr,
+__global__ __launch_bounds__(256) void q_epilogue_kernel(Partials Y, int H, int dn, int dr,
                                                          const float* __restrict__ cosT,
-                                                         const float* __restrict__ sinT,
-                                                         T* __restrict__ q) {
-  const int t = blockIdx.x, dqk = dn + dr, half = dr >> 1;
-  const float* y = Y + (size_t)t * ldy;
-  for (int e = threadIdx.x; e < H * dqk; e += blockDim.x) {
-    const int h = e / dqk, dd = e - h * dqk;
-    float v;
-    if (dd < dn) {
-      v = y[e];
-    } else {
-      const int i = (dd - dn) >> 1;
-      const float c = cosT[(size_t)t * half + i], sn = sinT[(size_t)t * half + i];
-      const float x0 = y[h * dqk + dn + 2 * i], x1 = y[h * dqk + dn + 2 * i + 1];
-      v = ((dd - dn) & 1) ? (x0 * sn + x1 * c) : (x0 * c - x1 * sn);
-    }
-    Act<T>::st(q, (size_t)t * H * dqk + e, v);
+                                                         const float* __restrict__ sinT, T* __restrict__ q) {
+  // one thread per (token, head, rope pair or nope element); grid (T, ceil(H * (dn + dr/2) / 256))
+  const int t = blockIdx.x, dqk = dn + dr, half = dr >> 1, per_head = dn + half;
+  const int e = blockIdx.y * blockDim.x + threadIdx.x;
+  if (e >= H * per_head) return;
+  const int h = e / per_head, u = e - h * per_head;
+  const size_t o = (size_t)t * H * dqk + (size_t)h * dqk;
+  if (u < dn) {
+    Act<T>::st(q, o + u, part_ld(Y, t, (int64_t)h * dqk + u));
+  } else {
+    const int i = u - dn;
+    const float c = cosT[(size_t)t * half + i], sn = sinT[(size_t)t * half + i];
+    const float x0 = part_ld(Y, t, (int64_t)h * dqk + dn + 2 * i), x1 = part_ld(Y, t, (int64_t)h * dqk + dn + 2 * i + 1);
+    Act<T>::st(q, o + dn + 2 * i, x0 * c - x1 * sn);
+    Act<T>::st(q, o + dn + 2 * i + 1, x0 * sn + x1 * c);
   }
 }
 
-hipError_t q_epilogue(const Dims& d, const float* Y, int64_t ldy, int T, const float* cosT,
-                      const float* sinT, void* q, hipStream_t s) {
+hipError_t q_epilogue(const Dims& d, const Partials& Y, int T, const float* cosT, const float* sinT, void* q,
+                      hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (d.act == 0)
-    q_epilogue_kernel<float><<<T, 256, 0, s>>>(Y, ldy, d.H, d.dn, d.dr, cosT, sinT, (float*)q);
-  else
-    q_epilogue_kernel<bf16_t><<<T, 256, 0, s>>>(Y, ldy, d.H, d.dn, d.dr, cosT, sinT, (bf16_t*)q);
+  dim3 grid(T, (d.H * (d.dn + d.dr / 2) + 255) / 256);
+  if (d.act == 0) q_epilogue_kernel<float><<<grid, 256, 0, s>>>(Y, d.H, d.dn, d.dr, cosT, sinT, (float*)q);
+  else q_epilogue_kernel<bf16_t><<<grid, 256, 0, s>>>(Y, d.H, d.dn, d.dr, cosT, sinT, (bf16_t*)q);
   return hipGetLastError();
 }
 
@@ -187,36 +192,40 @@ hipError_t q_epilogue(const Dims& d, const float* Y, int64_t ldy, int T, const f
 // KV split: [k_nope | v] per head -> K[..., :dn], V.
 // ===================================================================================
 template <typename T>
-__global__ __launch_bounds__(256) void kv_split_kernel(const float* __restrict__ KV, int H, int dn,
-                                                       int dr, int dv, T* __restrict__ k,
+__global__ __launch_bounds__(256) void kv_split_kernel(Partials KV, int H, int dn, int dr, int dv, T* __restrict__ k,
                                                        T* __restrict__ v) {
   const int t = blockIdx.x, w = dn + dv, dqk = dn + dr;
-  const float* y = KV + (size_t)t * H * w;
-  for (int e = threadIdx.x; e < H * w; e += blockDim.x) {
-    const int h = e / w, j = e - h * w;
-    if (j < dn) Act<T>::st(k, ((size_t)t * H + h) * dqk + j, y[e]);
-    else Act<T>::st(v, ((size_t)t * H + h) * dv + (j - dn), y[e]);
-  }
+  const int e = blockIdx.y * blockDim.x + threadIdx.x;
+  if (e >= H * w) return;
+  const int h = e / w, j = e - h * w;
+  const float x = part_ld(KV, t, e);
+  if (j < dn) Act<T>::st(k, ((size_t)t * H + h) * dqk + j, x);
+  else Act<T>::st(v, ((size_t)t * H + h) * dv + (j - dn), x);
 }
 
-hipError_t kv_split(const Dims& d, const float* KV, int T, void* k, void* v, hipStream_t s) {
+hipError_t kv_split(const Dims& d, const Partials& KV, int T, void* k, void* v, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (d.act == 0) kv_split_kernel<float><<<T, 256, 0, s>>>(KV, d.H, d.dn, d.dr, d.dv, (float*)k, (float*)v);
-  else kv_split_kernel<bf16_t><<<T, 256, 0, s>>>(KV, d.H, d.dn, d.dr, d.dv, (bf16_t*)k, (bf16_t*)v);
+  dim3 grid(T, (d.H * (d.dn + d.dv) + 255) / 256);
+  if (d.act == 0) kv_split_kernel<float><<<grid, 256, 0, s>>>(KV, d.H, d.dn, d.dr, d.dv, (float*)k, (float*)v);
+  else kv_split_kernel<bf16_t><<<grid, 256, 0, s>>>(KV, d.H, d.dn, d.dr, d.dv, (bf16_t*)k, (bf16_t*)v);
   return hipGetLastError();
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ Y, int64_t n, T* __restrict__ y) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    Act<T>::st(y, i, Y[i]);
+__global__ __launch_bounds__(256) void cast_kernel(Partials Y, int M, int N, T* __restrict__ y) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / N, n = i - m * N;
+    Act<T>::st(y, i, part_ld(Y, m, n));
+  }
 }
 
-hipError_t cast_rows(const Dims& d, const float* Y, int64_t n, void* y, hipStream_t s) {
+hipError_t cast_rows(const Dims& d, const Partials& Y, int M, int N, void* y, hipStream_t s) {
+  const int64_t n = (int64_t)M * N;
   if (n <= 0) return hipSuccess;
-  int grid = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-  if (d.act == 0) cast_kernel<float><<<grid, 256, 0, s>>>(Y, n, (float*)y);
-  else cast_kernel<bf16_t><<<grid, 256, 0, s>>>(Y, n, (bf16_t*)y);
+  const int grid = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+  if (d.act == 0) cast_kernel<float><<<grid, 256, 0, s>>>(Y, M, N, (float*)y);
+  else cast_kernel<bf16_t><<<grid, 256, 0, s>>>(Y, M, N, (bf16_t*)y);
   return hipGetLastError();
 }
 
@@ -470,12 +479,10 @@ hipError_t prefill_attn_simt(const Dims& d, const void* q, const void* k, const 
   dim3 grid((T + 15) / 16, d.H);
   const int dqk = d.dqk();
   const size_t sh = sizeof(float) * (16 * dqk + 32 * (dqk + 1) + 32 * d.dv + 16 * 32);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)prefill_attn_simt_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    hipFuncSetAttribute((const void*)prefill_attn_simt_kernel<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
+  // set on every call: the attribute is per device and the call is host-side only
+  const void* fn = d.act == 0 ? (const void*)prefill_attn_simt_kernel<float> : (const void*)prefill_attn_simt_kernel<bf16_t>;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+  if (e != hipSuccess) return e;
   if (d.act == 0)
     prefill_attn_simt_kernel<float><<<grid, 256, sh, s>>>((const float*)q, (const float*)k, (const float*)v, T,
                                                            d.H, dqk, d.dv, d.scale, (float*)o);
