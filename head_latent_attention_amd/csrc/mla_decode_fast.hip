@@ -43,10 +43,6 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^(s - m) <= 256 b
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
-
 // Eight consecutive weight elements (k fixed, n..n+7) as bf16; fp8 codes are
 // converted exactly (E4M3FN value times a power-of-two block scale).
 template <int WK>
@@ -201,11 +197,6 @@ __device__ __forceinline__ T sload(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
 // Block id of the (block-size aligned) 32-token sub-tile starting at token tok0, or -1.
 __device__ __forceinline__ int sub_tile_block(const AttnArgs& A, int b, int tok0, int tok_hi) {
   if (tok0 >= tok_hi) return -1;
@@ -216,8 +207,9 @@ __device__ __forceinline__ int sub_tile_block(const AttnArgs& A, int b, int tok0
 // Direct global->LDS copies of one 32-token sub-tile of block `blk`.  The block size is a
 // multiple of 32, so the sub-tile's rows are 32 consecutive rows of one cache block.  Wave
 // w copies the latent parts of tokens [4w, 4w + 4) (one 64-lane copy each); waves 0..3
-// also copy the rope parts of tokens [8w, 8w + 8) (8 lanes per token).  Rows past the
-// context or in an invalid block come from the zero row.
+// also copy the rope parts of tokens [8w, 8w + 8) (8 lanes per token).  Latent parts of
+// rows past the context, and all of an invalid block, come from the zero row: the value
+// product multiplies them by a zero probability, which must not meet a NaN.
 __device__ __forceinline__ void issue_tile_copy(const AttnArgs& A, int blk, int tok0, int tok_hi,
                                                 uint4* __restrict__ buf, int w, int lane) {
   const bool blk_ok = blk >= 0 && blk < A.n_blocks;
@@ -228,12 +220,16 @@ __device__ __forceinline__ void issue_tile_copy(const AttnArgs& A, int blk, int 
   for (int i = 0; i < 4; ++i) {
     const int t = 4 * w + i;
     const bf16_t* row = (blk_ok && tok0 + t < tok_hi) ? base + t * kR : A.zero_row;  // wave-uniform
-    dma16(row + 8 * (l ^ swz_c(t)), buf + 64 * t);
+    dma16_buf(row, kR * 2, 16 * (l ^ swz_c(t)), buf + 64 * t);
   }
   if (w < 4) {
-    const int t = 8 * w + (l >> 3);
-    const bf16_t* row = (blk_ok && tok0 + t < tok_hi) ? base + t * kR : A.zero_row;
-    dma16(row + kLkv + 8 * ((l & 7) ^ swz_pe(t)), buf + kCSlots + 64 * w);
+    // rope parts of tokens [8w, 8w + 8), 8 lanes each.  Rows past the context but inside the
+    // block are copied as they are: only the scores read them, and those are masked.
+    const int t0 = 8 * w, t = t0 + (l >> 3);
+    const bf16_t* slab = blk_ok ? base + t0 * kR : A.zero_row;  // wave-uniform
+    const uint32_t row = blk_ok ? (uint32_t)(l >> 3) : 0u;
+    dma16_buf(slab, blk_ok ? 8 * kR * 2 : kR * 2, row * kR * 2 + kLkv * 2 + 16 * ((l & 7) ^ swz_pe(t)),
+              buf + kCSlots + 64 * w);
   }
 }
 
@@ -268,57 +264,84 @@ __device__ __forceinline__ void wait_copies(int w, int later) {
   }
 }
 
-// One 32-token sub-tile.  `nxt` (the buffer three sub-tiles ahead) is refilled and,
-// when `compute` is set, `buf` is consumed.  Both are restrict-qualified so that, once
-// inlined, the copies into `nxt` carry alias scopes disjoint from the reads of `buf`;
-// every copy of a segment (also the first three) is issued by this one inlined call
-// site, so the compiler never makes the score/value reads wait for copies in flight.
-__device__ __forceinline__ void attn_sub_tile(const AttnArgs& A, int tok0, int tok_hi, int tok_pf, int blk_pf,
-                                              bool compute, const uint4* __restrict__ buf, uint4* __restrict__ nxt,
-                                              const bf16x8 (&qf)[kR / 32], f32x4 (&o)[kLkv / 16], float& m_run,
-                                              float& l_run, int w, int lane) {
+// Byte offsets, within an LDS buffer, of this lane's operand chunks.  (4*ks + g) ^ swz_c(j) equals
+// 16*(ks >> 2) + ((4*(ks & 3) + g) ^ swz_c(j)) as swz_c < 16, so four lane offsets plus immediates
+// cover the 16 latent k-steps of the score reads (two more the rope k-steps); likewise
+// (2*mt) ^ vU = 16*(mt >> 3) + ((2*(mt & 7)) ^ vU) leaves eight offsets for the value reads.
+struct LaneOffsets {
+  int s[4], pe[2], v[8];
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   const int g = lane >> 4, j = lane & 15;
-  if (tok_pf < tok_hi) issue_tile_copy(A, blk_pf, tok_pf, tok_hi, nxt, w, lane);
-  if (!compute) return;
-  const char* bbase = (const char*)buf;
-  // ---- scores S^T[token][head]: 2 token tiles of 16; k-steps 0..15 latent, 16..17 rope
-  // lane address parts: token 16*mt + j has the swizzle of j
+  LaneOffsets L;
   const int sj = swz_c(j), pj = swz_pe(j);
-  const int srow = 64 * j * 16, prow = (kCSlots + 8 * j) * 16;
-  auto s_addr = [&](int ks, int mt) -> const uint4* {
-    if (ks < 16) return (const uint4*)(bbase + srow + 16 * 64 * 16 * mt + ((4 * ks + g) ^ sj) * 16);
-    return (const uint4*)(bbase + prow + 16 * 8 * 16 * mt + ((4 * (ks - 16) + g) ^ pj) * 16);
-  };
-  f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  bf16x8 a_nx = as_bf16x8(*s_addr(0, 0));
 #pragma unroll
-  for (int it = 0; it < 2 * (kR / 32); ++it) {
+  for (int q = 0; q < 4; ++q) L.s[q] = (64 * j + ((4 * q + g) ^ sj)) * 16;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) L.pe[q] = (kCSlots + 8 * j + ((4 * q + g) ^ pj)) * 16;
+  // value reads: tokens {0,16} + 4*g + j/4 share the swizzle of 4*g + j/4; chunk 2*mt + half
+  const int tA = 4 * g + (j >> 2);
+  const int vU = ((j >> 1) & 1) ^ swz_c(tA);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) L.v[q] = 64 * tA * 16 + (j & 1) * 8 + ((2 * q) ^ vU) * 16;
+  return L;
+}
+
+constexpr int kSPre = 4;  // score operand reads in flight per wave
+constexpr int kVPre = 4;  // value operand reads in flight per wave
+
+// Scores of one sub-tile for this wave's 16 heads, then the online softmax (log2 domain,
+// lazy rescale of the running output).  Returns P^T as the B operand of the value product.
+__device__ __forceinline__ bf16x8 scores_softmax(const AttnArgs& A, int tok0, int tok_hi, const char* bbase,
+                                                 const LaneOffsets& LO, const bf16x8 (&qf)[kR / 32],
+                                                 f32x4 (&o)[kLkv / 16], float& m_run, float& l_run, int lane) {
+  const int g = lane >> 4;
+  // ---- S^T[token][head]: 2 token tiles of 16; k-steps 0..15 latent, 16..17 rope
+  auto s_read = [&](int it) -> bf16x8 {
     const int ks = it >> 1, mt = it & 1;
-    const bf16x8 a = a_nx;
-    if (it + 1 < 2 * (kR / 32)) a_nx = as_bf16x8(*s_addr((it + 1) >> 1, (it + 1) & 1));
-    s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[mt], 0, 0, 0);
-  }
-  // ---- online softmax (log2 domain); the lane's head is 16*w + j
-  float x[2][4];
-  float mx = -INFINITY;
+    if (ks < 16) return as_bf16x8(*(const uint4*)(bbase + LO.s[ks & 3] + 256 * (ks >> 2) + 16 * 64 * 16 * mt));
+    return as_bf16x8(*(const uint4*)(bbase + LO.pe[ks - 16] + 16 * 8 * 16 * mt));
+  };
+  constexpr int kSIt = 2 * (kR / 32);
+  f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  bf16x8 ring[kSPre];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int it = 0; it < kSPre; ++it) ring[it] = s_read(it);
+  // the program order below is the schedule: kSPre reads stay in flight ahead of the matrix ops
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int it = 0; it < kSIt; ++it) {
+    s[it & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[it % kSPre], qf[it >> 1], s[it & 1], 0, 0, 0);
+    if (it + kSPre < kSIt) ring[it % kSPre] = s_read(it + kSPre);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // ---- online softmax; the lane's head is 16*w + j, its tokens 16*mt + 4*g + i
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = s[0][i] * A.scale_log2;
+    x[4 + i] = s[1][i] * A.scale_log2;
+  }
+  if (tok0 + kSub > tok_hi) {  // only the last sub-tile of a segment has tokens past the end
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = tok0 + 16 * mt + 4 * g + i;
-      x[mt][i] = tok < tok_hi ? s[mt][i] * A.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[mt][i]);
+      if (tok0 + 4 * g + i >= tok_hi) x[i] = -INFINITY;
+      if (tok0 + 16 + 4 * g + i >= tok_hi) x[4 + i] = -INFINITY;
     }
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
   mx = xmax16_32(mx);
   const float m_new = (m_run == -INFINITY || mx > m_run + kRescaleThreshold) ? mx : m_run;
   const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
   float p[8];
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(x[0][i] - m_new);
-    p[4 + i] = __builtin_amdgcn_exp2f(x[1][i] - m_new);
-    sum += p[i] + p[4 + i];
+  for (int i = 0; i < 8; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+    sum += p[i];
   }
   const bf16x8 pb = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                          pack_bf16x2(p[6], p[7])));
@@ -329,26 +352,79 @@ __device__ __forceinline__ void attn_sub_tile(const AttnArgs& A, int tok0, int t
 #pragma unroll
     for (int mt = 0; mt < kLkv / 16; ++mt) o[mt] *= corr;
   }
-  // ---- O^T[latent][head] += V^T P^T over the 32 tokens (one k-step)
-  // tokens {0,16} + 4*g + j/4 share the swizzle of 4*g + j/4; chunk 2*mt + half
-  const int tA = 4 * g + (j >> 2);
-  const int vU = ((j >> 1) & 1) ^ swz_c(tA);
-  const int vrow = 64 * tA * 16 + (j & 1) * 8;
-  auto v_addr = [&](int mt) -> const char* { return bbase + vrow + ((2 * mt) ^ vU) * 16; };
-  bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)v_addr(0));
-  bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v_addr(0) + 16 * 64 * 16));
+  return pb;
+}
+
+// O^T[latent][head] += V^T P^T over one sub-tile's 32 tokens (one k-step per latent tile).
+__device__ __forceinline__ void value_product(const char* bbase, const LaneOffsets& LO, const bf16x8& pb,
+                                              f32x4 (&o)[kLkv / 16]) {
+  auto v_read = [&](int mt) -> bf16x8 {
+    const char* q = bbase + LO.v[mt & 7] + 256 * (mt >> 3);
+    const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
+    const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(q + 16 * 64 * 16));
+    return __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  bf16x8 vring[kVPre];
+#pragma unroll
+  for (int mt = 0; mt < kVPre; ++mt) vring[mt] = v_read(mt);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mt = 0; mt < kLkv / 16; ++mt) {
-    const bf16x8 a = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-    if (mt + 1 < kLkv / 16) {
-      b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)v_addr(mt + 1));
-      b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v_addr(mt + 1) + 16 * 64 * 16));
-    }
-    o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
+    o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vring[mt % kVPre], pb, o[mt], 0, 0, 0);
+    if (mt + kVPre < kLkv / 16) vring[mt % kVPre] = v_read(mt + kVPre);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// 512 threads = 8 waves; wave w owns heads [16w, 16w + 16).
+// One step: the copies of a later sub-tile go into `nxt`; then, when `compute` is set, this
+// wave takes sub-tile `cur` (tokens from tok0): scores, softmax and value product.  Both
+// buffers are restrict-qualified so that, once inlined, the copies into `nxt` carry alias
+// scopes disjoint from the reads of `cur`; every copy is issued by this one inlined call
+// site, so the compiler never makes the score/value reads wait for copies in flight.
+__device__ __forceinline__ void attn_step(const AttnArgs& A, int tok0, int tok_hi, bool copy, int blk_pf, int tok_pf,
+                                          int tok_hi_pf, bool compute, const uint4* __restrict__ cur,
+                                          uint4* __restrict__ nxt, const LaneOffsets& LO, const bf16x8 (&qf)[kR / 32],
+                                          f32x4 (&o)[kLkv / 16], float& m_run, float& l_run, int w, int lane) {
+  if (copy) issue_tile_copy(A, blk_pf, tok_pf, tok_hi_pf, nxt, w, lane);
+  if (!compute) return;
+  const bf16x8 pb = scores_softmax(A, tok0, tok_hi, (const char*)cur, LO, qf, o, m_run, l_run, lane);
+  value_product((const char*)cur, LO, pb, o);
+}
+
+constexpr int kPf = 3;  // sub-tiles whose copies are issued ahead of the one being computed
+static_assert(kNBuf >= kPf + 1, "buffers: the current one and the ones in flight");
+
+// A position in a workgroup's share of the work list: sequence b, sub-tile starting at
+// token tok, the share's part of sequence b ending at token tok_hi.
+struct Cursor {
+  int b, tok, tok_hi;
+};
+
+// Part of sequence b inside tiles [t_lo, t_hi): tokens [*lo, *hi); false when empty.
+__device__ __forceinline__ bool share_of(const AttnArgs& A, int b, int t_lo, int t_hi, int* lo, int* hi) {
+  const int p0 = sload(A.P + b), p1 = sload(A.P + b + 1);
+  const int a = max(t_lo, p0), e = min(t_hi, p1);
+  if (a >= e) return false;
+  *lo = (a - p0) * kTile;
+  *hi = min(sload(A.ctx + b), (e - p0) * kTile);
+  return true;
+}
+
+// Moves c to the first sub-tile of the next non-empty sequence of the share (b = B when none).
+__device__ __forceinline__ void next_segment(const AttnArgs& A, int t_lo, int t_hi, Cursor& c) {
+  for (++c.b; c.b < A.B; ++c.b)
+    if (share_of(A, c.b, t_lo, t_hi, &c.tok, &c.tok_hi)) return;
+}
+
+__device__ __forceinline__ void advance(const AttnArgs& A, int t_lo, int t_hi, Cursor& c) {
+  c.tok += kSub;
+  if (c.tok >= c.tok_hi) next_segment(A, t_lo, t_hi, c);
+}
+
+// 512 threads = 8 waves; wave w owns heads [16w, 16w + 16).  The workgroup's share of the
+// work list is one stream of 32-token sub-tiles across sequence boundaries: the copies run
+// kPf sub-tiles ahead of the computation without draining at a boundary, where the
+// finished sequence's partial result is written and the next sequence's query loaded.
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void decode_attn_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) uint4 kv[kNBuf][kBufSlots];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
@@ -364,57 +440,65 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void decode_attn_kernel(AttnArg
     if (sload(A.P + mid) <= t_lo) lo = mid;
     else hi = mid - 1;
   }
-  int b = lo;
-  int tile = t_lo;
+  Cursor cc{lo - 1, 0, 0};
+  next_segment(A, t_lo, t_hi, cc);
+  // sub-tiles of the whole share
+  int total = 0;
+  for (Cursor c = cc; c.b < A.B; next_segment(A, t_lo, t_hi, c)) total += (c.tok_hi - c.tok + kSub - 1) / kSub;
+  Cursor pc = cc;
   const int head = 16 * w + j;
-  while (tile < t_hi) {
-    while (sload(A.P + b + 1) <= tile) ++b;
-    const int pb0 = sload(A.P + b);
-    const int seg_end = min(t_hi, sload(A.P + b + 1));
-    const int tok_lo = (tile - pb0) * kTile;
-    const int tok_hi = min(sload(A.ctx + b), (seg_end - pb0) * kTile);
-    tile = seg_end;
-    const int n_sub = (tok_hi - tok_lo + kSub - 1) / kSub;
-    // Q^T fragments of this wave's 16 heads (B operand of S^T = K Q^T)
-    bf16x8 qf[kR / 32];
-    {
-      const bf16_t* qrow = A.Qabs + ((size_t)b * kH + head) * kR + 8 * g;
+  const LaneOffsets LO = lane_offsets(lane);
+  // The loads complete before the function returns (an explicit wait for every memory
+  // operation of the wave), so the compiler sees the fragments ready on every later step and
+  // never waits for the copies in flight before a score product.
+  auto load_q = [&](int b, bf16x8 (&qf)[kR / 32]) {
+    const bf16_t* qrow = A.Qabs + ((size_t)b * kH + head) * kR + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < kR / 32; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qrow + 32 * ks));
-    }
-    // nothing but cache-row copies may be in flight inside the loop below
-    __builtin_amdgcn_s_waitcnt(0);
-    f32x4 o[kLkv / 16];
+    for (int ks = 0; ks < kR / 32; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qrow + 32 * ks));
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
+  // Q^T fragments of this wave's 16 heads (B operand of S^T = K Q^T)
+  bf16x8 qf[kR / 32];
+  load_q(cc.b, qf);
+  f32x4 o[kLkv / 16];
 #pragma unroll
-    for (int mt = 0; mt < kLkv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    // iterations st < 0 only put the first kNBuf - 1 sub-tiles in flight
-    for (int st = -(kNBuf - 1); st < n_sub; ++st) {
-      const int tok_pf = tok_lo + (st + kNBuf - 1) * kSub;
-      const int blk_pf = sub_tile_block(A, b, tok_pf, tok_hi);  // scalar load, overlaps the barrier
-      if (st >= 0) {
-        // copies issued after sub-tile st's: those of st+1 and st+2 (when they exist)
-        wait_copies(w, min(n_sub - 1 - st, kNBuf - 2));
-        __syncthreads();
-      }
-      const int sb = st < 0 ? 0 : st % kNBuf;
-      attn_sub_tile(A, tok_lo + st * kSub, tok_hi, tok_pf, blk_pf, st >= 0, kv[sb], kv[(st + 2 * kNBuf - 1) % kNBuf], qf,
-                    o, m_run, l_run, w, lane);
+  for (int mt = 0; mt < kLkv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  // steps s < 0 only put the first kPf sub-tiles in flight
+  for (int s = -kPf; s < total; ++s) {
+    const bool copy = s + kPf < total;
+    const int blk_pf = copy ? sub_tile_block(A, pc.b, pc.tok, pc.tok_hi) : -1;  // scalar load, overlaps the barrier
+    if (s >= 0) {
+      // copies issued after sub-tile s's: those of the next min(kPf - 1, ...) sub-tiles.  Other
+      // memory operations issued in between (partial results, query loads) only make this
+      // wait longer, never shorter.
+      wait_copies(w, min(total - 1 - s, kPf - 1));
+      lds_barrier();
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // ---- partial result of (this workgroup, sequence b)
-    const size_t ps = (size_t)wg + b;
+    attn_step(A, cc.tok, cc.tok_hi, copy, blk_pf, pc.tok, pc.tok_hi, s >= 0, kv[s < 0 ? 0 : s % kNBuf],
+              kv[(s + kPf + kNBuf) % kNBuf], LO, qf, o, m_run, l_run, w, lane);
+    if (copy) advance(A, t_lo, t_hi, pc);
+    if (s < 0) continue;
+    if (cc.tok + kSub < cc.tok_hi) {
+      cc.tok += kSub;
+      continue;
+    }
+    // ---- last sub-tile of sequence cc.b: its partial result, normalised by its own sum
+    const size_t ps = (size_t)wg + cc.b;
     bf16_t* dst = A.part_o + (ps * kH + head) * kLkv + 4 * g;
     const float inv_l = 1.f / l_run;
 #pragma unroll
     for (int mt = 0; mt < kLkv / 16; ++mt)
       *(uint2*)(dst + 16 * mt) = make_uint2(pack_bf16x2(o[mt][0] * inv_l, o[mt][1] * inv_l),
                                             pack_bf16x2(o[mt][2] * inv_l, o[mt][3] * inv_l));
-    if (g == 0) {
-      A.part_ml[(ps * kH + head) * 2] = m_run;
-      A.part_ml[(ps * kH + head) * 2 + 1] = l_run;
-    }
+    if (g == 0) *(float2*)(A.part_ml + (ps * kH + head) * 2) = make_float2(m_run, l_run);
+    next_segment(A, t_lo, t_hi, cc);
+    if (cc.b >= A.B) break;
+    load_q(cc.b, qf);
+#pragma unroll
+    for (int mt = 0; mt < kLkv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
   }
 }
 

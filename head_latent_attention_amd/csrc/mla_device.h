@@ -15,10 +15,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 
 // Round to nearest even; NaN stays NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  // gfx950 v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two floats to a packed pair of bf16 (a in the low half), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // One OCP E4M3FN byte to fp32 with the gfx950 conversion instruction.
@@ -92,6 +97,28 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   float t = -INFINITY;
   for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
   return t;
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), which would wait for every
+// global->LDS copy still in flight (the prefetched tiles too).  Callers make LDS data safe
+// themselves: each wave waits for its own copies of the tile about to be read (vmcnt) and has
+// consumed its earlier LDS reads (lgkmcnt) before arriving.  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global->LDS copy, 16 bytes per lane, through a raw buffer resource based at the
+// wave-uniform address `base`: lane l's bytes [base + voff, base + voff + 16) land at
+// lds_base + 16*l.  The buffer form (unlike global_load_lds, which the compiler must treat
+// as possibly touching the LDS counter) leaves LDS reads issued while copies are in flight
+// waitable one by one.  Resource word 3 selects 32-bit data format, as untyped gfx9
+// buffer accesses need; every offset used stays below `bytes`.
+__device__ __forceinline__ void dma16_buf(const void* base, uint32_t bytes, uint32_t voff, void* lds_base) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
 }
 
 }  // namespace mla

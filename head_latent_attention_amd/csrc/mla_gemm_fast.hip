@@ -31,9 +31,6 @@ constexpr int BK = 64;   // k per LDS stage
 constexpr int BN = 128;  // output columns per workgroup
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
 
 // A tile: [BM][64] bf16, 8 chunks of 16 B per row; chunk c of row r at slot 8r + (c ^ ((r >> 1) & 7)).
 __device__ __forceinline__ int a_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
@@ -103,8 +100,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
         for (int q = 0; q < 4; ++q) {
           const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[q], false);
           const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[q], true);
-          out[2 * q] = pack2(lo[0] * s, lo[1] * s);
-          out[2 * q + 1] = pack2(hi[0] * s, hi[1] * s);
+          out[2 * q] = pack_bf16x2(lo[0] * s, lo[1] * s);
+          out[2 * q + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
         }
         rw[2 * it] = make_uint4(out[0], out[1], out[2], out[3]);
         rw[2 * it + 1] = make_uint4(out[4], out[5], out[6], out[7]);

@@ -30,9 +30,6 @@ constexpr float kRescaleThreshold = 8.0f;
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
 
 // K tile: key t, chunk c at slot KC*t + (c ^ k_swz(t)) (XOR inside aligned groups of 8).
 // V tile: key t, chunk c at slot VC*t + (c ^ v_swz(t)).  Both keep the 16-lane passes of
@@ -136,7 +133,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& P, int h, int kt
           p[4 + i] = m_new == -INFINITY ? 0.f : exp2f(x[2 * kk + 1][i] - m_new);
           sum += p[i] + p[4 + i];
         }
-        pb[nt][kk] = as_bf16x8(make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])));
+        pb[nt][kk] = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
       }
       sum += __shfl_xor(sum, 16, 64);
       sum += __shfl_xor(sum, 32, 64);
@@ -225,7 +222,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
 #pragma unroll
     for (int mt = 0; mt < DV / 16; ++mt) {
       const f32x4 v = o[mt][nt] * inv;
-      *(uint2*)(dst + 16 * mt) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+      *(uint2*)(dst + 16 * mt) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
   }
 }
