@@ -28,11 +28,23 @@ struct Partials {
   Partials offset(int64_t cols) const { return Partials{p + cols, splits, stride, ld}; }
 };
 
+// Sum in a fixed order: four independent running sums (parts z = 0, 1, 2, 3 mod 4) so that
+// the loads of a round are in flight together, then (s0 + s1) + (s2 + s3).
 __device__ __forceinline__ float part_ld(const Partials& P, int64_t m, int64_t n) {
   const float* q = P.p + m * P.ld + n;
-  float v = q[0];
-  for (int z = 1; z < P.splits; ++z) v += q[z * P.stride];
-  return v;
+  if (P.splits == 1) return q[0];
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int z = 0;
+  for (; z + 4 <= P.splits; z += 4) {
+    s0 += q[(int64_t)z * P.stride];
+    s1 += q[(int64_t)(z + 1) * P.stride];
+    s2 += q[(int64_t)(z + 2) * P.stride];
+    s3 += q[(int64_t)(z + 3) * P.stride];
+  }
+  if (z < P.splits) s0 += q[(int64_t)z * P.stride];
+  if (z + 1 < P.splits) s1 += q[(int64_t)(z + 1) * P.stride];
+  if (z + 2 < P.splits) s2 += q[(int64_t)(z + 2) * P.stride];
+  return (s0 + s1) + (s2 + s3);
 }
 
 // ---- general (any shape) kernels: SIMT fp32 arithmetic ------------------------------

@@ -81,8 +81,12 @@ hipError_t gemm_simt(const Dims& d, const void* A, int64_t lda, const WeightView
 // Row builder: RMSNorm of both latents, RoPE of k_pe, cache-row scatter, k_pe broadcast.
 // Grid (tokens, 2): y = 0 normalises the query latent, y = 1 builds the kv row.
 // ===================================================================================
+// Each thread keeps up to kRowCache of its values in registers between the two passes of
+// the RMSNorm (longer rows are read again).
+constexpr int kRowCache = 4;
+
 template <typename T>
-__global__ __launch_bounds__(256) void row_builder_kernel(
+__global__ __launch_bounds__(512) void row_builder_kernel(
     Partials Yq, Partials Ykv, int Lq, int Lkv, int dr, const float* __restrict__ gq, const float* __restrict__ gkv, float eps,
     const float* __restrict__ cosT, const float* __restrict__ sinT, T* __restrict__ cqn, T* __restrict__ cn,
     T* __restrict__ cache, int64_t n_slots, const int32_t* __restrict__ slot_mapping, T* __restrict__ kbuf, int H,
@@ -90,24 +94,43 @@ __global__ __launch_bounds__(256) void row_builder_kernel(
   __shared__ float red[16];
   const int t = blockIdx.x;
   const int R = Lkv + dr, dqk = dn + dr;
-  // the partial sums are re-read for the second pass (it hits L2)
+  const int nt = blockDim.x;
+  float v[kRowCache];
   if (blockIdx.y == 0) {
     // query latent: RMSNorm(cq) * gq
     if (Lq == 0 || cqn == nullptr) return;
     float ss = 0.f;
-    for (int i = threadIdx.x; i < Lq; i += blockDim.x) {
-      const float v = part_ld(Yq, t, i);
-      ss += v * v;
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c) {
+      const int i = threadIdx.x + c * nt;
+      v[c] = i < Lq ? part_ld(Yq, t, i) : 0.f;
+      ss += v[c] * v[c];
+    }
+    for (int i = threadIdx.x + kRowCache * nt; i < Lq; i += nt) {
+      const float x = part_ld(Yq, t, i);
+      ss += x * x;
     }
     const float r = rsqrtf(block_sum(ss, red) / (float)Lq + eps);
-    for (int i = threadIdx.x; i < Lq; i += blockDim.x) Act<T>::st(cqn, (size_t)t * Lq + i, part_ld(Yq, t, i) * r * gq[i]);
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c) {
+      const int i = threadIdx.x + c * nt;
+      if (i < Lq) Act<T>::st(cqn, (size_t)t * Lq + i, v[c] * r * gq[i]);
+    }
+    for (int i = threadIdx.x + kRowCache * nt; i < Lq; i += nt)
+      Act<T>::st(cqn, (size_t)t * Lq + i, part_ld(Yq, t, i) * r * gq[i]);
     return;
   }
   // kv latent: RMSNorm(c_kv) * gkv, RoPE(k_pe), cache row, k_pe broadcast
   float ss = 0.f;
-  for (int i = threadIdx.x; i < Lkv; i += blockDim.x) {
-    const float v = part_ld(Ykv, t, i);
-    ss += v * v;
+#pragma unroll
+  for (int c = 0; c < kRowCache; ++c) {
+    const int i = threadIdx.x + c * nt;
+    v[c] = i < Lkv ? part_ld(Ykv, t, i) : 0.f;
+    ss += v[c] * v[c];
+  }
+  for (int i = threadIdx.x + kRowCache * nt; i < Lkv; i += nt) {
+    const float x = part_ld(Ykv, t, i);
+    ss += x * x;
   }
   const float r = rsqrtf(block_sum(ss, red) / (float)Lkv + eps);
   int64_t slot = -1;
@@ -115,13 +138,19 @@ __global__ __launch_bounds__(256) void row_builder_kernel(
     slot = slot_mapping[t];
     if (slot >= n_slots) slot = -1;
   }
-  for (int i = threadIdx.x; i < Lkv; i += blockDim.x) {
-    const float v = Act<T>::round(part_ld(Ykv, t, i) * r * gkv[i]);
-    if (cn) Act<T>::st(cn, (size_t)t * Lkv + i, v);
-    if (slot >= 0) Act<T>::st(cache, (size_t)slot * R + i, v);
+  auto put = [&](int i, float x) {
+    const float y = Act<T>::round(x * r * gkv[i]);
+    if (cn) Act<T>::st(cn, (size_t)t * Lkv + i, y);
+    if (slot >= 0) Act<T>::st(cache, (size_t)slot * R + i, y);
+  };
+#pragma unroll
+  for (int c = 0; c < kRowCache; ++c) {
+    const int i = threadIdx.x + c * nt;
+    if (i < Lkv) put(i, v[c]);
   }
+  for (int i = threadIdx.x + kRowCache * nt; i < Lkv; i += nt) put(i, part_ld(Ykv, t, i));
   const int half = dr >> 1;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+  for (int i = threadIdx.x; i < half; i += nt) {
     const float c = cosT[(size_t)t * half + i], sn = sinT[(size_t)t * half + i];
     const float x0 = part_ld(Ykv, t, Lkv + 2 * i), x1 = part_ld(Ykv, t, Lkv + 2 * i + 1);
     const float y0 = Act<T>::round(x0 * c - x1 * sn), y1 = Act<T>::round(x0 * sn + x1 * c);
@@ -145,11 +174,11 @@ hipError_t row_builder(const Dims& d, const Partials& Yq, const Partials& Ykv, i
   if (T <= 0) return hipSuccess;
   dim3 grid(T, 2);
   if (d.act == 0)
-    row_builder_kernel<float><<<grid, 256, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT, (float*)cqn,
+    row_builder_kernel<float><<<grid, 512, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT, (float*)cqn,
                                                     (float*)cn, (float*)cache, n_slots, slot_mapping, (float*)kbuf,
                                                     d.H, d.dn);
   else
-    row_builder_kernel<bf16_t><<<grid, 256, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT, (bf16_t*)cqn,
+    row_builder_kernel<bf16_t><<<grid, 512, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT, (bf16_t*)cqn,
                                                      (bf16_t*)cn, (bf16_t*)cache, n_slots, slot_mapping,
                                                      (bf16_t*)kbuf, d.H, d.dn);
   return hipGetLastError();
