@@ -37,7 +37,16 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 constexpr int kH = 128, kLkv = 512, kDr = 64, kR = 576, kDn = 128, kDv = 128;
 constexpr int kChunks = kR / 8;   // 16-byte chunks per cache row
 constexpr int kTile = 64;         // tokens per work-list tile
+constexpr int kSub = 32;          // tokens per LDS buffer of the attention kernel
 constexpr int kAttnWGs = 256;     // workgroups of the attention kernel (one per CU on MI355X)
+constexpr int kXcds = 8;          // MI355X: accelerator dies, each with its own L2
+
+// Share of the work list taken by attention workgroup wg.  Workgroups are dealt to the
+// dies round-robin (wg % 8), so die x gets shares [32x, 32x + 32): workgroups that split
+// a sequence mostly sit on one die and fetch its query through the same L2.
+__device__ __forceinline__ int wg_share(int wg) {
+  return (wg % kXcds) * (kAttnWGs / kXcds) + wg / kXcds;
+}
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^(s - m) <= 256 between rescales
 
 
@@ -66,9 +75,22 @@ __device__ __forceinline__ uint4 load_w8(const WeightView& W, int64_t k, int64_t
 }
 
 // ------------------------------------------------------------------------------ plan
-// P[b] = number of 64-token tiles of sequences 0..b-1; P[B] = total.
+// P[b] = number of 64-token tiles of sequences 0..b-1; P[B] = total.  Then, for each share r
+// of the attention work list (tiles [r*N/G, (r+1)*N/G)), info[2r] = its first sequence with
+// tokens in the share (B when empty) and info[2r+1] = its number of 32-token sub-tiles, so
+// that no attention workgroup walks P with chains of dependent scalar loads.
+__device__ __forceinline__ int share_tokens(const int32_t* __restrict__ P, const int32_t* __restrict__ ctx, int b,
+                                            int t_lo, int t_hi, int* lo, int* hi) {
+  const int p0 = P[b], p1 = P[b + 1];
+  const int a = max(t_lo, p0), e = min(t_hi, p1);
+  if (a >= e) return 0;
+  *lo = (a - p0) * kTile;
+  *hi = min(ctx[b], (e - p0) * kTile);
+  return 1;
+}
+
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ ctx, int B, int32_t* __restrict__ P,
-                                                    bf16_t* __restrict__ zero_row) {
+                                                    int32_t* __restrict__ info, bf16_t* __restrict__ zero_row) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   if (tid < kR) zero_row[tid] = 0;
@@ -94,6 +116,29 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     base += c > 0 ? (c + kTile - 1) / kTile : 0;
   }
   if (tid == 1023) P[B] = part[1023];
+  __threadfence();
+  __syncthreads();
+  if (tid >= kAttnWGs) return;
+  const int N = part[1023];
+  const int t_lo = (int)((int64_t)tid * N / kAttnWGs), t_hi = (int)((int64_t)(tid + 1) * N / kAttnWGs);
+  int first = B, total = 0;
+  if (t_lo < t_hi) {
+    // the largest b with P[b] <= t_lo
+    int l = 0, h = B;
+    while (l < h) {
+      const int mid = (l + h + 1) >> 1;
+      if (P[mid] <= t_lo) l = mid;
+      else h = mid - 1;
+    }
+    for (int b = l; b < B && P[b] < t_hi; ++b) {
+      int a, e;
+      if (!share_tokens(P, ctx, b, t_lo, t_hi, &a, &e)) continue;
+      if (first == B) first = b;
+      total += (e - a + kSub - 1) / kSub;
+    }
+  }
+  info[2 * tid] = first;
+  info[2 * tid + 1] = total;
 }
 
 // ------------------------------------------------------------------------------ fold
@@ -166,7 +211,6 @@ __global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q,
 // 16-token score reads and the 4-token transposing value reads; swz_pe the score
 // reads of the rope chunks.  Four such buffers rotate: three tiles of
 // copies are in flight while the fourth is being consumed.
-constexpr int kSub = 32;                                  // tokens per LDS buffer
 constexpr int kCSlots = kSub * 64, kPeSlots = kSub * 8, kBufSlots = kCSlots + kPeSlots;
 constexpr int kNBuf = 4;
 constexpr int kAttnWaves = 8;
@@ -185,6 +229,7 @@ struct AttnArgs {
   int max_blocks;
   const int32_t* ctx;
   const int32_t* P;
+  const int32_t* info;  // per share: first sequence, number of sub-tiles
   int B;
   float scale_log2;
   bf16_t* part_o;  // [(G + B)][H][Lkv]  latent output of a share, normalised by its own sum
@@ -430,21 +475,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void decode_attn_kernel(AttnArg
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = sload(A.P + A.B);
-  const int wg = blockIdx.x;
+  const int wg = wg_share(blockIdx.x);
   const int t_lo = (int)((int64_t)wg * N / kAttnWGs), t_hi = (int)((int64_t)(wg + 1) * N / kAttnWGs);
-  if (t_lo >= t_hi) return;
-  // sequence holding tile t_lo: the largest b with P[b] <= t_lo
-  int lo = 0, hi = A.B;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (sload(A.P + mid) <= t_lo) lo = mid;
-    else hi = mid - 1;
-  }
-  Cursor cc{lo - 1, 0, 0};
-  next_segment(A, t_lo, t_hi, cc);
-  // sub-tiles of the whole share
-  int total = 0;
-  for (Cursor c = cc; c.b < A.B; next_segment(A, t_lo, t_hi, c)) total += (c.tok_hi - c.tok + kSub - 1) / kSub;
+  const int total = sload(A.info + 2 * wg + 1);
+  if (total == 0) return;
+  Cursor cc{sload(A.info + 2 * wg), 0, 0};
+  share_of(A, cc.b, t_lo, t_hi, &cc.tok, &cc.tok_hi);
   Cursor pc = cc;
   const int head = 16 * w + j;
   const LaneOffsets LO = lane_offsets(lane);
@@ -600,6 +636,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
 struct DecodeLayout {
   bf16_t* Qabs;
   int32_t* P;
+  int32_t* info;
   bf16_t* zero_row;
   bf16_t* part_o;
   float* part_ml;
@@ -616,6 +653,8 @@ DecodeLayout layout(int B, void* base) {
   off += al((size_t)B * kH * kR * sizeof(bf16_t));
   L.P = (int32_t*)(p + off);
   off += al((size_t)(B + 1) * sizeof(int32_t));
+  L.info = (int32_t*)(p + off);
+  off += al((size_t)2 * kAttnWGs * sizeof(int32_t));
   L.zero_row = (bf16_t*)(p + off);
   off += al((size_t)kR * sizeof(bf16_t));
   L.part_o = (bf16_t*)(p + off);
@@ -639,7 +678,7 @@ hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cac
                             const int32_t* block_table, int max_blocks, const int32_t* ctx,
                             const WeightView& wkv_b, void* o, const FastDecodeWs& ws, hipStream_t s) {
   const DecodeLayout L = layout(B, ws.base);
-  plan_kernel<<<1, 1024, 0, s>>>(ctx, B, L.P, L.zero_row);
+  plan_kernel<<<1, 1024, 0, s>>>(ctx, B, L.P, L.info, L.zero_row);
   dim3 fgrid(kH, kLkv / 128, (B + 63) / 64);
   if (d.wk == W_BF16) fold_kernel<W_BF16><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs);
   else fold_kernel<W_FP8><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs);
@@ -653,6 +692,7 @@ hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cac
   A.max_blocks = max_blocks;
   A.ctx = ctx;
   A.P = L.P;
+  A.info = L.info;
   A.B = B;
   A.scale_log2 = d.scale * 1.4426950408889634f;
   A.part_o = L.part_o;
