@@ -100,11 +100,15 @@ size_t qkv_ws(const Dims& d, int n, bool prefill, void* base, QkvWs* out) {
   Carver c(base);
   QkvWs w;
   const int HQ = d.H * d.dqk();
+  const int NKV = d.H * (d.dn + d.dv);
   w.P1 = (float*)c.take<char>(proj_out_bytes(d, n, stage1_q_cols(d) + d.R(), d.D));
-  w.P2 = d.Lq > 0 ? (float*)c.take<char>(proj_out_bytes(d, n, HQ, d.Lq)) : nullptr;
+  // results handed straight to their consumer need no buffer
+  const bool q_fused = fast_gemm_fusable(d, n, HQ, d.Lq, HQ, GemmEpilogue::QUERY);
+  const bool kv_fused = fast_gemm_fusable(d, n, NKV, d.Lkv, NKV, GemmEpilogue::KV);
+  w.P2 = d.Lq > 0 ? (float*)c.take<char>(q_fused ? 0 : proj_out_bytes(d, n, HQ, d.Lq)) : nullptr;
   w.cqn = d.Lq > 0 ? c.take<char>((size_t)n * d.Lq * act_bytes(d)) : nullptr;
   w.cn = prefill ? c.take<char>((size_t)n * d.Lkv * act_bytes(d)) : nullptr;
-  w.PKV = prefill ? (float*)c.take<char>(proj_out_bytes(d, n, d.H * (d.dn + d.dv), d.Lkv)) : nullptr;
+  w.PKV = prefill ? (float*)c.take<char>(kv_fused ? 0 : proj_out_bytes(d, n, NKV, d.Lkv)) : nullptr;
   if (out) *out = w;
   return c.used;
 }
@@ -147,7 +151,8 @@ size_t decode_attn_ws(const Dims& d, int B, int max_context, void* base, DecodeA
 
 size_t out_proj_ws(const Dims& d, int M, void* base, float** Y) {
   Carver c(base);
-  float* y = (float*)c.take<char>(proj_out_bytes(d, M, d.D, d.H * d.dv));
+  const bool fused = fast_gemm_fusable(d, M, d.D, d.H * d.dv, d.D, GemmEpilogue::STORE);
+  float* y = (float*)c.take<char>(fused ? 0 : proj_out_bytes(d, M, d.D, d.H * d.dv));
   if (Y) *Y = y;
   return c.used;
 }
@@ -166,11 +171,15 @@ mla_status hip_status(hipError_t e) {
     if (e_ != hipSuccess) return hip_status(e_);          \
   } while (0)
 
-// C = A @ [W0 | W1] (W0: output columns [0, n_split)), left as partial sums in `out`.
+// C = A @ [W0 | W1] (W0: output columns [0, n_split)), left as partial sums in `out`, or
+// handed straight to the consumer `epi` describes (then *fused is set and the caller skips
+// its own consumer kernel).
 mla_status project(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split, const WeightView& W1,
-                   int M, int N, int K, float* out, Partials* res, hipStream_t s) {
+                   int M, int N, int K, float* out, Partials* res, hipStream_t s, const GemmEpilogue* epi = nullptr,
+                   bool* fused = nullptr) {
+  if (fused) *fused = false;
   if (fast_proj_supported(d)) {
-    HIP_TRY(fast_gemm(d, A, lda, W0, n_split, W1, M, N, K, out, res, s));
+    HIP_TRY(fast_gemm(d, A, lda, W0, n_split, W1, M, N, K, out, res, epi, fused, s));
     return MLA_OK;
   }
   const int n0 = std::min(n_split, N);
@@ -197,8 +206,15 @@ mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, 
   Partials PQ = P1;
   if (d.Lq > 0) {
     const WeightView wqb = view(d, w->wq_b, HQ);
-    st = project(d, ws.cqn, d.Lq, wqb, HQ, wqb, n, HQ, d.Lq, ws.P2, &PQ, s);
+    GemmEpilogue epi;
+    epi.kind = GemmEpilogue::QUERY;
+    epi.y = q;
+    epi.cosT = cosT;
+    epi.sinT = sinT;
+    bool fused = false;
+    st = project(d, ws.cqn, d.Lq, wqb, HQ, wqb, n, HQ, d.Lq, ws.P2, &PQ, s, &epi, &fused);
     if (st != MLA_OK) return st;
+    if (fused) return MLA_OK;
   }
   HIP_TRY(q_epilogue(d, PQ, n, cosT, sinT, q, s));
   return MLA_OK;
@@ -260,9 +276,14 @@ mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const vo
   const int NKV = d.H * (d.dn + d.dv);
   const WeightView wkvb = view(d, w->wkv_b, NKV);
   Partials PKV;
-  st = project(d, L.cn, d.Lkv, wkvb, NKV, wkvb, T, NKV, d.Lkv, L.PKV, &PKV, s);
+  GemmEpilogue epi;
+  epi.kind = GemmEpilogue::KV;
+  epi.y = k;
+  epi.y2 = v;
+  bool fused = false;
+  st = project(d, L.cn, d.Lkv, wkvb, NKV, wkvb, T, NKV, d.Lkv, L.PKV, &PKV, s, &epi, &fused);
   if (st != MLA_OK) return st;
-  HIP_TRY(kv_split(d, PKV, T, k, v, s));
+  if (!fused) HIP_TRY(kv_split(d, PKV, T, k, v, s));
   return MLA_OK;
 }
 
@@ -342,9 +363,13 @@ mla_status mla_out_proj(const mla_config* cfg, const mla_weights* w, const void*
   const int K = d.H * d.dv;
   const WeightView wo = view(d, w->wo, d.D);
   Partials P;
-  st = project(d, o, K, wo, d.D, wo, M, d.D, K, Y, &P, s);
+  GemmEpilogue epi;
+  epi.kind = GemmEpilogue::STORE;
+  epi.y = y;
+  bool fused = false;
+  st = project(d, o, K, wo, d.D, wo, M, d.D, K, Y, &P, s, &epi, &fused);
   if (st != MLA_OK) return st;
-  HIP_TRY(cast_rows(d, P, M, d.D, y, s));
+  if (!fused) HIP_TRY(cast_rows(d, P, M, d.D, y, s));
   return MLA_OK;
 }
 

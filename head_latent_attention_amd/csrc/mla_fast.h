@@ -11,13 +11,30 @@ struct FastDecodeWs {
   size_t bytes = 0;
 };
 
+// Consumers a projection can hand its result to directly when K is not split:
+//   STORE  y[m, n] = C[m, n] (act)
+//   QUERY  q[m, h, :] = [C[m, h*dqk : +dn] | RoPE_m(C[m, h*dqk+dn : (h+1)*dqk])] (act)
+//   KV     k[m, h, j] = C[m, h*(dn+dv) + j] (j < dn), v[m, h, j - dn] = the rest (act)
+struct GemmEpilogue {
+  enum Kind { PARTIALS = 0, STORE = 1, QUERY = 2, KV = 3 };
+  int kind = PARTIALS;
+  void* y = nullptr;   // STORE: y; QUERY: q; KV: k
+  void* y2 = nullptr;  // KV: v
+  const float* cosT = nullptr;
+  const float* sinT = nullptr;
+};
+
 // Projection GEMM / GEMV: C[M, N] = A[M, K] (act) @ [W0 | W1], W0 giving output columns
 // [0, n_split) and W1 columns [n_split, N) (n_split >= N: W0 only).  C is left in `out`
-// (fast_gemm_out_bytes(M, N, K) bytes) as split-K partial sums, described by *res.
+// (fast_gemm_out_bytes(M, N, K) bytes) as split-K partial sums, described by *res; or, when
+// `epi` asks for a consumer and K is not split, written straight to it (*fused = true).
 bool fast_proj_supported(const Dims& d);
 size_t fast_gemm_out_bytes(int M, int N, int K);
+// whether fast_gemm hands the result of this shape straight to a consumer of `kind`
+bool fast_gemm_fusable(const Dims& d, int M, int N, int K, int n_split, int kind);
 hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split,
-                     const WeightView& W1, int M, int N, int K, float* out, Partials* res, hipStream_t s);
+                     const WeightView& W1, int M, int N, int K, float* out, Partials* res,
+                     const GemmEpilogue* epi, bool* fused, hipStream_t s);
 
 // Absorbed decode: fold, split-context attention over the paged cache, combine with W_UV.
 bool fast_decode_supported(const Dims& d);

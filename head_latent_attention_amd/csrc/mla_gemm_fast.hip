@@ -49,10 +49,20 @@ struct Gemm {
   static_assert(WM * WN == 4, "4 waves");
 };
 
+struct EpiArgs {
+  int kind;
+  bf16_t* y;
+  bf16_t* y2;
+  const float* cosT;
+  const float* sinT;
+  int H, dn, dr, dv;
+};
+
 template <int BM, int WM, int WN, int WK>
 __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda, WeightView W0,
                                                    WeightView W1, int n_split, float* __restrict__ C, int64_t ldc,
-                                                   int M, int N, int K, int k_split, int64_t split_stride) {
+                                                   int M, int N, int K, int k_split, int64_t split_stride,
+                                                   EpiArgs E) {
   using G = Gemm<BM, WM, WN, WK>;
   __shared__ __attribute__((aligned(16))) uint4 As[2][G::A_SLOTS];
   __shared__ __attribute__((aligned(16))) uint4 Ws[2][G::W_SLOTS];
@@ -174,18 +184,53 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
     __syncthreads();
     cur ^= 1;
   }
+  if (E.kind == GemmEpilogue::PARTIALS) {
 #pragma unroll
-  for (int mt = 0; mt < G::MT; ++mt)
+    for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * (BM / WM) + 16 * mt + 4 * g + i;
-      if (m >= M) continue;
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * (BM / WM) + 16 * mt + 4 * g + i;
+        if (m >= M) continue;
 #pragma unroll
-      for (int nt = 0; nt < G::NT; ++nt) {
-        const int n = n0 + wcol0 + 16 * nt + j;
-        if (n < N) C[(int64_t)m * ldc + n] = acc[mt][nt][i];
+        for (int nt = 0; nt < G::NT; ++nt) {
+          const int n = n0 + wcol0 + 16 * nt + j;
+          if (n < N) C[(int64_t)m * ldc + n] = acc[mt][nt][i];
+        }
       }
-    }
+    return;
+  }
+  // consumers: column n of the lane (j) and its RoPE partner n ^ 1 (lane j ^ 1, same rows)
+  const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const int n = n0 + wcol0 + 16 * nt + j;
+    int h = 0, u = 0;
+    if (E.kind == GemmEpilogue::QUERY) { h = n / dqk; u = n - h * dqk; }
+    if (E.kind == GemmEpilogue::KV) { h = n / dkv; u = n - h * dkv; }
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * (BM / WM) + 16 * mt + 4 * g + i;
+        const float x = acc[mt][nt][i];
+        const float other = __shfl_xor(x, 1);  // every lane takes part
+        if (m >= M || n >= N) continue;
+        if (E.kind == GemmEpilogue::STORE) {
+          E.y[(int64_t)m * N + n] = f32_to_bf16(x);
+        } else if (E.kind == GemmEpilogue::QUERY) {
+          float yv = x;
+          if (u >= E.dn) {
+            const int p = (u - E.dn) >> 1;
+            const float c = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
+            yv = (u - E.dn) & 1 ? other * sn + x * c : x * c - other * sn;
+          }
+          E.y[(int64_t)m * N + n] = f32_to_bf16(yv);
+        } else {
+          if (u < E.dn) E.y[((int64_t)m * E.H + h) * dqk + u] = f32_to_bf16(x);
+          else E.y2[((int64_t)m * E.H + h) * E.dv + (u - E.dn)] = f32_to_bf16(x);
+        }
+      }
+  }
 }
 
 struct Plan {
@@ -207,22 +252,22 @@ Plan plan(int M, int N, int K) {
 template <int BM, int WM, int WN>
 hipError_t launch(const Dims& d, const void* A, int64_t lda, const WeightView& W0, const WeightView& W1, int n_split,
                   float* C, int64_t ldc, int M, int N, int K, int k_split, int splits, int64_t split_stride,
-                  hipStream_t s) {
+                  const EpiArgs& E, hipStream_t s) {
   dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, splits);
   if (d.wk == W_FP8)
     gemm_kernel<BM, WM, WN, W_FP8><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W0, W1, n_split, C, ldc, M, N, K,
-                                                        k_split, split_stride);
+                                                        k_split, split_stride, E);
   else
     gemm_kernel<BM, WM, WN, W_BF16><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W0, W1, n_split, C, ldc, M, N, K,
-                                                         k_split, split_stride);
+                                                         k_split, split_stride, E);
   return hipGetLastError();
 }
 
 hipError_t launch_plan(const Plan& p, const Dims& d, const void* A, int64_t lda, const WeightView& W0,
                        const WeightView& W1, int n_split, float* C, int64_t ldc, int M, int N, int K, int64_t stride,
-                       hipStream_t s) {
-  return p.bm == 64 ? launch<64, 1, 4>(d, A, lda, W0, W1, n_split, C, ldc, M, N, K, p.k_split, p.splits, stride, s)
-                    : launch<128, 2, 2>(d, A, lda, W0, W1, n_split, C, ldc, M, N, K, p.k_split, p.splits, stride, s);
+                       const EpiArgs& E, hipStream_t s) {
+  return p.bm == 64 ? launch<64, 1, 4>(d, A, lda, W0, W1, n_split, C, ldc, M, N, K, p.k_split, p.splits, stride, E, s)
+                    : launch<128, 2, 2>(d, A, lda, W0, W1, n_split, C, ldc, M, N, K, p.k_split, p.splits, stride, E, s);
 }
 
 }  // namespace
@@ -240,18 +285,37 @@ size_t fast_gemm_out_bytes(int M, int N, int K) {
   return (size_t)plan(M, N, K).splits * M * N * sizeof(float);
 }
 
+bool fast_gemm_fusable(const Dims& d, int M, int N, int K, int n_split, int kind) {
+  if (!fast_proj_supported(d) || kind == GemmEpilogue::PARTIALS || M <= 0 || N <= 0 || K <= 0) return false;
+  const bool aligned = n_split >= N || n_split % BN == 0;
+  // the query consumer pairs columns 2i, 2i+1 of each head's rope part within a lane pair
+  const bool pairs_ok = d.dn % 2 == 0 && (d.dn + d.dr) % 2 == 0;
+  return plan(M, N, K).splits == 1 && aligned && (kind != GemmEpilogue::QUERY || pairs_ok);
+}
+
 hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split, const WeightView& W1,
-                     int M, int N, int K, float* out, Partials* res, hipStream_t s) {
+                     int M, int N, int K, float* out, Partials* res, const GemmEpilogue* epi, bool* fused,
+                     hipStream_t s) {
   const Plan p = plan(M, N, K);
   const int64_t stride = (int64_t)M * N;
   *res = Partials{out, p.splits, stride, N};
+  if (fused) *fused = false;
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
-  if (n_split >= N || n_split % BN == 0)
-    return launch_plan(p, d, A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, stride, s);
+  EpiArgs E{GemmEpilogue::PARTIALS, nullptr, nullptr, nullptr, nullptr, d.H, d.dn, d.dr, d.dv};
+  const bool aligned = n_split >= N || n_split % BN == 0;
+  if (epi && fast_gemm_fusable(d, M, N, K, n_split, epi->kind)) {
+    E.kind = epi->kind;
+    E.y = (bf16_t*)epi->y;
+    E.y2 = (bf16_t*)epi->y2;
+    E.cosT = epi->cosT;
+    E.sinT = epi->sinT;
+    if (fused) *fused = true;
+  }
+  if (aligned) return launch_plan(p, d, A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, stride, E, s);
   // segments not aligned to the column tile: one launch each, same split plan and partial layout
-  hipError_t e = launch_plan(p, d, A, lda, W0, W0, n_split, out, N, M, n_split, K, stride, s);
+  hipError_t e = launch_plan(p, d, A, lda, W0, W0, n_split, out, N, M, n_split, K, stride, E, s);
   if (e != hipSuccess) return e;
-  return launch_plan(p, d, A, lda, W1, W1, N - n_split, out + n_split, N, M, N - n_split, K, stride, s);
+  return launch_plan(p, d, A, lda, W1, W1, N - n_split, out + n_split, N, M, N - n_split, K, stride, E, s);
 }
 
 }  // namespace mla
