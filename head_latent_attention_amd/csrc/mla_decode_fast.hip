@@ -2,8 +2,9 @@
 // DeepSeek-V2/V3 head geometry: 128 heads, kv_lora 512, qk_rope 64, qk_nope 128,
 // v_dim 128, bf16 activations and cache, bf16 or block-scaled E4M3FN weights.
 //
-// Three kernels plus a one-block planner:
-//   plan     prefix sums of 64-token tiles over the batch (the work list).
+// Three kernels; the first also plans:
+//   plan     prefix sums of 64-token tiles over the batch (the work list), by one extra
+//            workgroup of the fold launch.
 //   fold     q_lat[b,h] = q_nope[b,h] @ W_UK[h], W_UK read straight out of wkv_b
 //            (AWS NKI "MLA Decode QKV Kernel API Reference": the query is absorbed
 //            into the cache's latent space; atlas "Struct MlaWeights": w_uk_t).
@@ -79,7 +80,7 @@ __device__ __forceinline__ uint4 load_w8(const WeightView& W, int64_t k, int64_t
 // of the attention work list (tiles [r*N/G, (r+1)*N/G)), info[2r] = its first sequence with
 // tokens in the share (B when empty) and info[2r+1] = its number of 32-token sub-tiles, so
 // that no attention workgroup walks P with chains of dependent scalar loads.
-__device__ __forceinline__ int share_tokens(const int32_t* __restrict__ P, const int32_t* __restrict__ ctx, int b,
+__device__ __forceinline__ int share_tokens(const int32_t* P, const int32_t* ctx, int b,
                                             int t_lo, int t_hi, int* lo, int* hi) {
   const int p0 = P[b], p1 = P[b + 1];
   const int a = max(t_lo, p0), e = min(t_hi, p1);
@@ -89,37 +90,49 @@ __device__ __forceinline__ int share_tokens(const int32_t* __restrict__ P, const
   return 1;
 }
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ ctx, int B, int32_t* __restrict__ P,
-                                                    int32_t* __restrict__ info, bf16_t* __restrict__ zero_row) {
-  __shared__ int32_t part[1024];
+constexpr int kPlanLds = 2048;  // batches up to this size are planned out of LDS
+
+constexpr int kPlanThreads = 256;
+static_assert(kAttnWGs == kPlanThreads, "one planning thread per attention share");
+
+// Run by one 256-thread workgroup (the last workgroup of the fold launch).
+__device__ void plan_block(const int32_t* __restrict__ ctx, int B, int32_t* __restrict__ P, int32_t* __restrict__ info,
+                           bf16_t* __restrict__ zero_row, int32_t* scan, int32_t* Ps, int32_t* Cs) {
   const int tid = threadIdx.x;
-  if (tid < kR) zero_row[tid] = 0;
-  const int per = (B + 1023) / 1024;
-  const int lo = min(B, tid * per), hi = min(B, lo + per);
-  int s = 0;
-  for (int b = lo; b < hi; ++b) {
-    const int c = ctx[b];
-    s += c > 0 ? (c + kTile - 1) / kTile : 0;
+  const bool in_lds = B <= kPlanLds;
+  for (int i = tid; i < kR; i += kPlanThreads) zero_row[i] = 0;
+  if (tid == 0) {
+    P[0] = 0;
+    Ps[0] = 0;
   }
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
+  // P[b + 1] = P[b] + tiles of sequence b, 256 sequences per round (inclusive scan in LDS)
+  int carry = 0;
+  for (int c0 = 0; c0 < B; c0 += kPlanThreads) {
+    const int b = c0 + tid;
+    const int c = b < B ? ctx[b] : 0;
+    scan[tid] = c > 0 ? (c + kTile - 1) / kTile : 0;
     __syncthreads();
-    part[tid] += v;
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    if (b < B) {
+      P[b + 1] = carry + scan[tid];
+      if (in_lds) {
+        Ps[b + 1] = carry + scan[tid];
+        Cs[b] = c;
+      }
+    }
+    carry += scan[kPlanThreads - 1];
     __syncthreads();
   }
-  int base = tid ? part[tid - 1] : 0;
-  for (int b = lo; b < hi; ++b) {
-    P[b] = base;
-    const int c = ctx[b];
-    base += c > 0 ? (c + kTile - 1) / kTile : 0;
-  }
-  if (tid == 1023) P[B] = part[1023];
   __threadfence();
   __syncthreads();
-  if (tid >= kAttnWGs) return;
-  const int N = part[1023];
+  const int32_t* PP = in_lds ? Ps : P;
+  const int32_t* CC = in_lds ? Cs : ctx;
+  const int N = carry;
   const int t_lo = (int)((int64_t)tid * N / kAttnWGs), t_hi = (int)((int64_t)(tid + 1) * N / kAttnWGs);
   int first = B, total = 0;
   if (t_lo < t_hi) {
@@ -127,12 +140,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     int l = 0, h = B;
     while (l < h) {
       const int mid = (l + h + 1) >> 1;
-      if (P[mid] <= t_lo) l = mid;
+      if (PP[mid] <= t_lo) l = mid;
       else h = mid - 1;
     }
-    for (int b = l; b < B && P[b] < t_hi; ++b) {
+    for (int b = l; b < B && PP[b] < t_hi; ++b) {
       int a, e;
-      if (!share_tokens(P, ctx, b, t_lo, t_hi, &a, &e)) continue;
+      if (!share_tokens(PP, CC, b, t_lo, t_hi, &a, &e)) continue;
       if (first == B) first = b;
       total += (e - a + kSub - 1) / kSub;
     }
@@ -143,12 +156,21 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 
 // ------------------------------------------------------------------------------ fold
 // Qabs[b][h] = [q_nope[b][h] @ W_UK[h] | q_pe[b][h]] in bf16, W_UK[h][p][c] = wkv_b[c][h*256 + p].
-// Grid (H, 4, ceil(B/64)): workgroup (h, cg) covers latent columns [128cg, 128cg + 128) of 64
+// Grid (H + 1, 4, ceil(B/64)): workgroup (h, cg) covers latent columns [128cg, 128cg + 128) of 64
 // rows, wave w the 32 columns [128cg + 32w, 128cg + 32w + 32).  Every operand load of a wave is
 // issued before its first matrix op.
 template <int WK>
 __global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q, int B, WeightView W,
-                                                   bf16_t* __restrict__ Qabs) {
+                                                   bf16_t* __restrict__ Qabs, const int32_t* __restrict__ ctx,
+                                                   int32_t* __restrict__ P, int32_t* __restrict__ info,
+                                                   bf16_t* __restrict__ zero_row) {
+  if (blockIdx.x == kH) {  // one extra workgroup plans the attention's work list
+    __shared__ int32_t scan[kPlanThreads];
+    __shared__ int32_t Ps[kPlanLds + 1];
+    __shared__ int32_t Cs[kPlanLds];
+    if (blockIdx.y == 0 && blockIdx.z == 0) plan_block(ctx, B, P, info, zero_row, scan, Ps, Cs);
+    return;
+  }
   const int h = blockIdx.x, cg = blockIdx.y, b0 = blockIdx.z * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
   constexpr int qs = kH * (kDn + kDr);
@@ -546,7 +568,9 @@ __device__ __forceinline__ bool wg_nonempty(int w, int N) {
 // ------------------------------------------------------------------------------ combine + W_UV
 // Grid (H, ceil(B/16)).  Merges the partials of 16 sequences for one head, then
 // o[b][h] = o_lat[b][h] @ W_UV[h] on the matrix cores (W_UV[h][c][j] = wkv_b[c][h*256 + 128 + j]).
-// A share's weight in the merge is 2^(m - M) * l (its normalised output times its own sum).
+// A share's weight in the merge is 2^(m - M) * l (its normalised output times its own sum),
+// accumulated online (running max M) in share order.  The first 128 rows of W_UV[h] are
+// loaded before the merge so that their latency overlaps it.
 template <int WK>
 __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, const int32_t* __restrict__ P,
@@ -556,6 +580,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   const int h = blockIdx.x, b0 = blockIdx.y * 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
   const int N = P[B];
+  const int64_t col0 = (int64_t)h * (kDn + kDv) + kDn;
+  uint4 wr[8];
+  auto load_w_chunk = [&](int cc) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
+      wr[it] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
+    }
+  };
+  load_w_chunk(0);
   // ---- merge: wave w handles local rows 4w..4w+3, each lane 8 latent columns
   for (int r = 0; r < 4; ++r) {
     const int lb = 4 * w + r, b = b0 + lb;
@@ -563,32 +597,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
     if (b < B && P[b + 1] > P[b]) {
       const int wf = (int)(((int64_t)(P[b] + 1) * kAttnWGs - 1) / N);
       const int wl = (int)(((int64_t)P[b + 1] * kAttnWGs - 1) / N);
-      float M = -INFINITY;
-      for (int wq = wf; wq <= wl; ++wq)
-        if (wg_nonempty(wq, N)) M = fmaxf(M, part_ml[(((size_t)wq + b) * kH + h) * 2]);
-      float L = 0.f;
+      float M = -INFINITY, L = 0.f;
       // four shares per round, all loads of a round issued together
       for (int wq0 = wf; wq0 <= wl; wq0 += 4) {
-        float f[4];
+        float2 ml[4];
         uint4 v[4];
+        bool ok[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int wq = wq0 + u;
-          const bool ok = wq <= wl && wg_nonempty(wq, N);
-          const size_t ps = ((size_t)(ok ? wq : wf) + b) * kH + h;
-          const float2 ml = *(const float2*)(part_ml + ps * 2);
-          const uint4 x = *(const uint4*)(part_o + ps * kLkv + 8 * lane);
-          v[u] = ok ? x : make_uint4(0, 0, 0, 0);  // an empty share's slot was never written
-          f[u] = ok ? exp2f(ml.x - M) * ml.y : 0.f;
+          ok[u] = wq <= wl && wg_nonempty(wq, N);
+          const size_t ps = ((size_t)(ok[u] ? wq : wf) + b) * kH + h;
+          ml[u] = *(const float2*)(part_ml + ps * 2);
+          v[u] = *(const uint4*)(part_o + ps * kLkv + 8 * lane);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          L += f[u];
+          if (!ok[u]) continue;  // an empty share's slot was never written
+          const float Mn = fmaxf(M, ml[u].x);
+          const float sa = M == -INFINITY ? 0.f : exp2f(M - Mn);
+          const float f = exp2f(ml[u].x - Mn) * ml[u].y;
+          L = L * sa + f;
+          M = Mn;
           const uint32_t wds[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += f[u] * __uint_as_float(wds[e] << 16);
-            acc[2 * e + 1] += f[u] * __uint_as_float(wds[e] & 0xFFFF0000u);
+            acc[2 * e] = acc[2 * e] * sa + f * __uint_as_float(wds[e] << 16);
+            acc[2 * e + 1] = acc[2 * e + 1] * sa + f * __uint_as_float(wds[e] & 0xFFFF0000u);
           }
         }
       }
@@ -601,15 +636,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   }
   // ---- o[16 x 128] = As[16 x 512] @ W_UV[512 x 128]; wave w owns columns [32w, 32w + 32)
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  const int64_t col0 = (int64_t)h * (kDn + kDv) + kDn;
   for (int cc = 0; cc < kLkv / 128; ++cc) {
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
-      *(uint4*)&Ws[r][8 * ch] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
+      *(uint4*)&Ws[r][8 * ch] = wr[it];
     }
     __syncthreads();
+    if (cc + 1 < kLkv / 128) load_w_chunk(cc + 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 a = as_bf16x8(*(const uint4*)&As[j][128 * cc + 32 * ks + 8 * g]);
@@ -678,10 +713,11 @@ hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cac
                             const int32_t* block_table, int max_blocks, const int32_t* ctx,
                             const WeightView& wkv_b, void* o, const FastDecodeWs& ws, hipStream_t s) {
   const DecodeLayout L = layout(B, ws.base);
-  plan_kernel<<<1, 1024, 0, s>>>(ctx, B, L.P, L.info, L.zero_row);
-  dim3 fgrid(kH, kLkv / 128, (B + 63) / 64);
-  if (d.wk == W_BF16) fold_kernel<W_BF16><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs);
-  else fold_kernel<W_FP8><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs);
+  dim3 fgrid(kH + 1, kLkv / 128, (B + 63) / 64);
+  if (d.wk == W_BF16)
+    fold_kernel<W_BF16><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs, ctx, L.P, L.info, L.zero_row);
+  else
+    fold_kernel<W_FP8><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs, ctx, L.P, L.info, L.zero_row);
   AttnArgs A;
   A.Qabs = L.Qabs;
   A.cache = (const bf16_t*)cache;

@@ -16,8 +16,8 @@ import json
 import os
 import sys
 
-# kernels launched once by each mla_decode_attn_absorbed call (MFMA path)
-DECODE_ATTN_KERNELS = ("plan_kernel", "fold_kernel", "decode_attn_kernel", "combine_kernel")
+# kernels launched once by each mla_decode_attn_absorbed call (MFMA path; the fold launch also plans)
+DECODE_ATTN_KERNELS = ("fold_kernel", "decode_attn_kernel", "combine_kernel")
 COPY_BYTES = 1 << 30
 
 
