@@ -233,12 +233,197 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Large-M variant (prefill): a 256 x 256 output tile per workgroup of 8 waves (2 x 4, each
+// 128 x 64), K steps of 32 copied global->LDS by buffer_load ... lds four stages deep.  Each
+// LDS operand read feeds 4 (A) or 8 (B) matrix ops instead of 2 and 2 in gemm_kernel.  K and
+// the column split must be multiples of 32 and 256.
+constexpr int kBigM = 256, kBigN = 256, kBigK = 32, kBigStages = 4;
+constexpr int kBigCopies = 4;  // per wave per stage: 2 activation + 2 weight copies of 1 KB
+
+// A stage: [256 rows][4 chunks of 16 B]; chunk c of row r at slot 4r + (c ^ a4_swz(r)), which
+// keeps every 16-lane pass of the operand reads on distinct banks.
+__device__ __forceinline__ int a4_swz(int r) { return ((r >> 2) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1); }
+
+struct BigArgs {
+  const bf16_t* A;
+  int64_t lda;
+  WeightView W0, W1;
+  int n_split;
+  float* C;
+  int64_t ldc;
+  int M, N, K;
+};
+
+// Copies of K step k0 into one stage.  Rows past M and columns past the segment are clamped
+// to valid memory; they only feed outputs that are not stored.
+__device__ __forceinline__ void big_issue(const BigArgs& G, const WeightView& W, int m0, int wn0, int wn_end, int k0,
+                                          uint4* __restrict__ as, uint4* __restrict__ ws, int w, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = 64 * (2 * w + i) + l, r = e >> 2, c = (e & 3) ^ a4_swz(r);
+    const int m = min(m0 + r, G.M - 1);
+    dma16_buf(G.A + k0, 0x7FFFFFF0u, (uint32_t)((m * G.lda + 8 * c) * 2), as + 64 * (2 * w + i));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = 2 * w + i, hb = blk >> 3, e = 64 * (blk & 7) + l;  // half hb: columns [128hb, 128hb + 128)
+    const int kr = e >> 4, c = (e & 15) ^ (((kr & 3) << 1) ^ (((kr >> 3) & 1) << 3));
+    const int n = min(wn0 + 128 * hb + 8 * c, wn_end - 8);
+    dma16_buf((const bf16_t*)W.w + (int64_t)k0 * W.ld, 0x7FFFFFF0u, (uint32_t)((kr * W.ld + n) * 2),
+              ws + 512 * hb + 64 * (blk & 7));
+  }
+}
+
+__device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, int m0, int wn0, int wn_end, bool copy,
+                                         int k_pf, bool compute, const uint4* __restrict__ as,
+                                         const uint4* __restrict__ ws, uint4* __restrict__ as_nx,
+                                         uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4], int w, int lane) {
+  if (copy) big_issue(G, W, m0, wn0, wn_end, k_pf, as_nx, ws_nx, w, lane);
+  if (!compute) return;
+  const int g = lane >> 4, j = lane & 15, wm = w >> 2, wn = w & 3;
+  bf16x8 af[8], bfr[4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const int r = 128 * wm + 16 * mt + j;
+    af[mt] = as_bf16x8(as[4 * r + (g ^ a4_swz(r))]);
+  }
+  const char* wsb = (const char*)(ws + 512 * (wn >> 1));
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = 64 * (wn & 1) + 16 * nt + 4 * (j & 3);
+    const int c = col >> 3, byte_in = (col & 7) * 2;
+    const int k = 8 * g + (j >> 2);
+    const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k, c) * 16 + byte_in));
+    const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k + 4, c) * 16 + byte_in));
+    bfr[nt] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) {
+  __shared__ __attribute__((aligned(16))) uint4 As[kBigStages][kBigM * 4];
+  __shared__ __attribute__((aligned(16))) uint4 Ws[kBigStages][2 * kBigK * 16];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 2, wn = w & 3;
+  // column tiles fastest; grid x = column tiles, y = row tiles
+  const int n0 = blockIdx.x * kBigN, m0 = blockIdx.y * kBigM;
+  const bool seg1 = n0 >= G.n_split;
+  const WeightView W = seg1 ? G.W1 : G.W0;
+  const int wn0 = seg1 ? n0 - G.n_split : n0, wn_end = seg1 ? G.N - G.n_split : G.n_split;
+  const int nsteps = G.K / kBigK;
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = -(kBigStages - 1); s < nsteps; ++s) {
+    if (s >= 0) {
+      // copies issued after step s's: those of the next min(kBigStages - 2, ...) steps
+      const int later = min(nsteps - 1 - s, kBigStages - 2);
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kBigCopies));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kBigCopies);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      lds_barrier();
+    }
+    const int s_pf = s + kBigStages - 1;
+    const int b_pf = (s_pf + kBigStages) % kBigStages, b_cur = s < 0 ? 0 : s % kBigStages;
+    // opaque copies of the stage pointers: accesses through them keep the restrict scopes of
+    // big_step's parameters (pointers the compiler can trace to the __shared__ arrays lose them,
+    // and every operand read would then wait for the copies in flight)
+    typedef __attribute__((address_space(3))) uint4 lds_uint4;
+    lds_uint4 *a_cur = (lds_uint4*)As[b_cur], *w_cur = (lds_uint4*)Ws[b_cur];
+    lds_uint4 *a_nx = (lds_uint4*)As[b_pf], *w_nx = (lds_uint4*)Ws[b_pf];
+    asm volatile("" : "+s"(a_cur), "+s"(w_cur), "+s"(a_nx), "+s"(w_nx));
+    big_step(G, W, m0, wn0, wn_end, s_pf < nsteps, s_pf * kBigK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
+             (uint4*)a_nx, (uint4*)w_nx, acc, w, lane);
+  }
+  // ---- epilogue (same consumers as gemm_kernel); one loop per consumer keeps each simple
+  const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
+  const int mb = m0 + 128 * wm + 4 * g;  // + 16 mt + i
+  if (E.kind == GemmEpilogue::PARTIALS || E.kind == GemmEpilogue::STORE) {
+    const bool f32 = E.kind == GemmEpilogue::PARTIALS;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = n0 + 64 * wn + 16 * nt + j;
+      if (n >= G.N) continue;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mb + 16 * mt + i;
+          if (m >= G.M) continue;
+          if (f32) G.C[(int64_t)m * G.ldc + n] = acc[mt][nt][i];
+          else E.y[(int64_t)m * G.N + n] = f32_to_bf16(acc[mt][nt][i]);
+        }
+    }
+  } else if (E.kind == GemmEpilogue::QUERY) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = n0 + 64 * wn + 16 * nt + j;
+      const int h = n / dqk, u = n - h * dqk;
+      const bool rope = u >= E.dn, odd = (u - E.dn) & 1;
+      const int p = (u - E.dn) >> 1;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mb + 16 * mt + i;
+          const float x = acc[mt][nt][i];
+          const float other = __shfl_xor(x, 1);  // every lane takes part
+          if (m >= G.M || n >= G.N) continue;
+          float yv = x;
+          if (rope) {
+            const float c = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
+            yv = odd ? other * sn + x * c : x * c - other * sn;
+          }
+          E.y[(int64_t)m * G.N + n] = f32_to_bf16(yv);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = n0 + 64 * wn + 16 * nt + j;
+      if (n >= G.N) continue;
+      const int h = n / dkv, u = n - h * dkv;
+      bf16_t* dst = u < E.dn ? E.y + (int64_t)h * dqk + u : E.y2 + (int64_t)h * E.dv + (u - E.dn);
+      const int64_t row = u < E.dn ? (int64_t)E.H * dqk : (int64_t)E.H * E.dv;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mb + 16 * mt + i;
+          if (m < G.M) dst[m * row] = f32_to_bf16(acc[mt][nt][i]);
+        }
+    }
+  }
+}
+
+bool big_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda) {
+  // activation offsets are 32-bit byte offsets from the K step's column
+  return d.wk == W_BF16 && M > 1024 && K % kBigK == 0 && (n_split >= N || n_split % kBigN == 0) && N % 8 == 0 &&
+         (n_split >= N || (N - n_split) % 8 == 0) && ((int64_t)M * lda + K) * 2 < 0x7FFFFFF0LL;
+}
+
 struct Plan {
   int bm, splits, k_split;
 };
 
 Plan plan(int M, int N, int K) {
   Plan p;
+  if (M > 1024) {  // prefill shapes: whole K per workgroup
+    p.bm = 128;
+    p.splits = 1;
+    p.k_split = K;
+    return p;
+  }
   p.bm = M <= 64 ? 64 : 128;
   const int tiles = ((N + BN - 1) / BN) * ((M + p.bm - 1) / p.bm);
   int splits = 1;
@@ -310,6 +495,11 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
     E.cosT = epi->cosT;
     E.sinT = epi->sinT;
     if (fused) *fused = true;
+  }
+  if (big_ok(d, M, N, K, n_split, lda)) {
+    BigArgs G{(const bf16_t*)A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K};
+    gemm_big_kernel<<<dim3((N + kBigN - 1) / kBigN, (M + kBigM - 1) / kBigM), 512, 0, s>>>(G, E);
+    return hipGetLastError();
   }
   if (aligned) return launch_plan(p, d, A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, stride, E, s);
   // segments not aligned to the column tile: one launch each, same split plan and partial layout
