@@ -300,22 +300,6 @@ __device__ __forceinline__ void issue_tile_copy(const AttnArgs& A, int blk, int 
   }
 }
 
-// Reductions over the lanes that share (lane & 15): the gfx950 row-swap permutes
-// (v_permlane16_swap / v_permlane32_swap) leave {x[l], x[l ^ 16]} (resp. 32) in the
-// two results of every lane.
-__device__ __forceinline__ float xmax16_32(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ float xsum16_32(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
 // Waits until this wave's copies of the oldest in-flight sub-tile have landed, given
 // that `later` further sub-tiles' copies were issued after it.
 __device__ __forceinline__ void wait_copies(int w, int later) {

@@ -99,6 +99,22 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return t;
 }
 
+// Reductions over the lanes that share (lane & 15): the gfx950 row-swap permutes
+// (v_permlane16_swap / v_permlane32_swap) leave {x[l], x[l ^ 16]} (resp. 32) in the
+// two results of every lane.
+__device__ __forceinline__ float xmax16_32(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float xsum16_32(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(), which would wait for every
 // global->LDS copy still in flight (the prefetched tiles too).  Callers make LDS data safe
 // themselves: each wave waits for its own copies of the tile about to be read (vmcnt) and has

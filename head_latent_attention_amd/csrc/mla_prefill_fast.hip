@@ -4,7 +4,8 @@
 // (NeMo "MLA" module: forward with a causal attention mask and softmax_scale).
 //
 // Flash-style: a workgroup owns 32*NW queries of one head and streams 64-key tiles
-// of K and V through double-buffered LDS (direct global->LDS copies).  Each wave
+// of K and V through three LDS buffers (direct global->LDS buffer copies, two tiles in
+// flight, one fence-free barrier per tile).  Each wave
 // keeps 32 queries: S^T = K Q^T with keys as the M dimension, so the softmax
 // probabilities are already in the B-operand layout of O^T = V^T P^T; V^T is read
 // with the transposing LDS read.  Online softmax in the log2 domain with a lazy
@@ -38,11 +39,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 __device__ __forceinline__ int k_swz(int t) { return (t >> 1) & 7; }
 __device__ __forceinline__ int v_swz(int t) { return 2 * (t & 7); }
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
 struct PrefillArgs {
   const bf16_t* q;
   const bf16_t* k;
@@ -53,40 +49,45 @@ struct PrefillArgs {
   int n_qtiles;
 };
 
-// Copies of key tile kt: NW waves share K_SLOTS + V_SLOTS 16-byte slots.
+// Copies of key tile kt: NW waves share K_SLOTS + V_SLOTS 16-byte slots.  Keys past T
+// repeat the last key (their scores are masked).  Offsets are taken from the tile's first
+// row of head h, so they stay far below 4 GB.
 template <int NW>
 __device__ __forceinline__ void issue_kv_copy(const PrefillArgs& P, int h, int kt, uint4* __restrict__ kb,
                                               uint4* __restrict__ vb, int w, int lane) {
   int l = lane;
   asm volatile("" : "+v"(l));
   constexpr int KI = K_SLOTS / 64 / NW, VI = V_SLOTS / 64 / NW;
+  const int k0 = kt * KT, t_max = P.T - 1 - k0;
+  const bf16_t* kbase = P.k + ((int64_t)k0 * P.H + h) * DQK;
+  const bf16_t* vbase = P.v + ((int64_t)k0 * P.H + h) * DV;
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
     const int p = 64 * (KI * w + i) + l;
     const int t = p / KC, c = (p - t * KC) ^ k_swz(t);
-    const int key = min(kt * KT + t, P.T - 1);
-    dma16(P.k + ((int64_t)key * P.H + h) * DQK + 8 * c, kb + 64 * (KI * w + i));
+    const int tt = min(t, t_max);
+    dma16_buf(kbase, 0x7FFFFFF0u, (uint32_t)((tt * P.H * DQK + 8 * c) * 2), kb + 64 * (KI * w + i));
   }
 #pragma unroll
   for (int i = 0; i < VI; ++i) {
     const int p = 64 * (VI * w + i) + l;
     const int t = p / VC, c = (p - t * VC) ^ v_swz(t);
-    const int key = min(kt * KT + t, P.T - 1);
-    dma16(P.v + ((int64_t)key * P.H + h) * DV + 8 * c, vb + 64 * (VI * w + i));
+    const int tt = min(t, t_max);
+    dma16_buf(vbase, 0x7FFFFFF0u, (uint32_t)((tt * P.H * DV + 8 * c) * 2), vb + 64 * (VI * w + i));
   }
 }
 
 template <int NW>
-__device__ __forceinline__ void prefill_tile(const PrefillArgs& P, int h, int kt, int n_kt, int qw0,
-                                             const uint4* __restrict__ kb, const uint4* __restrict__ vb,
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& P, int h, int kt, bool copy, int kt_pf, bool compute,
+                                             int qw0, const uint4* __restrict__ kb, const uint4* __restrict__ vb,
                                              uint4* __restrict__ kn, uint4* __restrict__ vn,
                                              const bf16x8 (&qf)[2][DQK / 32], f32x4 (&o)[DV / 16][2],
                                              float (&m_run)[2], float (&l_run)[2], const int (&kbase)[2],
                                              const int (&vbase)[4], int w, int lane) {
   const int g = lane >> 4, j = lane & 15;
-  if (kt + 1 < n_kt) issue_kv_copy<NW>(P, h, kt + 1, kn, vn, w, lane);
+  if (copy) issue_kv_copy<NW>(P, h, kt_pf, kn, vn, w, lane);
   const int k0 = kt * KT;
-  if (k0 <= qw0 + 31) {  // this wave has queries that see keys of the tile
+  if (compute && k0 <= qw0 + 31) {  // this wave has queries that see keys of the tile
     // ---- S^T[key][query]
     f32x4 s[4][2];
 #pragma unroll
@@ -101,42 +102,46 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& P, int h, int kt
         for (int nt = 0; nt < 2; ++nt) s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nt][ks], s[mt][nt], 0, 0, 0);
       }
     }
-    // ---- online softmax per query (lane's query: qw0 + 16*nt + j)
+    // ---- online softmax per query (lane's query: qw0 + 16*nt + j).  Every query sees key 0 in
+    // tile 0 (computed by every wave), so the running max is finite from the first tile on.
     const bool diag = k0 + KT - 1 > qw0;
     bf16x8 pb[2][2];  // [nt][kk]
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int qi = qw0 + 16 * nt + j;
       float x[4][4];
-      float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * mt + 4 * g + i;
-          const float v = s[mt][nt][i] * P.scale_log2;
-          x[mt][i] = (diag && key > qi) ? -INFINITY : v;
-          mx = fmaxf(mx, x[mt][i]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int i = 0; i < 4; ++i) x[mt][i] = s[mt][nt][i] * P.scale_log2;
+      if (diag) {  // causal mask inside the diagonal tiles only
+        const int qi = qw0 + 16 * nt + j;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + 16 * mt + 4 * g + i > qi) x[mt][i] = -INFINITY;
+      }
+      float mx = x[0][0];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[mt][i]);
+      mx = xmax16_32(mx);
       const float m_new = (m_run[nt] == -INFINITY || mx > m_run[nt] + kRescaleThreshold) ? mx : m_run[nt];
-      const float corr = (m_run[nt] == -INFINITY || m_new == -INFINITY) ? (m_run[nt] == m_new ? 1.f : 0.f)
-                                                                         : exp2f(m_run[nt] - m_new);
+      const float corr = m_run[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
       float sum = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         float p[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = m_new == -INFINITY ? 0.f : exp2f(x[2 * kk][i] - m_new);
-          p[4 + i] = m_new == -INFINITY ? 0.f : exp2f(x[2 * kk + 1][i] - m_new);
+          p[i] = __builtin_amdgcn_exp2f(x[2 * kk][i] - m_new);
+          p[4 + i] = __builtin_amdgcn_exp2f(x[2 * kk + 1][i] - m_new);
           sum += p[i] + p[4 + i];
         }
         pb[nt][kk] = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
       }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
+      sum = xsum16_32(sum);
       l_run[nt] = l_run[nt] * corr + sum;
       m_run[nt] = m_new;
       if (__any(corr != 1.f)) {
@@ -160,14 +165,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& P, int h, int kt
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
 }
+
+constexpr int kStages = 3;  // K/V tiles in LDS: the current one and two in flight
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P) {
-  __shared__ __attribute__((aligned(16))) uint4 kbuf[2][K_SLOTS];
-  __shared__ __attribute__((aligned(16))) uint4 vbuf[2][V_SLOTS];
+  __shared__ __attribute__((aligned(16))) uint4 kbuf[kStages][K_SLOTS];
+  __shared__ __attribute__((aligned(16))) uint4 vbuf[kStages][V_SLOTS];
   constexpr int BQ = 32 * NW;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -192,7 +197,6 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
     vbase[1] = half ^ v_swz(tA);            // chunk XOR
     vbase[2] = vbase[3] = 0;
   }
-  issue_kv_copy<NW>(P, h, 0, kbuf[0], vbuf[0], w, lane);
   bf16x8 qf[2][DQK / 32];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -205,13 +209,26 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
 #pragma unroll
   for (int mt = 0; mt < DV / 16; ++mt) o[mt][0] = o[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // the query fragments are complete before the loop, so no read in it waits for the copies
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int cur = 0;
-  for (int kt = 0; kt < n_kt; ++kt) {
-    prefill_tile<NW>(P, h, kt, n_kt, qw0, kbuf[cur], vbuf[cur], kbuf[cur ^ 1], vbuf[cur ^ 1], qf, o, m_run, l_run,
-                     kbase, vbase, w, lane);
-    cur ^= 1;
+  constexpr int kCopies = (K_SLOTS + V_SLOTS) / 64 / NW;  // per wave per tile
+  typedef __attribute__((address_space(3))) uint4 lds_uint4;
+  // steps kt < 0 only put the first kStages - 1 tiles in flight
+  for (int kt = -(kStages - 1); kt < n_kt; ++kt) {
+    if (kt >= 0) {
+      // copies issued after tile kt's: those of the next min(kStages - 2, ...) tiles
+      if (kt + 1 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70 | kCopies);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      lds_barrier();
+    }
+    const int kt_pf = kt + kStages - 1;
+    const int b_pf = (kt_pf + kStages) % kStages, b_cur = kt < 0 ? 0 : kt % kStages;
+    // opaque copies of the buffer pointers keep the restrict scopes of prefill_tile's parameters
+    lds_uint4 *kc = (lds_uint4*)kbuf[b_cur], *vc = (lds_uint4*)vbuf[b_cur];
+    lds_uint4 *kn = (lds_uint4*)kbuf[b_pf], *vn = (lds_uint4*)vbuf[b_pf];
+    asm volatile("" : "+s"(kc), "+s"(vc), "+s"(kn), "+s"(vn));
+    prefill_tile<NW>(P, h, kt < 0 ? 0 : kt, kt_pf < n_kt, kt_pf, kt >= 0, qw0, (const uint4*)kc, (const uint4*)vc,
+                     (uint4*)kn, (uint4*)vn, qf, o, m_run, l_run, kbase, vbase, w, lane);
   }
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
