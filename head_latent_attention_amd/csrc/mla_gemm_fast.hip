@@ -253,6 +253,8 @@ struct BigArgs {
   float* C;
   int64_t ldc;
   int M, N, K;
+  int k_split;           // K range per workgroup along grid z (partial sums)
+  int64_t split_stride;  // elements between the partial sums of consecutive ranges
 };
 
 // Copies of K step k0 into one stage.  Rows past M and columns past the segment are clamped
@@ -318,7 +320,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
   const bool seg1 = n0 >= G.n_split;
   const WeightView W = seg1 ? G.W1 : G.W0;
   const int wn0 = seg1 ? n0 - G.n_split : n0, wn_end = seg1 ? G.N - G.n_split : G.n_split;
-  const int nsteps = G.K / kBigK;
+  const int kbeg = blockIdx.z * G.k_split;
+  const int nsteps = (min(G.K, kbeg + G.k_split) - kbeg) / kBigK;
   f32x4 acc[8][4];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
     lds_uint4 *a_cur = (lds_uint4*)As[b_cur], *w_cur = (lds_uint4*)Ws[b_cur];
     lds_uint4 *a_nx = (lds_uint4*)As[b_pf], *w_nx = (lds_uint4*)Ws[b_pf];
     asm volatile("" : "+s"(a_cur), "+s"(w_cur), "+s"(a_nx), "+s"(w_nx));
-    big_step(G, W, m0, wn0, wn_end, s_pf < nsteps, s_pf * kBigK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
+    big_step(G, W, m0, wn0, wn_end, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
              (uint4*)a_nx, (uint4*)w_nx, acc, w, lane);
   }
   // ---- epilogue (same consumers as gemm_kernel); one loop per consumer keeps each simple
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
         for (int i = 0; i < 4; ++i) {
           const int m = mb + 16 * mt + i;
           if (m >= G.M) continue;
-          if (f32) G.C[(int64_t)m * G.ldc + n] = acc[mt][nt][i];
+          if (f32) G.C[(int64_t)blockIdx.z * G.split_stride + (int64_t)m * G.ldc + n] = acc[mt][nt][i];
           else E.y[(int64_t)m * G.N + n] = f32_to_bf16(acc[mt][nt][i]);
         }
     }
@@ -418,10 +421,18 @@ struct Plan {
 
 Plan plan(int M, int N, int K) {
   Plan p;
-  if (M > 1024) {  // prefill shapes: whole K per workgroup
+  if (M > 1024) {  // prefill shapes (256 x 256 tiles): whole K per workgroup, unless the
+    // tile count leaves most of a last round of one workgroup per CU idle and K is long:
+    // then two K ranges (partial sums) halve the rounds' length
     p.bm = 128;
     p.splits = 1;
     p.k_split = K;
+    const int64_t tiles = (int64_t)((N + 255) / 256) * ((M + 255) / 256);
+    const double r1 = (double)((tiles + 255) / 256), r2 = (double)((2 * tiles + 255) / 256) / 2.0;
+    if (K >= 2048 && K % 64 == 0 && r2 <= 0.75 * r1) {
+      p.splits = 2;
+      p.k_split = K / 2;
+    }
     return p;
   }
   p.bm = M <= 64 ? 64 : 128;
@@ -497,8 +508,8 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
     if (fused) *fused = true;
   }
   if (big_ok(d, M, N, K, n_split, lda)) {
-    BigArgs G{(const bf16_t*)A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K};
-    gemm_big_kernel<<<dim3((N + kBigN - 1) / kBigN, (M + kBigM - 1) / kBigM), 512, 0, s>>>(G, E);
+    BigArgs G{(const bf16_t*)A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, p.k_split, stride};
+    gemm_big_kernel<<<dim3((N + kBigN - 1) / kBigN, (M + kBigM - 1) / kBigM, p.splits), 512, 0, s>>>(G, E);
     return hipGetLastError();
   }
   if (aligned) return launch_plan(p, d, A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, stride, E, s);
