@@ -348,11 +348,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
     big_step(G, W, m0, wn0, wn_end, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
              (uint4*)a_nx, (uint4*)w_nx, acc, w, lane);
   }
-  // ---- epilogue (same consumers as gemm_kernel); one loop per consumer keeps each simple
+  // ---- epilogue (same consumers as gemm_kernel)
   const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
-  const int mb = m0 + 128 * wm + 4 * g;  // + 16 mt + i
-  if (E.kind == GemmEpilogue::PARTIALS || E.kind == GemmEpilogue::STORE) {
-    const bool f32 = E.kind == GemmEpilogue::PARTIALS;
+  const int mb = 128 * wm + 4 * g;  // tile row of acc[mt][.][i]: mb + 16 mt + i
+  if (E.kind == GemmEpilogue::PARTIALS) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int n = n0 + 64 * wn + 16 * nt + j;
@@ -361,50 +360,55 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = mb + 16 * mt + i;
-          if (m >= G.M) continue;
-          if (f32) G.C[(int64_t)blockIdx.z * G.split_stride + (int64_t)m * G.ldc + n] = acc[mt][nt][i];
-          else E.y[(int64_t)m * G.N + n] = f32_to_bf16(acc[mt][nt][i]);
+          const int m = m0 + mb + 16 * mt + i;
+          if (m < G.M) G.C[(int64_t)blockIdx.z * G.split_stride + (int64_t)m * G.ldc + n] = acc[mt][nt][i];
         }
     }
-  } else if (E.kind == GemmEpilogue::QUERY) {
+    return;
+  }
+  // bf16 consumers: the tile is staged in LDS (row-major, 512-byte rows, 16-byte chunks XOR-
+  // swizzled by row) so that global stores are whole 16-byte chunks of 8 consecutive columns;
+  // the query's RoPE is applied on the way (the partner column of a pair sits in lane j ^ 1)
+  lds_barrier();  // every wave is done with the stage buffers
+  bf16_t* st = (bf16_t*)&As[0][0];  // 256 x 256 bf16 = the 128 KB of stage buffers
+  auto chunk_of = [](int r, int c) { return 32 * r + (c ^ (r & 31)); };  // 16-byte chunk slot
+  const bool query = E.kind == GemmEpilogue::QUERY;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = n0 + 64 * wn + 16 * nt + j;
-      const int h = n / dqk, u = n - h * dqk;
-      const bool rope = u >= E.dn, odd = (u - E.dn) & 1;
-      const int p = (u - E.dn) >> 1;
+  for (int nt = 0; nt < 4; ++nt) {
+    const int c = 64 * wn + 16 * nt + j;
+    const int u = (n0 + c) % dqk;
+    const bool rope = query && u >= E.dn, odd = (u - E.dn) & 1;
+    const int p = (u - E.dn) >> 1;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mb + 16 * mt + i;
-          const float x = acc[mt][nt][i];
-          const float other = __shfl_xor(x, 1);  // every lane takes part
-          if (m >= G.M || n >= G.N) continue;
-          float yv = x;
+      for (int i = 0; i < 4; ++i) {
+        const int r = mb + 16 * mt + i;
+        float y = acc[mt][nt][i];
+        if (query) {
+          const float other = __shfl_xor(y, 1);  // every lane takes part
           if (rope) {
-            const float c = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
-            yv = odd ? other * sn + x * c : x * c - other * sn;
+            const int m = min(m0 + r, G.M - 1);
+            const float cs = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
+            y = odd ? other * sn + y * cs : y * cs - other * sn;
           }
-          E.y[(int64_t)m * G.N + n] = f32_to_bf16(yv);
         }
-    }
-  } else {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = n0 + 64 * wn + 16 * nt + j;
-      if (n >= G.N) continue;
+        st[chunk_of(r, c >> 3) * 8 + (c & 7)] = f32_to_bf16(y);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's part of the tile is in LDS
+  lds_barrier();
+  for (int e = tid; e < kBigM * kBigN / 8; e += 512) {
+    const int r = e >> 5, c8 = e & 31;
+    const int m = m0 + r, n = n0 + 8 * c8;
+    if (m >= G.M || n >= G.N) continue;
+    const uint4 v = *(const uint4*)&st[chunk_of(r, c8) * 8];
+    if (E.kind == GemmEpilogue::KV) {
       const int h = n / dkv, u = n - h * dkv;
-      bf16_t* dst = u < E.dn ? E.y + (int64_t)h * dqk + u : E.y2 + (int64_t)h * E.dv + (u - E.dn);
-      const int64_t row = u < E.dn ? (int64_t)E.H * dqk : (int64_t)E.H * E.dv;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mb + 16 * mt + i;
-          if (m < G.M) dst[m * row] = f32_to_bf16(acc[mt][nt][i]);
-        }
+      bf16_t* dst = u < E.dn ? E.y + ((int64_t)m * E.H + h) * dqk + u : E.y2 + ((int64_t)m * E.H + h) * E.dv + (u - E.dn);
+      *(uint4*)dst = v;
+    } else {
+      *(uint4*)&E.y[(int64_t)m * G.N + n] = v;
     }
   }
 }
@@ -486,7 +490,10 @@ bool fast_gemm_fusable(const Dims& d, int M, int N, int K, int n_split, int kind
   const bool aligned = n_split >= N || n_split % BN == 0;
   // the query consumer pairs columns 2i, 2i+1 of each head's rope part within a lane pair
   const bool pairs_ok = d.dn % 2 == 0 && (d.dn + d.dr) % 2 == 0;
-  return plan(M, N, K).splits == 1 && aligned && (kind != GemmEpilogue::QUERY || pairs_ok);
+  // the k/v consumer stores 16-byte chunks of 8 columns, which must stay inside one head part
+  const bool kv_ok = d.dn % 8 == 0 && d.dv % 8 == 0 && (d.dn + d.dr) % 8 == 0;
+  return plan(M, N, K).splits == 1 && aligned && (kind != GemmEpilogue::QUERY || pairs_ok) &&
+         (kind != GemmEpilogue::KV || kv_ok);
 }
 
 hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split, const WeightView& W1,
