@@ -16,6 +16,9 @@ Page references (titles of the source pages):
   [MlaWeights] atlas docs, spark_model::layers::qwen3_attention, Struct MlaWeights
   [NKI-Decode] AWS Neuron NKI, "MLA Decode QKV Kernel API Reference"
   [NKI-CTE]    AWS Neuron NKI, "QKV CTE MLA Kernel API Reference"
+  [YaRN]       Peng, Quesnelle, Fan, Shippole, "YaRN: Efficient Context Window Extension
+               of Large Language Models" (2023), the published method the [Mla] scale
+               and the [MlaWeights] yarn_inv_freq table refer to
 
 Readings where the pages are silent (each listed in the design notes too):
   * RMSNorm is x * (mean(x^2) + eps)^-1/2 * gamma with gamma used as is.
@@ -24,6 +27,13 @@ Readings where the pages are silent (each listed in the design notes too):
   * The cached row is [normalised c_kv | roped k_pe]; k_pe is not normalised.
   * Positions are 0-based; a decode token at position ctx-1 attends to all ctx
     rows including its own.
+  * YaRN: pair i keeps its frequency while its wavelength fits at least beta_fast
+    times into the original context, is divided by the extension factor once it
+    fits at most beta_slow times, and in between is blended with a weight that is
+    linear in the pair index (the pair bounds rounded outward); the magnitude
+    0.1*m*ln(factor)+1 enters the score scale squared and leaves cos/sin unscaled.
+  * The optional layer-input RMSNorm (input_norm_w) uses the same formula and eps
+    as the two latent norms and is applied to x before the stage-1 projection.
 
 Parity pins: every function here is checked in tests/test_oracle_*.py against
 closed forms, textbook special cases, torch's CPU float8 decoding, or
@@ -38,7 +48,7 @@ import numpy as np
 
 __all__ = [
     "e4m3fn_value", "decode_tensor", "rms_norm", "rope_angles", "rope_interleaved",
-    "softmax_scale", "project", "project_rows", "expand_kv", "attention", "mla_prefill", "mla_decode", "decode_attention",
+    "softmax_scale", "yarn_inv_freq", "yarn_mscale", "input_norm", "project", "project_rows", "expand_kv", "attention", "mla_prefill", "mla_decode", "decode_attention",
     "place_rows", "cache_read_dense", "decode_weights", "dims_of",
 ]
 
@@ -96,13 +106,49 @@ def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     return x / np.sqrt(ms + eps) * gamma
 
 
-def rope_angles(positions: np.ndarray, rope_dim: int, theta: float = 10000.0) -> np.ndarray:
-    """Angle of pair i at each position: pos * theta^(-2i/rope_dim), shape [T, rope_dim/2].
+def rope_angles(positions: np.ndarray, rope_dim: int, theta: float = 10000.0,
+                inv_freq: Optional[np.ndarray] = None) -> np.ndarray:
+    """Angle of pair i at each position: pos * inv_freq[i], shape [T, rope_dim/2].
 
-    [MlaWeights] main_inv_freq: the plain theta = 10000 inverse frequencies with no YaRN."""
+    Without a table inv_freq[i] = theta^(-2i/rope_dim) ([MlaWeights] main_inv_freq:
+    the plain theta = 10000 inverse frequencies with no YaRN); a given table is
+    used as is ([MlaWeights] yarn_inv_freq)."""
+    if inv_freq is None:
+        i = np.arange(rope_dim // 2, dtype=np.float64)
+        inv_freq = theta ** (-2.0 * i / rope_dim)
+    return np.asarray(positions, dtype=np.float64)[:, None] * np.asarray(inv_freq, np.float64)[None, :]
+
+
+def yarn_inv_freq(rope_dim: int, theta: float, factor: float, original_max_position: int,
+                  beta_fast: float = 32.0, beta_slow: float = 1.0) -> np.ndarray:
+    """YaRN inverse frequencies [rope_dim/2] ([YaRN] section 3.2, interpolation by parts).
+
+    A pair whose wavelength 2*pi/f_i fits at least beta_fast times into the original
+    context keeps f_i; one that fits at most beta_slow times is interpolated to
+    f_i/factor; in between the two are blended.  The pair index at which the count
+    equals n solves original_max_position * f_i / (2*pi) = n; the blend weight is
+    linear in the pair index between floor(index(beta_fast)) (clamped at 0) and
+    ceil(index(beta_slow)) (clamped at rope_dim-1).  factor <= 1 is plain RoPE."""
     i = np.arange(rope_dim // 2, dtype=np.float64)
-    inv_freq = theta ** (-2.0 * i / rope_dim)
-    return np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    plain = theta ** (-2.0 * i / rope_dim)
+    if factor <= 1.0:
+        return plain
+
+    def pair_index(rotations: float) -> float:
+        return rope_dim * math.log(original_max_position / (rotations * 2.0 * math.pi)) / (2.0 * math.log(theta))
+
+    lo = max(math.floor(pair_index(beta_fast)), 0)
+    hi = min(math.ceil(pair_index(beta_slow)), rope_dim - 1)
+    if hi > lo:
+        w_interp = np.clip((i - lo) / (hi - lo), 0.0, 1.0)
+    else:
+        w_interp = (i > lo).astype(np.float64)
+    return plain / factor * w_interp + plain * (1.0 - w_interp)
+
+
+def yarn_mscale(factor: float, m: float = 1.0) -> float:
+    """YaRN's attention magnitude 0.1 * m * ln(factor) + 1 ([YaRN] section 3.4), 1 for factor <= 1."""
+    return 1.0 if factor <= 1.0 else 0.1 * m * math.log(factor) + 1.0
 
 
 def rope_interleaved(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
@@ -122,9 +168,19 @@ def rope_interleaved(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
     return np.stack([re, im], axis=-1).reshape(shape)
 
 
-def softmax_scale(qk_nope: int, qk_rope: int) -> float:
-    """[NeMo-MLA] softmax_scale = qk_head_dim ** -0.5; [Mla] scale = 1/sqrt(qk_nope + qk_rope)."""
-    return 1.0 / math.sqrt(qk_nope + qk_rope)
+def softmax_scale(qk_nope: int, qk_rope: int, rope_factor: float = 1.0, mscale_all_dim: float = 1.0) -> float:
+    """[NeMo-MLA] softmax_scale = qk_head_dim ** -0.5; [Mla] scale: 1/sqrt(qk_nope + qk_rope)
+    times the square of YaRN's magnitude (which is 1 without YaRN)."""
+    return yarn_mscale(rope_factor, mscale_all_dim) ** 2 / math.sqrt(qk_nope + qk_rope)
+
+
+def input_norm(W: Dict[str, np.ndarray], x: np.ndarray, dims: dict) -> np.ndarray:
+    """The layer's input RMSNorm when an input_norm_w gamma [hidden] is given, else x
+    ([NKI-Decode] input_norm_w: folded into the hidden load; norm_eps is the epsilon of
+    every RMSNorm of that kernel)."""
+    if "input_norm_w" not in W:
+        return x
+    return rms_norm(x, W["input_norm_w"], dims["norm_eps"])
 
 
 # ----------------------------------------------------------------------------- projections
@@ -139,11 +195,15 @@ def project(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, dims
     RoPE on each head's trailing qk_rope dims and once on k_pe ([Mla] description:
     the rope key is shared by every head; [NKI-CTE] final assembly).
 
+    With input_norm_w in W, x first goes through the layer's input RMSNorm.
+
     Returns q [T, H, dqk] (q_pe roped) and rows [T, kv_lora + qk_rope] = [c_norm | k_pe roped].
     """
     H, dn, dr, Lkv = dims["n_heads"], dims["qk_nope"], dims["qk_rope"], dims["kv_lora_rank"]
     eps = dims["norm_eps"]
-    ang = rope_angles(positions, dr, dims.get("rope_theta", 10000.0))
+    ang = rope_angles(positions, dr, dims.get("rope_theta", 10000.0), dims.get("inv_freq"))
+    rows = project_rows(W, x, positions, dims)
+    x = input_norm(W, x, dims)
     if "wq_a" in W:
         cq = rms_norm(x @ W["wq_a"], W["q_norm_w"], eps)
         q = cq @ W["wq_b"]
@@ -151,7 +211,7 @@ def project(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, dims
         q = x @ W["wq_b"]
     q = q.reshape(x.shape[0], H, dn + dr)
     q = np.concatenate([q[..., :dn], rope_interleaved(q[..., dn:], ang)], axis=-1)
-    return q, project_rows(W, x, positions, dims)
+    return q, rows
 
 
 def project_rows(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, dims: dict) -> np.ndarray:
@@ -159,10 +219,11 @@ def project_rows(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray,
 
     x @ wkv_a gives one cache row per token split as [c_kv | k_pe] ([NKI-Decode]
     wkv_a parameter; [NKI-CTE] stage-1 split); the latent is RMS-normed with
-    kv_norm_w, the rope key rotated at the token's position and not normed."""
+    kv_norm_w, the rope key rotated at the token's position and not normed.  x is
+    first put through the layer-input RMSNorm when W holds input_norm_w."""
     Lkv, dr = dims["kv_lora_rank"], dims["qk_rope"]
-    ang = rope_angles(positions, dr, dims.get("rope_theta", 10000.0))
-    kva = x @ W["wkv_a"]
+    ang = rope_angles(positions, dr, dims.get("rope_theta", 10000.0), dims.get("inv_freq"))
+    kva = input_norm(W, x, dims) @ W["wkv_a"]
     c = rms_norm(kva[:, :Lkv], W["kv_norm_w"], dims["norm_eps"])
     p = rope_interleaved(kva[:, Lkv:], ang)
     return np.concatenate([c, p], axis=-1)
@@ -289,8 +350,15 @@ def decode_weights(tensors: dict) -> Dict[str, np.ndarray]:
 
 def dims_of(shape) -> dict:
     """The scalar parameters of a layer as a plain dict (names follow [NKI-Decode] /
-    [NKI-CTE] parameters)."""
-    return dict(hidden=shape.hidden, n_heads=shape.n_heads, q_lora_rank=shape.q_lora_rank,
-                kv_lora_rank=shape.kv_lora_rank, qk_nope=shape.qk_nope, qk_rope=shape.qk_rope,
-                v_dim=shape.v_dim, norm_eps=shape.norm_eps, rope_theta=shape.rope_theta,
-                softmax_scale=softmax_scale(shape.qk_nope, shape.qk_rope))
+    [NKI-CTE] parameters).  With a YaRN factor above 1 the dict also holds the
+    YaRN inverse-frequency table and the score scale includes YaRN's magnitude."""
+    factor = getattr(shape, "rope_factor", 1.0)
+    d = dict(hidden=shape.hidden, n_heads=shape.n_heads, q_lora_rank=shape.q_lora_rank,
+             kv_lora_rank=shape.kv_lora_rank, qk_nope=shape.qk_nope, qk_rope=shape.qk_rope,
+             v_dim=shape.v_dim, norm_eps=shape.norm_eps, rope_theta=shape.rope_theta,
+             softmax_scale=softmax_scale(shape.qk_nope, shape.qk_rope, factor,
+                                         getattr(shape, "rope_mscale_all_dim", 1.0)))
+    if factor > 1.0:
+        d["inv_freq"] = yarn_inv_freq(shape.qk_rope, shape.rope_theta, factor, shape.rope_original_max,
+                                      shape.rope_beta_fast, shape.rope_beta_slow)
+    return d

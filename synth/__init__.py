@@ -41,6 +41,14 @@ class MlaShape:
     block_size: int = 64
     rope_theta: float = 10000.0
     norm_eps: float = 1e-6
+    # YaRN context extension (factor 1 = plain RoPE); the values of the other fields are
+    # the published DeepSeek-V3 rope-scaling settings
+    rope_factor: float = 1.0
+    rope_original_max: int = 4096
+    rope_beta_fast: float = 32.0
+    rope_beta_slow: float = 1.0
+    rope_mscale_all_dim: float = 1.0
+    input_norm: bool = False  # the layer-input RMSNorm gamma input_norm_w is given
 
     @property
     def qk_head(self) -> int:
@@ -178,7 +186,10 @@ def make_weights(w: Workload) -> dict:
     for name, shp in weight_shapes(s).items():
         g = rng(w.number, name).standard_normal(shp, dtype=np.float32) * np.float32(0.02)
         out[name] = encode(g, s.weight, w.number, name)
-    for name, n in (("q_norm_w", s.q_lora_rank), ("kv_norm_w", s.kv_lora_rank)):
+    gammas = [("q_norm_w", s.q_lora_rank), ("kv_norm_w", s.kv_lora_rank)]
+    if s.input_norm:
+        gammas.append(("input_norm_w", s.hidden))
+    for name, n in gammas:
         if n == 0:
             continue
         g = (1.0 + 0.1 * rng(w.number, name).standard_normal(n)).astype(np.float32)

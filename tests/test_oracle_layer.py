@@ -9,7 +9,7 @@ import synth
 from oracle import mla_oracle as O
 
 
-def _tiny_weights(seed, D, H, Lq, Lkv, dn, dr, dv):
+def _tiny_weights(seed, D, H, Lq, Lkv, dn, dr, dv, input_norm=False):
     r = synth.rng(seed, "tiny")
     W = {
         "wq_b": r.standard_normal((Lq or D, H * (dn + dr))) * 0.3,
@@ -21,16 +21,18 @@ def _tiny_weights(seed, D, H, Lq, Lkv, dn, dr, dv):
     if Lq:
         W["wq_a"] = r.standard_normal((D, Lq)) * 0.3
         W["q_norm_w"] = 1 + 0.1 * r.standard_normal(Lq)
+    if input_norm:
+        W["input_norm_w"] = 1 + 0.1 * r.standard_normal(D)
     dims = dict(hidden=D, n_heads=H, q_lora_rank=Lq, kv_lora_rank=Lkv, qk_nope=dn, qk_rope=dr,
                 v_dim=dv, norm_eps=1e-6, rope_theta=10000.0, softmax_scale=1 / math.sqrt(dn + dr))
     return W, dims
 
 
-def _rope_pair_loops(vec, pos, theta=10000.0):
+def _rope_pair_loops(vec, pos, theta=10000.0, inv_freq=None):
     dr = len(vec)
     out = list(vec)
     for i in range(dr // 2):
-        a = pos * theta ** (-2.0 * i / dr)
+        a = pos * (theta ** (-2.0 * i / dr) if inv_freq is None else inv_freq[i])
         out[2 * i] = vec[2 * i] * math.cos(a) - vec[2 * i + 1] * math.sin(a)
         out[2 * i + 1] = vec[2 * i] * math.sin(a) + vec[2 * i + 1] * math.cos(a)
     return out
@@ -50,19 +52,23 @@ def _layer_loops(W, x, d):
     K = [[[0.0] * dqk for _ in range(H)] for _ in range(T)]
     V = [[[0.0] * dv for _ in range(H)] for _ in range(T)]
     rows = []
+    f = d.get("inv_freq")
     for t in range(T):
+        xt = [x[t, i] for i in range(D)]
+        if "input_norm_w" in W:
+            xt = _rms_loops(xt, W["input_norm_w"], d["norm_eps"])
         if Lq:
-            cq = [sum(x[t, i] * W["wq_a"][i, j] for i in range(D)) for j in range(Lq)]
+            cq = [sum(xt[i] * W["wq_a"][i, j] for i in range(D)) for j in range(Lq)]
             qin = _rms_loops(cq, W["q_norm_w"], d["norm_eps"])
         else:
-            qin = [x[t, i] for i in range(D)]
+            qin = xt
         qf = [sum(qin[j] * W["wq_b"][j, c] for j in range(len(qin))) for c in range(H * dqk)]
         for h in range(H):
             head = qf[h * dqk:(h + 1) * dqk]
-            q[t][h] = head[:dn] + _rope_pair_loops(head[dn:], t)
-        kva = [sum(x[t, i] * W["wkv_a"][i, c] for i in range(D)) for c in range(Lkv + dr)]
+            q[t][h] = head[:dn] + _rope_pair_loops(head[dn:], t, inv_freq=f)
+        kva = [sum(xt[i] * W["wkv_a"][i, c] for i in range(D)) for c in range(Lkv + dr)]
         cn = _rms_loops(kva[:Lkv], W["kv_norm_w"], d["norm_eps"])
-        p = _rope_pair_loops(kva[Lkv:], t)
+        p = _rope_pair_loops(kva[Lkv:], t, inv_freq=f)
         rows.append(cn + p)
         for h in range(H):
             e = [sum(cn[c] * W["wkv_b"][c, h * (dn + dv) + j] for c in range(Lkv)) for j in range(dn + dv)]
@@ -82,9 +88,14 @@ def _layer_loops(W, x, d):
     return dict(q=np.array(q), k=np.array(K), v=np.array(V), rows=np.array(rows), o=np.array(o), y=np.array(y))
 
 
-@pytest.mark.parametrize("Lq", [5, 0])
-def test_prefill_matches_scalar_loops(Lq):
-    W, d = _tiny_weights(11 + Lq, D=7, H=2, Lq=Lq, Lkv=6, dn=3, dr=4, dv=2)
+@pytest.mark.parametrize("Lq,extras", [(5, False), (0, False), (5, True), (0, True)])
+def test_prefill_matches_scalar_loops(Lq, extras):
+    """extras: the layer-input RMSNorm, a given two-pair frequency table in place of
+    theta^(-2i/dr), and the score scale with YaRN's factor-4 magnitude."""
+    W, d = _tiny_weights(11 + Lq, D=7, H=2, Lq=Lq, Lkv=6, dn=3, dr=4, dv=2, input_norm=extras)
+    if extras:
+        d["inv_freq"] = np.array([0.9, 0.004])
+        d["softmax_scale"] = O.softmax_scale(3, 4, 4.0, 1.0)
     x = synth.rng(12, "x").standard_normal((4, 7))
     ref = _layer_loops(W, x, d)
     got = O.mla_prefill(W, x, d)

@@ -135,6 +135,92 @@ def test_rope_invariants():
             np.testing.assert_allclose(out[t, h], O.rope_interleaved(qh[t:t + 1, h], O.rope_angles(np.array([t + 1]), dr))[0])
 
 
+# ----------------------------------------------------------------------------- YaRN
+def _turns(rope_dim, theta, L):
+    """Full turns pair i makes over L positions when it advances theta^(-2i/d) rad per position."""
+    return np.array([L * theta ** (-2.0 * i / rope_dim) / (2 * math.pi) for i in range(rope_dim // 2)])
+
+
+def test_yarn_factor_one_is_plain_rope():
+    for dr in (16, 64):
+        np.testing.assert_allclose(O.yarn_inv_freq(dr, 10000.0, 1.0, 4096),
+                                   [10000.0 ** (-2 * i / dr) for i in range(dr // 2)], rtol=1e-15)
+    assert O.yarn_mscale(1.0, 1.0) == 1.0 and O.yarn_mscale(0.5, 3.0) == 1.0
+    assert O.softmax_scale(128, 64, 1.0, 1.0) == O.softmax_scale(128, 64)
+
+
+@pytest.mark.parametrize("dr,theta,s,L,bf,bs", [(64, 1e4, 40.0, 4096, 32.0, 1.0), (64, 1e4, 4.0, 2048, 32.0, 1.0),
+                                                (128, 5e5, 8.0, 8192, 16.0, 2.0), (16, 1e4, 8.0, 256, 32.0, 1.0)])
+def test_yarn_regions_follow_turn_counts(dr, theta, s, L, bf, bs):
+    """Kept iff the pair turns >= beta_fast times over the original context, divided by the
+    factor iff it turns <= beta_slow times, blended in between with the interpolated share
+    growing in equal steps from the last kept pair to the first interpolated one."""
+    plain = np.array([theta ** (-2.0 * i / dr) for i in range(dr // 2)])
+    turns = _turns(dr, theta, L)
+    f = O.yarn_inv_freq(dr, theta, s, L, bf, bs)
+    keep, interp = turns >= bf, turns <= bs
+    assert keep.any() and interp.any()
+    np.testing.assert_allclose(f[keep], plain[keep], rtol=1e-15)
+    np.testing.assert_allclose(f[interp], plain[interp] / s, rtol=1e-15)
+    mid = ~keep & ~interp
+    share = (plain[mid] - f[mid]) / (plain[mid] - plain[mid] / s)
+    assert ((share > 0) & (share < 1)).all()
+    steps = np.diff(np.concatenate([[0.0], share, [1.0]]))
+    np.testing.assert_allclose(steps, 1.0 / (mid.sum() + 1), rtol=1e-9)
+
+
+def test_yarn_v3_golden():
+    g = {k: float(v) for k, v in _golden_rows("yarn_v3.txt")}
+    plain = np.array([10000.0 ** (-2.0 * i / 64) for i in range(32)])
+    f = O.yarn_inv_freq(64, 10000.0, 40.0, 4096, 32.0, 1.0)
+    kept = np.nonzero(np.isclose(f, plain, rtol=1e-15, atol=0))[0]
+    interp = np.nonzero(np.isclose(f, plain / 40.0, rtol=1e-15, atol=0))[0]
+    assert kept.max() == g["last_kept_pair"] and (kept == np.arange(kept.max() + 1)).all()
+    assert interp.min() == g["first_interpolated_pair"] and (interp == np.arange(interp.min(), 32)).all()
+    assert O.yarn_mscale(40.0, 1.0) == pytest.approx(g["mscale"], rel=1e-15)
+    assert O.softmax_scale(128, 64, 40.0, 1.0) == pytest.approx(g["score_scale"], rel=1e-15)
+    assert O.yarn_mscale(math.exp(10.0), 1.0) == pytest.approx(2.0, rel=1e-15)
+    assert O.yarn_mscale(math.exp(10.0), 0.5) == pytest.approx(1.5, rel=1e-15)
+    d = O.dims_of(synth.custom(synth.WORKLOADS[3], 120, "yarn", rope_factor=40.0).shape)
+    np.testing.assert_array_equal(d["inv_freq"], f)
+    assert d["softmax_scale"] == pytest.approx(g["score_scale"], rel=1e-15)
+
+
+def test_rope_with_yarn_table_invariants():
+    dr = 64
+    f = O.yarn_inv_freq(dr, 10000.0, 40.0, 4096)
+    r = synth.rng(4, "rope-yarn")
+    q, k = r.standard_normal(dr), r.standard_normal(dr)
+    ang = O.rope_angles(np.array([0, 7, 40000]), dr, inv_freq=f)
+    np.testing.assert_allclose(ang[1], 7 * f, rtol=1e-15)
+    Q = O.rope_interleaved(np.tile(q, (3, 1)), ang)
+    np.testing.assert_allclose(Q[0], q, atol=0)
+    a = O.rope_interleaved(np.stack([q, q]), O.rope_angles(np.array([22, 30005]), dr, inv_freq=f))
+    b = O.rope_interleaved(np.stack([k, k]), O.rope_angles(np.array([17, 30000]), dr, inv_freq=f))
+    assert abs(a[0] @ b[0] - a[1] @ b[1]) < 1e-9
+
+
+# ----------------------------------------------------------------------------- layer-input RMSNorm
+def test_input_norm_closed_form():
+    """Rows that are constant vectors c*1 normalise to c/sqrt(c^2+eps)*gamma, so a layer with
+    input_norm_w equals the layer without it fed with that closed form."""
+    w = synth.custom(synth.WORKLOADS[1], 121, "input-norm", input_norm=True)
+    W = O.decode_weights(synth.make_weights(w))
+    d = O.dims_of(w.shape)
+    cs = np.array([0.5, -3.0, 1e-2, 7.25])
+    x = cs[:, None] * np.ones((1, w.shape.hidden))
+    xn = (cs / np.sqrt(cs * cs + 1e-6))[:, None] * W["input_norm_w"][None]
+    plain = {k: v for k, v in W.items() if k != "input_norm_w"}
+    pos = np.array([0, 3, 9, 200])
+    q1, r1 = O.project(W, x, pos, d)
+    q2, r2 = O.project(plain, xn, pos, d)
+    np.testing.assert_allclose(q1, q2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(r1, r2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(O.project_rows(W, x, pos, d), r2, rtol=1e-12, atol=1e-14)
+    # without the gamma the layer differs (the fold is not a no-op)
+    assert np.abs(O.project(plain, x, pos, d)[0] - q1).max() > 1e-3
+
+
 # ----------------------------------------------------------------------------- softmax attention
 def _attention_loops(q, K, V, scale, qpos):
     Tq, H, _ = q.shape
