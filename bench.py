@@ -14,7 +14,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -55,11 +54,12 @@ def decode_setup(w, device="cuda"):
         slots = synth.slots_for(pg.block_table[b], np.arange(int(n)), s.block_size).astype(np.int64)
         flat[torch.from_numpy(slots).to(device)] = rows
     x = torch_io.to_device(synth.make_x(w, w.B, "x.decode"), device)
-    pos = ctx.astype(np.int64) - 1
-    cos, sin = mla.rope_cos_sin(pos, s.qk_rope, device=device)
     slot = torch.from_numpy(synth.decode_slot_mapping(pg)).to(device)
     bt = torch.from_numpy(pg.block_table).to(device)
     cl = torch.from_numpy(ctx).to(device)
+    # each step builds its rope tables on the device at positions context_lens - 1
+    cos = torch.empty((w.B, s.qk_rope // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
     q = torch.empty((w.B, s.n_heads, s.qk_head), dtype=torch.bfloat16, device=device)
     o = torch.empty((w.B, s.n_heads, s.v_dim), dtype=torch.bfloat16, device=device)
     y = torch.empty((w.B, s.hidden), dtype=torch.bfloat16, device=device)
@@ -77,6 +77,7 @@ def decode_step(S, ev=None):
     mla = S["mla"]
     if ev:
         ev[0].record()
+    mla.mla_rope_tables(S["cl"], S["cl"].numel(), S["cfg"].qk_rope, None, pos_offset=-1, cos=S["cos"], sin=S["sin"])
     mla.mla_decode_qkv_and_scatter(S["cfg"], S["dw"], S["x"], S["cos"], S["sin"], S["cache"], S["slot"], S["q"],
                                    ws=S["ws"]["qkv"])
     if ev:
@@ -118,12 +119,8 @@ def attn_algorithmic_bytes(s, ctx, B):
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "head_latent_attention_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(d, f), "rb").read())
-    return h.hexdigest()[:16]
+    from head_latent_attention_amd.profiling import source_hash
+    return source_hash(os.path.join(ROOT, "head_latent_attention_amd", "csrc"))
 
 
 def traffic_from_profiles(name):

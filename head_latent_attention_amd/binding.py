@@ -8,9 +8,8 @@ happens in the library's HIP kernels; torch supplies device memory and streams.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
-from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, Structure, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 from typing import Dict, Optional
 
 import numpy as np
@@ -23,7 +22,9 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 FN_QKV_PREFILL, FN_PREFILL_ATTN, FN_DECODE_QKV, FN_DECODE_ATTN, FN_OUT_PROJ = range(5)
 _DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 SYMBOLS = ("mla_qkv_prefill", "mla_prefill_attn", "mla_decode_qkv_and_scatter", "mla_decode_attn_absorbed",
-           "mla_out_proj", "mla_workspace_size", "mla_status_string")
+           "mla_out_proj", "mla_rope_inv_freq", "mla_rope_tables", "mla_workspace_size", "mla_status_string",
+           "mla_rope_score_scale")
+_STATUS_FNS = SYMBOLS[:7]
 
 
 class MlaError(RuntimeError):
@@ -42,7 +43,18 @@ class MlaWeight(Structure):
 
 class MlaWeights(Structure):
     _fields_ = [("wq_a", MlaWeight), ("wq_b", MlaWeight), ("wkv_a", MlaWeight), ("wkv_b", MlaWeight),
-                ("wo", MlaWeight), ("q_norm_w", c_void_p), ("kv_norm_w", c_void_p)]
+                ("wo", MlaWeight), ("q_norm_w", c_void_p), ("kv_norm_w", c_void_p), ("input_norm_w", c_void_p)]
+
+
+class MlaRope(Structure):
+    _fields_ = [("theta", c_double), ("factor", c_double), ("original_max_position", c_int32),
+                ("beta_fast", c_double), ("beta_slow", c_double), ("mscale_all_dim", c_double)]
+
+
+def rope(theta=10000.0, factor=1.0, original_max_position=4096, beta_fast=32.0, beta_slow=1.0,
+         mscale_all_dim=1.0) -> MlaRope:
+    """Rotary settings: plain RoPE with base theta, or YaRN when factor > 1."""
+    return MlaRope(theta, factor, original_max_position, beta_fast, beta_slow, mscale_all_dim)
 
 
 _lib = None
@@ -63,20 +75,27 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_qkv_and_scatter.argtypes = [C, W, P, I32, P, P, P, I64, P, P, P, SZ, P]
     lib.mla_decode_attn_absorbed.argtypes = [C, W, P, I32, P, I64, P, I32, P, P, P, SZ, P]
     lib.mla_out_proj.argtypes = [C, W, P, I32, P, P, SZ, P]
+    lib.mla_rope_inv_freq.argtypes = [POINTER(MlaRope), I32, P, P]
+    lib.mla_rope_tables.argtypes = [I32, I32, P, I32, P, P, P, P]
+    lib.mla_rope_score_scale.argtypes = [POINTER(MlaRope), I32, I32]
+    lib.mla_rope_score_scale.restype = c_double
     lib.mla_workspace_size.argtypes = [C, I32, I32, I32]
     lib.mla_workspace_size.restype = SZ
     lib.mla_status_string.argtypes = [I32]
     lib.mla_status_string.restype = c_char_p
-    for name in SYMBOLS[:5]:
+    for name in _STATUS_FNS:
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
 
 
 def config(hidden, n_heads, q_lora_rank, kv_lora_rank, qk_nope, qk_rope, v_dim, *, act="bf16",
-           weight="bf16", block_size=64, softmax_scale=None, norm_eps=1e-6) -> MlaConfig:
+           weight="bf16", block_size=64, softmax_scale=None, norm_eps=1e-6, rope: Optional[MlaRope] = None) -> MlaConfig:
+    """The layer's config; the score scale defaults to mla_rope_score_scale(rope) (1/sqrt(dqk)
+    times YaRN's magnitude squared when rope has factor > 1)."""
     if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(qk_nope + qk_rope)
+        softmax_scale = load().mla_rope_score_scale(ctypes.byref(rope) if rope is not None else None,
+                                                    qk_nope, qk_rope)
     return MlaConfig(hidden, n_heads, q_lora_rank or 0, kv_lora_rank, qk_nope, qk_rope, v_dim, softmax_scale,
                      norm_eps, block_size, _DTYPES[act], _DTYPES[weight])
 
@@ -104,6 +123,7 @@ class Weights:
             setattr(s, name, MlaWeight(_ptr(t) if t is not None else None, _ptr(sc) if sc is not None else None))
         s.q_norm_w = _ptr(self.tensors.get("q_norm_w")) if "q_norm_w" in self.tensors else None
         s.kv_norm_w = _ptr(self.tensors.get("kv_norm_w"))
+        s.input_norm_w = _ptr(self.tensors.get("input_norm_w"))
         self.struct = s
 
 
@@ -133,16 +153,36 @@ def _ws(ws, cfg, fn, n, max_context=0, device="cuda"):
     return ws, ws.numel()
 
 
-def rope_cos_sin(positions, rope_dim: int, theta: float = 10000.0, device="cuda"):
-    """cos/sin tables [T, rope_dim/2] (fp32) of the interleaved-RoPE angles
-    pos * theta^(-2i/rope_dim), evaluated in float64 on the host.  These are the
-    cos/sin inputs of the projection entry points."""
-    pos = np.asarray(positions, dtype=np.float64)
-    inv = theta ** (-2.0 * np.arange(rope_dim // 2, dtype=np.float64) / rope_dim)
-    ang = pos[:, None] * inv[None, :]
-    c = torch.from_numpy(np.cos(ang).astype(np.float32)).to(device)
-    s = torch.from_numpy(np.sin(ang).astype(np.float32)).to(device)
-    return c, s
+def mla_rope_inv_freq(rope: MlaRope, qk_rope: int, device="cuda", stream=None) -> torch.Tensor:
+    """Inverse frequencies [qk_rope/2] fp64 on the device (plain, or YaRN when factor > 1)."""
+    out = torch.empty(qk_rope // 2, dtype=torch.float64, device=device)
+    _check(load().mla_rope_inv_freq(ctypes.byref(rope), qk_rope, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def mla_rope_tables(positions: Optional[torch.Tensor], n: int, qk_rope: int, inv_freq=None, pos_offset: int = 0,
+                    cos=None, sin=None, stream=None):
+    """cos/sin [n, qk_rope/2] fp32 of (positions[t] + pos_offset) * inv_freq[i] (positions int32 on
+    the device, or None for 0..n-1; inv_freq None for theta = 10000)."""
+    dev = positions.device if positions is not None else (inv_freq.device if inv_freq is not None else "cuda")
+    if positions is not None and (positions.dtype != torch.int32 or positions.numel() != n):
+        raise MlaError("positions must be int32 [n]")
+    if inv_freq is not None and (inv_freq.dtype != torch.float64 or inv_freq.numel() != qk_rope // 2):
+        raise MlaError("inv_freq must be float64 [qk_rope/2]")
+    cos = torch.empty((n, qk_rope // 2), dtype=torch.float32, device=dev) if cos is None else cos
+    sin = torch.empty((n, qk_rope // 2), dtype=torch.float32, device=dev) if sin is None else sin
+    _check(load().mla_rope_tables(n, qk_rope, _ptr(positions), pos_offset, _ptr(inv_freq), _ptr(cos), _ptr(sin),
+                                  _stream(stream)))
+    return cos, sin
+
+
+def rope_cos_sin(positions, rope_dim: int, theta: float = 10000.0, device="cuda", inv_freq=None):
+    """cos/sin tables [T, rope_dim/2] (fp32, on the device) for the given token positions,
+    built by mla_rope_tables; inv_freq (fp64 device table) defaults to plain RoPE with base theta."""
+    pos = torch.as_tensor(np.asarray(positions, dtype=np.int32)).to(device)
+    if inv_freq is None and theta != 10000.0:
+        inv_freq = mla_rope_inv_freq(rope(theta=theta), rope_dim, device)
+    return mla_rope_tables(pos, pos.numel(), rope_dim, inv_freq)
 
 
 def mla_qkv_prefill(cfg, w: Weights, x, cos, sin, q, k, v, kv_cache=None, slot_mapping=None, ws=None,

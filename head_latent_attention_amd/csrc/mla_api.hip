@@ -89,6 +89,7 @@ size_t proj_out_bytes(const Dims& d, int M, int N, int K) {
 int stage1_q_cols(const Dims& d) { return d.Lq > 0 ? d.Lq : d.H * d.dqk(); }
 
 struct QkvWs {
+  void* xn;    // [n, D]                  x after the layer-input RMSNorm (act), when input_norm_w is given
   float* P1;   // [n, stage1_q_cols + R]  stage-1 projection
   float* P2;   // [n, H*dqk]              query up-projection (Lq > 0)
   void* cqn;   // [n, Lq]                 RMSNorm(q latent) * gamma (act)
@@ -101,6 +102,7 @@ size_t qkv_ws(const Dims& d, int n, bool prefill, void* base, QkvWs* out) {
   QkvWs w;
   const int HQ = d.H * d.dqk();
   const int NKV = d.H * (d.dn + d.dv);
+  w.xn = c.take<char>((size_t)n * d.D * act_bytes(d));
   w.P1 = (float*)c.take<char>(proj_out_bytes(d, n, stage1_q_cols(d) + d.R(), d.D));
   // results handed straight to their consumer need no buffer
   const bool q_fused = fast_gemm_fusable(d, n, HQ, d.Lq, HQ, GemmEpilogue::QUERY);
@@ -189,7 +191,8 @@ mla_status project(const Dims& d, const void* A, int64_t lda, const WeightView& 
   return MLA_OK;
 }
 
-// Shared front end of prefill and decode: one projection of x by [wq_a | wkv_a] (by
+// Shared front end of prefill and decode: the layer-input RMSNorm when its gamma is
+// given, one projection of x by [wq_a | wkv_a] (by
 // [wq_b | wkv_a] without a query latent), row builder, query up-projection and RoPE.
 mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, const float* cosT,
                      const float* sinT, void* q, void* kbuf, void* kv_cache, int64_t n_blocks,
@@ -197,6 +200,10 @@ mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, 
   const int64_t n_slots = kv_cache ? n_blocks * d.bs : 0;
   const int HQ = d.H * d.dqk();
   const int NQ1 = stage1_q_cols(d);
+  if (w->input_norm_w) {
+    HIP_TRY(input_norm(d, x, n, w->input_norm_w, ws.xn, s));
+    x = ws.xn;
+  }
   Partials P1;
   const WeightView w1q = d.Lq > 0 ? view(d, w->wq_a, d.Lq) : view(d, w->wq_b, HQ);
   mla_status st = project(d, x, d.D, w1q, NQ1, view(d, w->wkv_a, d.R()), n, NQ1 + d.R(), d.D, ws.P1, &P1, s);
@@ -254,6 +261,31 @@ size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t 
     case MLA_FN_OUT_PROJ: return out_proj_ws(d, n, nullptr, nullptr);
   }
   return 0;
+}
+
+mla_status mla_rope_inv_freq(const mla_rope* r, int32_t qk_rope, double* inv_freq, void* stream) {
+  if (!r || !inv_freq || qk_rope <= 0 || qk_rope % 2 != 0) return MLA_ERR_INVALID_ARG;
+  if (!(r->theta > 1.0) || !std::isfinite(r->theta) || std::isnan(r->factor)) return MLA_ERR_INVALID_ARG;
+  if (r->factor > 1.0 && (!std::isfinite(r->factor) || r->original_max_position <= 0 || !(r->beta_slow > 0.0) ||
+                          !(r->beta_fast > r->beta_slow) || !std::isfinite(r->beta_fast)))
+    return MLA_ERR_INVALID_ARG;
+  HIP_TRY(rope_inv_freq(qk_rope, r->theta, r->factor, r->original_max_position, r->beta_fast, r->beta_slow,
+                        inv_freq, (hipStream_t)stream));
+  return MLA_OK;
+}
+
+double mla_rope_score_scale(const mla_rope* r, int32_t qk_nope, int32_t qk_rope) {
+  if (qk_nope < 0 || qk_rope <= 0) return 0.0;
+  double m = 1.0;
+  if (r && r->factor > 1.0) m = 0.1 * r->mscale_all_dim * std::log(r->factor) + 1.0;
+  return m * m / std::sqrt((double)qk_nope + (double)qk_rope);
+}
+
+mla_status mla_rope_tables(int32_t n, int32_t qk_rope, const int32_t* positions, int32_t pos_offset,
+                           const double* inv_freq, float* cos, float* sin, void* stream) {
+  if (n <= 0 || qk_rope <= 0 || qk_rope % 2 != 0 || !cos || !sin) return MLA_ERR_INVALID_ARG;
+  HIP_TRY(rope_tables(n, qk_rope, positions, pos_offset, inv_freq, cos, sin, (hipStream_t)stream));
+  return MLA_OK;
 }
 
 mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const void* x, int32_t T,

@@ -47,6 +47,17 @@ __device__ __forceinline__ float part_ld(const Partials& P, int64_t m, int64_t n
   return (s0 + s1) + (s2 + s3);
 }
 
+// ---- rotary tables and the layer-input RMSNorm ---------------------------------------
+// inv_freq [dr/2] fp64: theta^(-2i/dr), or its YaRN blend when factor > 1.
+hipError_t rope_inv_freq(int dr, double theta, double factor, int original_max_position, double beta_fast,
+                         double beta_slow, double* inv_freq, hipStream_t s);
+// cos/sin [n, dr/2] fp32 of (positions[t] (t if null) + pos_offset) * inv_freq[i]
+// (theta = 10000 frequencies if inv_freq is null).
+hipError_t rope_tables(int n, int dr, const int32_t* positions, int pos_offset, const double* inv_freq, float* cosT,
+                       float* sinT, hipStream_t s);
+// y [n, D] act = x * rsqrt(mean(x^2) + eps) * gamma per row.
+hipError_t input_norm(const Dims& d, const void* x, int n, const float* gamma, void* y, hipStream_t s);
+
 // ---- general (any shape) kernels: SIMT fp32 arithmetic ------------------------------
 // C[M, N] fp32 (row stride ldc) = A[M, K] (act, row stride lda) @ W[K, N]
 hipError_t gemm_simt(const Dims& d, const void* A, int64_t lda, const WeightView& W, float* C,

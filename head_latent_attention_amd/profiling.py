@@ -54,11 +54,16 @@ def _largest(d: str, counter: str) -> float:
     return max(vals.values())
 
 
-def source_hash(csrc: str) -> str:
+# files holding the device code of the decode-attention kernels the counters measure
+DECODE_ATTN_SOURCES = ("mla_decode_fast.hip", "mla_device.h")
+
+
+def source_hash(csrc: str, files=DECODE_ATTN_SOURCES) -> str:
+    """Short sha256 of the given kernel source files: a stored traffic figure is valid only
+    while it matches the sources."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 

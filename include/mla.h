@@ -7,6 +7,8 @@
  *   [MlaWeights] atlas docs, spark_model::layers::qwen3_attention, Struct MlaWeights
  *   [NKI-Decode] AWS Neuron NKI, "MLA Decode QKV Kernel API Reference"
  *   [NKI-CTE]    AWS Neuron NKI, "QKV CTE MLA Kernel API Reference"
+ *   [YaRN]       Peng et al., "YaRN: Efficient Context Window Extension of Large Language
+ *                Models" (2023), the method behind the [Mla] scale and [MlaWeights] yarn_inv_freq
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is DEVICE memory owned by the caller.  The library keeps
@@ -91,7 +93,46 @@ typedef struct {
   mla_weight wo;     /* [H*dv, D] output projection                                            */
   const float* q_norm_w;   /* [Lq]  fp32 RMSNorm gamma of the query latent; unused when Lq == 0 */
   const float* kv_norm_w;  /* [Lkv] fp32 RMSNorm gamma of the KV latent                         */
+  const float* input_norm_w;  /* [D] fp32 gamma of the layer's input RMSNorm, or NULL.  When given,
+                                 the projection entry points normalise each row of x first:
+                                 x * rsqrt(mean(x^2) + norm_eps) * input_norm_w ([NKI-Decode]
+                                 input_norm_w: the input norm folded into the hidden load)      */
 } mla_weights;
+
+/* Rotary-embedding frequencies ([MlaWeights] yarn_inv_freq / main_inv_freq; [Mla] scale).
+ * Pair i of the qk_rope rotating dims turns by position * inv_freq[i] radians. */
+typedef struct {
+  double theta;                  /* base of the plain frequencies theta^(-2i/dr), normally 10000       */
+  double factor;                 /* YaRN context-extension factor; <= 1 means plain RoPE                */
+  int32_t original_max_position; /* context length the plain frequencies were trained for (factor > 1) */
+  double beta_fast, beta_slow;   /* turn counts over that context bounding the blend (normally 32, 1)  */
+  double mscale_all_dim;         /* m of YaRN's magnitude 0.1 * m * ln(factor) + 1 (normally 1)         */
+} mla_rope;
+
+/* Inverse frequencies inv_freq [qk_rope/2] (fp64, device, out).  factor <= 1: theta^(-2i/dr).
+ * factor > 1, YaRN by parts ([YaRN] section 3.2): a pair whose wavelength 2*pi/f turns at least
+ * beta_fast times over original_max_position keeps f; one that turns at most beta_slow times
+ * gets f / factor; in between the share of f / factor grows linearly in the pair index from
+ * floor(index where the count is beta_fast) (at least 0) to ceil(index where it is beta_slow)
+ * (at most qk_rope - 1).  Requires theta > 1, qk_rope even; with factor > 1 also
+ * original_max_position > 0 and beta_fast > beta_slow > 0. */
+mla_status mla_rope_inv_freq(const mla_rope* rope, int32_t qk_rope, double* inv_freq, void* stream);
+
+/* The score scale 1/sqrt(qk_nope + qk_rope) times the square of YaRN's magnitude
+ * 0.1 * mscale_all_dim * ln(factor) + 1 (magnitude 1 when factor <= 1 or rope is NULL)
+ * ([Mla] scale field; [YaRN] section 3.4).  Host-only; returns 0 for non-positive dims. */
+double mla_rope_score_scale(const mla_rope* rope, int32_t qk_nope, int32_t qk_rope);
+
+/* cos/sin tables for the projection entry points: for token t < n and pair i < qk_rope/2,
+ *   angle = (positions[t] + pos_offset) * inv_freq[i],  cos[t][i] = cos(angle), sin[t][i] = sin(angle)
+ * with the angle, cos and sin evaluated in fp64 and stored as fp32.
+ *   positions  int32 [n] device, or NULL for positions 0..n-1 (e.g. context_lens with
+ *              pos_offset -1 gives each decode token's position).
+ *   inv_freq   fp64 [qk_rope/2] device (mla_rope_inv_freq), or NULL for theta = 10000.
+ *   cos, sin   fp32 [n, qk_rope/2] device out.
+ * n >= 1, qk_rope even. */
+mla_status mla_rope_tables(int32_t n, int32_t qk_rope, const int32_t* positions, int32_t pos_offset,
+                           const double* inv_freq, float* cos, float* sin, void* stream);
 
 /* Identifiers of the entry points, for mla_workspace_size. */
 enum {

@@ -77,3 +77,31 @@ def test_invalid_arguments_fail_before_launch():
     assert lib.mla_qkv_prefill(ctypes.byref(cfg), ctypes.byref(W), 1, 4, 1, 1, 1, 1, 1, None, None, 0, 1,
                                1 << 20, None) == -1
     assert lib.mla_decode_qkv_and_scatter(None, ctypes.byref(W), 1, 4, 1, 1, 1, 1, 1, 1, 1, 1 << 20, None) == -1
+
+
+def test_rope_entry_points_validate_before_launch():
+    lib = mla.load()
+    r = mla.rope(factor=40.0)
+    assert lib.mla_rope_inv_freq(None, 64, 1, None) == -1
+    assert lib.mla_rope_inv_freq(ctypes.byref(r), 63, 1, None) == -1
+    assert lib.mla_rope_inv_freq(ctypes.byref(r), 64, None, None) == -1
+    assert lib.mla_rope_inv_freq(ctypes.byref(mla.rope(theta=1.0)), 64, 1, None) == -1
+    assert lib.mla_rope_inv_freq(ctypes.byref(mla.rope(factor=4.0, original_max_position=0)), 64, 1, None) == -1
+    assert lib.mla_rope_inv_freq(ctypes.byref(mla.rope(factor=4.0, beta_fast=1.0, beta_slow=2.0)), 64, 1, None) == -1
+    assert lib.mla_rope_tables(0, 64, None, 0, None, 1, 1, None) == -1
+    assert lib.mla_rope_tables(4, 7, None, 0, None, 1, 1, None) == -1
+    assert lib.mla_rope_tables(4, 64, None, 0, None, None, 1, None) == -1
+
+
+def test_rope_score_scale_host_function():
+    """Host-side score scale against the oracle's (1/sqrt(dqk) times YaRN's magnitude squared)."""
+    from oracle import mla_oracle as O
+    lib = mla.load()
+    assert lib.mla_rope_score_scale(None, 128, 64) == pytest.approx(O.softmax_scale(128, 64), rel=1e-15)
+    for f, m in [(40.0, 1.0), (4.0, 0.707), (1.0, 1.0), (0.5, 1.0)]:
+        r = mla.rope(factor=f, mscale_all_dim=m)
+        assert lib.mla_rope_score_scale(ctypes.byref(r), 128, 64) == pytest.approx(O.softmax_scale(128, 64, f, m),
+                                                                                   rel=1e-14)
+    assert lib.mla_rope_score_scale(None, 128, 0) == 0.0
+    cfg = mla.config(7168, 128, 1536, 512, 128, 64, 128, rope=mla.rope(factor=40.0))
+    assert cfg.softmax_scale == pytest.approx(O.softmax_scale(128, 64, 40.0, 1.0), rel=1e-7)
