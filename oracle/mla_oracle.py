@@ -48,7 +48,7 @@ import numpy as np
 
 __all__ = [
     "e4m3fn_value", "decode_tensor", "rms_norm", "rope_angles", "rope_interleaved",
-    "softmax_scale", "yarn_inv_freq", "yarn_mscale", "input_norm", "project", "project_rows", "expand_kv", "attention", "mla_prefill", "mla_decode", "decode_attention",
+    "softmax_scale", "yarn_inv_freq", "yarn_mscale", "input_norm", "project", "project_rows", "expand_kv", "attention", "mla_prefill", "mla_decode", "decode_attention", "chunk_attention",
     "place_rows", "cache_read_dense", "decode_weights", "dims_of",
 ]
 
@@ -311,6 +311,28 @@ def decode_attention(W: Dict[str, np.ndarray], q: np.ndarray, seqs: Sequence[np.
             sub = _head_slice(W, dims, hs)
             K, V = expand_kv(sub, rows, dict(dims, n_heads=hs.stop - hs.start))
             o[b, hs] = attention(q[b:b + 1, hs], K, V, dims["softmax_scale"], np.array([len(rows) - 1]))[0]
+    return o
+
+
+def chunk_attention(W: Dict[str, np.ndarray], q: np.ndarray, prefix_rows: np.ndarray, chunk_rows: np.ndarray,
+                    dims: dict, head_chunk: int = 16) -> np.ndarray:
+    """Causal attention of a prefill chunk over an existing prefix of one sequence.
+
+    q [T, H, dqk] are the chunk's queries at positions P..P+T-1 (P = len(prefix_rows),
+    q_pe roped there); prefix_rows [P, R] and chunk_rows [T, R] are the sequence's latent
+    rows.  Query t sees rows 0..P+t.  Keys and values of every row are expanded per head
+    through wkv_b ([NKI-CTE] KV path stage 2 and final assembly), as in the whole-prompt
+    prefill ([NeMo-MLA] forward, causal mask).  Returns o [T, H, dv]."""
+    H, dv = dims["n_heads"], dims["v_dim"]
+    rows = np.concatenate([np.asarray(prefix_rows, np.float64).reshape(-1, chunk_rows.shape[1]),
+                           np.asarray(chunk_rows, np.float64)], axis=0)
+    P, T = rows.shape[0] - chunk_rows.shape[0], q.shape[0]
+    o = np.zeros((T, H, dv))
+    for h0 in range(0, H, head_chunk):
+        hs = slice(h0, min(H, h0 + head_chunk))
+        sub = _head_slice(W, dims, hs)
+        K, V = expand_kv(sub, rows, dict(dims, n_heads=hs.stop - hs.start))
+        o[:, hs] = attention(q[:, hs], K, V, dims["softmax_scale"], P + np.arange(T))
     return o
 
 

@@ -149,3 +149,17 @@ def test_fp8_weights_decode_exactly():
     grid = np.array([O.e4m3fn_value(c) for c in range(256)])
     assert np.isin(dec / full, grid).all()
     assert set(np.log2(t.scale).ravel().astype(int)) <= {-4, -3, -2, -1, 0}
+
+
+@pytest.mark.parametrize("P", [0, 5, 9])
+def test_chunk_attention_equals_whole_prefill(P):
+    """Attention of tokens P..N-1 over the prefix 0..P-1 equals the same tokens' output of one
+    prefill of all N tokens (scalar loops pin that prefill); a one-token chunk equals decode."""
+    W, d = _tiny_weights(31, D=7, H=2, Lq=5, Lkv=6, dn=3, dr=4, dv=2, input_norm=True)
+    x = synth.rng(32, "x").standard_normal((12, 7))
+    ref = _layer_loops(W, x, d)
+    got = O.chunk_attention(W, ref["q"][P:], ref["rows"][:P], ref["rows"][P:], d, head_chunk=1)
+    np.testing.assert_allclose(got, ref["o"][P:], rtol=1e-11, atol=1e-12)
+    one = O.chunk_attention(W, ref["q"][11:12], ref["rows"][:11], ref["rows"][11:12], d)
+    dec = O.decode_attention(W, ref["q"][11:12], [ref["rows"][:12]], d)
+    np.testing.assert_allclose(one, dec, rtol=1e-13, atol=1e-14)
