@@ -195,6 +195,71 @@ def run_prefill(w, reps):
                 wall_ms=wall * 1e3, flops=f_qkv + f_attn + f_out)
 
 
+def run_chunked(w, prefix, T, reps):
+    """Chunked prefill: T new tokens after `prefix` cached rows of one sequence (front end
+    without the K/V expansion, absorbed attention over the paged cache, output projection)."""
+    import torch
+    import synth
+    from synth import torch_io
+    import head_latent_attention_amd as mla
+    s = w.shape
+    host = synth.make_weights(w)
+    dw = mla.Weights({k: torch_io.to_device(v) for k, v in host.items()},
+                     {k: torch_io.scale_to_device(v) for k, v in host.items() if v.scale is not None})
+    cfg = mla.config(s.hidden, s.n_heads, s.q_lora_rank, s.kv_lora_rank, s.qk_nope, s.qk_rope, s.v_dim,
+                     act=s.act, weight=s.weight, block_size=s.block_size)
+    N = prefix + T
+    pg = synth.make_paging(w.number, np.array([N], np.int32), s.block_size, name="chunk.blocks")
+    cache = torch.empty((pg.n_blocks, 1, s.block_size, s.row), dtype=torch.bfloat16, device="cuda")
+    rows = torch_io.to_device(synth.history_rows(w, 0, prefix))
+    flat_slots = synth.slots_for(pg.block_table[0], np.arange(prefix), s.block_size).astype(np.int64)
+    cache.view(-1, s.row)[torch.from_numpy(flat_slots).cuda()] = rows
+    table = torch.from_numpy(pg.block_table[0].copy()).cuda()
+    x = torch_io.to_device(synth.make_x(w, T, "x.chunk"))
+    pos = np.arange(prefix, N)
+    cos, sin = mla.rope_cos_sin(pos, s.qk_rope)
+    slots = torch.from_numpy(synth.slots_for(pg.block_table[0], pos, s.block_size)).cuda()
+    q = torch.empty((T, s.n_heads, s.qk_head), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((T, s.n_heads, s.v_dim), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, s.hidden), dtype=torch.bfloat16, device="cuda")
+    ws_q = mla.workspace(cfg, 0, T)
+    ws_a = mla.workspace(cfg, 5, T, pg.block_table.shape[1] * s.block_size)
+    ws_o = mla.workspace(cfg, 4, T)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def once(rec):
+        if rec:
+            ev[0].record()
+        mla.mla_qkv_prefill(cfg, dw, x, cos, sin, q, None, None, cache, slots, ws=ws_q)
+        if rec:
+            ev[1].record()
+        mla.mla_prefill_attn_paged(cfg, dw, q, cache, table, prefix, o, ws=ws_a)
+        if rec:
+            ev[2].record()
+        mla.mla_out_proj(cfg, dw, o, y, ws=ws_o)
+        if rec:
+            ev[3].record()
+
+    once(False)
+    torch.cuda.synchronize()
+    tq = ta = to = 0.0
+    for _ in range(reps):
+        once(True)
+        torch.cuda.synchronize()
+        tq += ev[0].elapsed_time(ev[1])
+        ta += ev[1].elapsed_time(ev[2])
+        to += ev[2].elapsed_time(ev[3])
+    tq, ta, to = tq / reps, ta / reps, to / reps
+    D, H, Lq, Lkv, dn, dr, dv = s.hidden, s.n_heads, s.q_lora_rank, s.kv_lora_rank, s.qk_nope, s.qk_rope, s.v_dim
+    seen = T * prefix + T * (T + 1) // 2          # (query, row) pairs
+    f_qkv = 2 * T * D * (Lq + Lkv + dr) + 2 * T * Lq * H * (dn + dr)
+    f_attn = 2 * seen * H * (Lkv + dr + Lkv) + 2 * T * H * dn * Lkv + 2 * T * H * Lkv * dv
+    f_out = 2 * T * H * dv * D
+    return dict(ms=tq + ta + to, ms_qkv=tq, ms_attn=ta, ms_out=to, pairs=seen,
+                tflops=(f_qkv + f_attn + f_out) / ((tq + ta + to) * 1e-3) / 1e12,
+                attn_tflops=f_attn / (ta * 1e-3) / 1e12, flops=f_qkv + f_attn + f_out)
+
+
 def cpu_baseline(w, S, budget_s=12.0):
     """The float64 oracle on a bounded sample of the same decode batch."""
     from threadpoolctl import threadpool_info
@@ -230,6 +295,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -332,6 +398,16 @@ def main():
                           "ms_out_proj": round(pf["ms_out"], 3), "attn_TFLOPs": round(pf["attn_tflops"], 2),
                           "frac_bf16_peak": round(pf["tflops"] / BF16_PEAK_TFLOPS, 4),
                           "causal_counted_flops": pf["flops"]}
+    if not args.no_chunk:
+        prefix, T = 7168, 1024
+        log(f"[bench] V3 chunked prefill, {T} tokens after {prefix}")
+        ch = run_chunked(synth.WORKLOADS[4], prefix, T, args.prefill_reps)
+        out["chunked_prefill"] = {"workload": f"v3-chunk-{T}-after-{prefix}", "ms": round(ch["ms"], 3),
+                                  "ms_qkv": round(ch["ms_qkv"], 3), "ms_attn": round(ch["ms_attn"], 3),
+                                  "ms_out_proj": round(ch["ms_out"], 3), "TFLOPs": round(ch["tflops"], 2),
+                                  "attn_TFLOPs": round(ch["attn_tflops"], 2),
+                                  "frac_bf16_peak": round(ch["tflops"] / BF16_PEAK_TFLOPS, 4),
+                                  "absorbed_counted_flops": ch["flops"], "query_row_pairs": ch["pairs"]}
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(w, S)

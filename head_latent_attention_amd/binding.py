@@ -19,12 +19,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmla.so")
 
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
-FN_QKV_PREFILL, FN_PREFILL_ATTN, FN_DECODE_QKV, FN_DECODE_ATTN, FN_OUT_PROJ = range(5)
+FN_QKV_PREFILL, FN_PREFILL_ATTN, FN_DECODE_QKV, FN_DECODE_ATTN, FN_OUT_PROJ, FN_PREFILL_ATTN_PAGED = range(6)
 _DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 SYMBOLS = ("mla_qkv_prefill", "mla_prefill_attn", "mla_decode_qkv_and_scatter", "mla_decode_attn_absorbed",
-           "mla_out_proj", "mla_rope_inv_freq", "mla_rope_tables", "mla_workspace_size", "mla_status_string",
-           "mla_rope_score_scale")
-_STATUS_FNS = SYMBOLS[:7]
+           "mla_out_proj", "mla_prefill_attn_paged", "mla_rope_inv_freq", "mla_rope_tables", "mla_workspace_size",
+           "mla_status_string", "mla_rope_score_scale")
+_STATUS_FNS = SYMBOLS[:8]
 
 
 class MlaError(RuntimeError):
@@ -75,6 +75,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_qkv_and_scatter.argtypes = [C, W, P, I32, P, P, P, I64, P, P, P, SZ, P]
     lib.mla_decode_attn_absorbed.argtypes = [C, W, P, I32, P, I64, P, I32, P, P, P, SZ, P]
     lib.mla_out_proj.argtypes = [C, W, P, I32, P, P, SZ, P]
+    lib.mla_prefill_attn_paged.argtypes = [C, W, P, I32, P, I64, P, I32, I32, P, P, SZ, P]
     lib.mla_rope_inv_freq.argtypes = [POINTER(MlaRope), I32, P, P]
     lib.mla_rope_tables.argtypes = [I32, I32, P, I32, P, P, P, P]
     lib.mla_rope_score_scale.argtypes = [POINTER(MlaRope), I32, I32]
@@ -185,8 +186,9 @@ def rope_cos_sin(positions, rope_dim: int, theta: float = 10000.0, device="cuda"
     return mla_rope_tables(pos, pos.numel(), rope_dim, inv_freq)
 
 
-def mla_qkv_prefill(cfg, w: Weights, x, cos, sin, q, k, v, kv_cache=None, slot_mapping=None, ws=None,
+def mla_qkv_prefill(cfg, w: Weights, x, cos, sin, q, k=None, v=None, kv_cache=None, slot_mapping=None, ws=None,
                     stream=None):
+    """k = v = None skips the per-head K/V expansion (a chunk attended on the latent cache)."""
     T = x.shape[0]
     ws, nb = _ws(ws, cfg, FN_QKV_PREFILL, T, device=x.device)
     n_blocks = kv_cache.shape[0] if kv_cache is not None else 0
@@ -216,6 +218,16 @@ def mla_decode_attn_absorbed(cfg, w: Weights, q, kv_cache, block_table, context_
     _check(load().mla_decode_attn_absorbed(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(q), B, _ptr(kv_cache),
                                            kv_cache.shape[0], _ptr(block_table), max_blocks, _ptr(context_lens),
                                            _ptr(o), _ptr(ws), nb, _stream(stream)))
+
+
+def mla_prefill_attn_paged(cfg, w: Weights, q, kv_cache, block_table, prefix_len: int, o, ws=None, stream=None):
+    """Chunk of T = q.shape[0] tokens at positions prefix_len.. over one sequence's cache
+    (block_table int32 [max_blocks])."""
+    T, max_blocks = q.shape[0], block_table.numel()
+    ws, nb = _ws(ws, cfg, FN_PREFILL_ATTN_PAGED, T, max_blocks * cfg.block_size, device=q.device)
+    _check(load().mla_prefill_attn_paged(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(q), T, _ptr(kv_cache),
+                                         kv_cache.shape[0], _ptr(block_table), max_blocks, int(prefix_len), _ptr(o),
+                                         _ptr(ws), nb, _stream(stream)))
 
 
 def mla_out_proj(cfg, w: Weights, o, y, ws=None, stream=None):

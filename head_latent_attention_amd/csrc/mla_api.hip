@@ -151,6 +151,17 @@ size_t decode_attn_ws(const Dims& d, int B, int max_context, void* base, DecodeA
   return c.used;
 }
 
+// Chunked prefill over a paged prefix: the decode workspace for T queries plus their
+// context lengths.
+size_t chunk_attn_ws(const Dims& d, int T, int max_context, void* base, DecodeAttnWs* out, int32_t** ctx) {
+  Carver c(base);
+  const size_t dec = decode_attn_ws(d, T, max_context, base, out);
+  c.used = align_up(dec);
+  int32_t* p = c.take<int32_t>((size_t)T);
+  if (ctx) *ctx = p;
+  return c.used;
+}
+
 size_t out_proj_ws(const Dims& d, int M, void* base, float** Y) {
   Carver c(base);
   const bool fused = fast_gemm_fusable(d, M, d.D, d.H * d.dv, d.D, GemmEpilogue::STORE);
@@ -259,6 +270,9 @@ size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t 
       if (max_context <= 0) return 0;
       return decode_attn_ws(d, n, max_context, nullptr, nullptr);
     case MLA_FN_OUT_PROJ: return out_proj_ws(d, n, nullptr, nullptr);
+    case MLA_FN_PREFILL_ATTN_PAGED:
+      if (max_context <= 0) return 0;
+      return chunk_attn_ws(d, n, max_context, nullptr, nullptr, nullptr);
   }
   return 0;
 }
@@ -295,7 +309,8 @@ mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const vo
   Dims d;
   mla_status st = check_cfg(cfg, &d);
   if (st != MLA_OK) return st;
-  if (T <= 0 || !x || !cos || !sin || !q || !k || !v || !check_weights_front(d, w) || !check_weight(d, w->wkv_b))
+  if (T <= 0 || !x || !cos || !sin || !q || ((k == nullptr) != (v == nullptr)) || !check_weights_front(d, w) ||
+      (k && !check_weight(d, w->wkv_b)))
     return MLA_ERR_INVALID_ARG;
   if ((kv_cache == nullptr) != (slot_mapping == nullptr)) return MLA_ERR_INVALID_ARG;
   if (kv_cache && n_blocks <= 0) return MLA_ERR_INVALID_ARG;
@@ -304,7 +319,7 @@ mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const vo
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   st = front_end(d, w, x, T, cos, sin, q, k, kv_cache, n_blocks, slot_mapping, L, s);
-  if (st != MLA_OK) return st;
+  if (st != MLA_OK || !k) return st;
   const int NKV = d.H * (d.dn + d.dv);
   const WeightView wkvb = view(d, w->wkv_b, NKV);
   Partials PKV;
@@ -371,14 +386,48 @@ mla_status mla_decode_attn_absorbed(const mla_config* cfg, const mla_weights* w,
   hipStream_t s = (hipStream_t)stream;
   const WeightView wkv_b = view(d, w->wkv_b, (int64_t)d.H * (d.dn + d.dv));
   if (fast_decode_supported(d)) {
-    HIP_TRY(fast_decode_attn(d, q, B, kv_cache, n_blocks, block_table, max_blocks, context_lens, wkv_b, o,
-                             L.fast, s));
+    HIP_TRY(fast_decode_attn(d, q, B, kv_cache, n_blocks, block_table, max_blocks, max_blocks, context_lens,
+                             wkv_b, o, L.fast, s));
     return MLA_OK;
   }
   HIP_TRY(fold_simt(d, q, B, wkv_b, L.Qabs, s));
-  HIP_TRY(decode_attn_simt(d, L.Qabs, B, kv_cache, n_blocks, block_table, max_blocks, context_lens, L.nsplit,
-                           L.chunk, L.part_o, L.part_ml, s));
+  HIP_TRY(decode_attn_simt(d, L.Qabs, B, kv_cache, n_blocks, block_table, max_blocks, max_blocks, context_lens,
+                           L.nsplit, L.chunk, L.part_o, L.part_ml, s));
   HIP_TRY(combine_simt(d, B, L.nsplit, L.part_o, L.part_ml, wkv_b, o, s));
+  return MLA_OK;
+}
+
+mla_status mla_prefill_attn_paged(const mla_config* cfg, const mla_weights* w, const void* q, int32_t T,
+                                  const void* kv_cache, int64_t n_blocks, const int32_t* block_table,
+                                  int32_t max_blocks, int32_t prefix_len, void* o, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  Dims d;
+  mla_status st = check_cfg(cfg, &d);
+  if (st != MLA_OK) return st;
+  if (T <= 0 || prefix_len < 0 || !w || !q || !kv_cache || n_blocks <= 0 || !block_table || max_blocks <= 0 ||
+      !o || !check_weight(d, w->wkv_b))
+    return MLA_ERR_INVALID_ARG;
+  const int64_t max_ctx64 = (int64_t)max_blocks * d.bs;
+  if ((int64_t)prefix_len + T > max_ctx64) return MLA_ERR_INVALID_ARG;
+  if (max_ctx64 > (1 << 30)) return MLA_ERR_UNSUPPORTED;
+  const int max_ctx = (int)max_ctx64;
+  DecodeAttnWs L;
+  int32_t* ctx = nullptr;
+  const size_t need = chunk_attn_ws(d, T, max_ctx, ws, &L, &ctx);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const WeightView wkv_b = view(d, w->wkv_b, (int64_t)d.H * (d.dn + d.dv));
+  HIP_TRY(chunk_ctx(T, prefix_len, ctx, s));
+  // every query of the chunk is a decode query of the same sequence at its own position:
+  // one block-table row shared by all (stride 0) and context length prefix + t + 1
+  if (fast_decode_supported(d)) {
+    HIP_TRY(fast_decode_attn(d, q, T, kv_cache, n_blocks, block_table, max_blocks, 0, ctx, wkv_b, o, L.fast, s));
+    return MLA_OK;
+  }
+  HIP_TRY(fold_simt(d, q, T, wkv_b, L.Qabs, s));
+  HIP_TRY(decode_attn_simt(d, L.Qabs, T, kv_cache, n_blocks, block_table, max_blocks, 0, ctx, L.nsplit, L.chunk,
+                           L.part_o, L.part_ml, s));
+  HIP_TRY(combine_simt(d, T, L.nsplit, L.part_o, L.part_ml, wkv_b, o, s));
   return MLA_OK;
 }
 

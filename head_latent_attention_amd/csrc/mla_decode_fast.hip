@@ -249,6 +249,7 @@ struct AttnArgs {
   int bs;
   const int32_t* bt;
   int max_blocks;
+  int64_t bt_stride;  // elements between the table rows of consecutive sequences (0: one shared row)
   const int32_t* ctx;
   const int32_t* P;
   const int32_t* info;  // per share: first sequence, number of sub-tiles
@@ -268,7 +269,7 @@ __device__ __forceinline__ T sload(const T* p) {
 __device__ __forceinline__ int sub_tile_block(const AttnArgs& A, int b, int tok0, int tok_hi) {
   if (tok0 >= tok_hi) return -1;
   const int lb = tok0 / A.bs;
-  return lb < A.max_blocks ? sload(A.bt + (size_t)b * A.max_blocks + lb) : -1;
+  return lb < A.max_blocks ? sload(A.bt + (size_t)b * A.bt_stride + lb) : -1;
 }
 
 // Direct global->LDS copies of one 32-token sub-tile of block `blk`.  The block size is a
@@ -694,7 +695,7 @@ bool fast_decode_supported(const Dims& d) {
 size_t fast_decode_ws_bytes(const Dims& d, int B, int) { return layout(B, nullptr).bytes; }
 
 hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cache, int64_t n_blocks,
-                            const int32_t* block_table, int max_blocks, const int32_t* ctx,
+                            const int32_t* block_table, int max_blocks, int64_t bt_stride, const int32_t* ctx,
                             const WeightView& wkv_b, void* o, const FastDecodeWs& ws, hipStream_t s) {
   const DecodeLayout L = layout(B, ws.base);
   dim3 fgrid(kH + 1, kLkv / 128, (B + 63) / 64);
@@ -710,6 +711,7 @@ hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cac
   A.bs = d.bs;
   A.bt = block_table;
   A.max_blocks = max_blocks;
+  A.bt_stride = bt_stride;
   A.ctx = ctx;
   A.P = L.P;
   A.info = L.info;

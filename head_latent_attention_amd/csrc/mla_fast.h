@@ -39,8 +39,9 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
 // Absorbed decode: fold, split-context attention over the paged cache, combine with W_UV.
 bool fast_decode_supported(const Dims& d);
 size_t fast_decode_ws_bytes(const Dims& d, int B, int max_context);
+// Query b reads its block ids from block_table + b * bt_stride (0: one shared table).
 hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cache, int64_t n_blocks,
-                            const int32_t* block_table, int max_blocks, const int32_t* ctx,
+                            const int32_t* block_table, int max_blocks, int64_t bt_stride, const int32_t* ctx,
                             const WeightView& wkv_b, void* o, const FastDecodeWs& ws, hipStream_t s);
 
 // Causal prefill flash attention.

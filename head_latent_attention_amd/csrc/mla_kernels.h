@@ -87,11 +87,14 @@ hipError_t cast_rows(const Dims& d, const Partials& Y, int M, int N, void* y, hi
 hipError_t fold_simt(const Dims& d, const void* q, int B, const WeightView& wkv_b, float* Qabs,
                      hipStream_t s);
 // Split-context attention over the paged cache: partial (o_lat[Lkv], m, l) per
-// (b, h, split) with split s covering tokens [s*chunk, (s+1)*chunk).
+// (b, h, split) with split s covering tokens [s*chunk, (s+1)*chunk).  Query b reads
+// its block ids from block_table + b * bt_stride (bt_stride 0: one table for all).
 hipError_t decode_attn_simt(const Dims& d, const float* Qabs, int B, const void* cache,
                             int64_t n_blocks, const int32_t* block_table, int max_blocks,
-                            const int32_t* ctx, int nsplit, int chunk, float* part_o,
+                            int64_t bt_stride, const int32_t* ctx, int nsplit, int chunk, float* part_o,
                             float* part_ml, hipStream_t s);
+// ctx[t] = prefix + t + 1 for t < T (the rows query t of a prefill chunk sees).
+hipError_t chunk_ctx(int T, int prefix, int32_t* ctx, hipStream_t s);
 // Log-sum-exp merge of the splits, then o[b, h] = o_lat @ W_UV[h] (act).
 hipError_t combine_simt(const Dims& d, int B, int nsplit, const float* part_o, const float* part_ml,
                         const WeightView& wkv_b, void* o, hipStream_t s);

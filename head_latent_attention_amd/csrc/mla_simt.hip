@@ -295,7 +295,7 @@ hipError_t fold_simt(const Dims& d, const void* q, int B, const WeightView& W, f
 template <typename T>
 __global__ __launch_bounds__(256) void decode_attn_simt_kernel(
     const float* __restrict__ Qabs, int H, int Lkv, int dr, float scale, const T* __restrict__ cache,
-    int64_t n_blocks, int bs, const int32_t* __restrict__ block_table, int max_blocks,
+    int64_t n_blocks, int bs, const int32_t* __restrict__ block_table, int max_blocks, int64_t bt_stride,
     const int32_t* __restrict__ ctx_lens, int nsplit, int chunk, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   extern __shared__ float sh[];
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256) void decode_attn_simt_kernel(
     float sc = -INFINITY;
     int64_t off = -1;
     if (t < t1 && t / bs < max_blocks) {
-      const int blk = block_table[(size_t)b * max_blocks + t / bs];
+      const int blk = block_table[(size_t)b * bt_stride + t / bs];
       if (blk >= 0 && blk < n_blocks) {
         off = ((int64_t)blk * bs + (t % bs)) * R;
         float acc = 0.f;
@@ -360,18 +360,18 @@ __global__ __launch_bounds__(256) void decode_attn_simt_kernel(
 }
 
 hipError_t decode_attn_simt(const Dims& d, const float* Qabs, int B, const void* cache, int64_t n_blocks,
-                            const int32_t* block_table, int max_blocks, const int32_t* ctx, int nsplit,
-                            int chunk, float* part_o, float* part_ml, hipStream_t s) {
+                            const int32_t* block_table, int max_blocks, int64_t bt_stride, const int32_t* ctx,
+                            int nsplit, int chunk, float* part_o, float* part_ml, hipStream_t s) {
   dim3 grid(B * d.H, nsplit);
   const size_t sh = sizeof(float) * (d.R() + 256);
   if (d.act == 0)
     decode_attn_simt_kernel<float><<<grid, 256, sh, s>>>(Qabs, d.H, d.Lkv, d.dr, d.scale, (const float*)cache,
-                                                          n_blocks, d.bs, block_table, max_blocks, ctx, nsplit,
-                                                          chunk, part_o, part_ml);
+                                                          n_blocks, d.bs, block_table, max_blocks, bt_stride, ctx,
+                                                          nsplit, chunk, part_o, part_ml);
   else
     decode_attn_simt_kernel<bf16_t><<<grid, 256, sh, s>>>(Qabs, d.H, d.Lkv, d.dr, d.scale, (const bf16_t*)cache,
-                                                           n_blocks, d.bs, block_table, max_blocks, ctx, nsplit,
-                                                           chunk, part_o, part_ml);
+                                                           n_blocks, d.bs, block_table, max_blocks, bt_stride, ctx,
+                                                           nsplit, chunk, part_o, part_ml);
   return hipGetLastError();
 }
 
@@ -518,6 +518,18 @@ hipError_t prefill_attn_simt(const Dims& d, const void* q, const void* k, const 
   else
     prefill_attn_simt_kernel<bf16_t><<<grid, 256, sh, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
                                                             T, d.H, dqk, d.dv, d.scale, (bf16_t*)o);
+  return hipGetLastError();
+}
+
+// Context length of each query of a prefill chunk: query t at position prefix + t sees
+// prefix + t + 1 rows.
+__global__ void chunk_ctx_kernel(int T, int prefix, int32_t* __restrict__ ctx) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < T) ctx[t] = prefix + t + 1;
+}
+
+hipError_t chunk_ctx(int T, int prefix, int32_t* ctx, hipStream_t s) {
+  chunk_ctx_kernel<<<(T + 255) / 256, 256, 0, s>>>(T, prefix, ctx);
   return hipGetLastError();
 }
 

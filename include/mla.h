@@ -140,7 +140,8 @@ enum {
   MLA_FN_PREFILL_ATTN = 1,
   MLA_FN_DECODE_QKV = 2,
   MLA_FN_DECODE_ATTN = 3,
-  MLA_FN_OUT_PROJ = 4
+  MLA_FN_OUT_PROJ = 4,
+  MLA_FN_PREFILL_ATTN_PAGED = 5
 };
 
 /* Context-encoding projections for T tokens at positions 0..T-1 of one sequence
@@ -156,6 +157,10 @@ enum {
  *         is written to flat row slot_mapping[t] (block slot/bs, offset slot%bs); -1 skips.
  *         kv_cache and slot_mapping may both be NULL (no cache write).
  *   slot_mapping  int32 [T] or NULL.
+ * k and v may both be NULL: the per-head expansion through wkv_b is skipped (wkv_b may then
+ * be unset), as for a chunk whose attention runs on the latent cache (mla_prefill_attn_paged).
+ * The cos/sin rows give the tokens' positions, so a chunk later in a sequence passes the
+ * tables of its own positions.
  * T >= 1. */
 mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const void* x, int32_t T,
                            const float* cos, const float* sin, void* q, void* k, void* v,
@@ -203,13 +208,32 @@ mla_status mla_decode_attn_absorbed(const mla_config* cfg, const mla_weights* w,
                                     const int32_t* context_lens, void* o, void* ws,
                                     size_t ws_bytes, void* stream);
 
+/* Chunked prefill over a paged prefix: causal attention of T new tokens of one sequence over
+ * that sequence's latent cache, in the absorbed form ([MlaWeights] w_uk_block_diag /
+ * w_uv_block_diag: query absorption and value extraction used for prefill too; [NKI-Decode]
+ * paged kv_cache).  Query t sits at position prefix_len + t and attends to rows
+ * 0 .. prefix_len + t, read through block_table; each query is computed exactly as
+ * mla_decode_attn_absorbed computes a decode query with context prefix_len + t + 1.
+ *   q        [T, H, dqk] act: per head [q_nope | RoPE(q_pe)] at the tokens' positions
+ *            (mla_qkv_prefill with the tables of positions prefix_len ..).
+ *   kv_cache [n_blocks, 1, bs, R] act (read only); rows prefix_len .. prefix_len + T - 1 must
+ *            already hold the chunk's own rows (mla_qkv_prefill with slot_mapping).
+ *   block_table  int32 [max_blocks]: the sequence's blocks; prefix_len + T <= max_blocks * bs.
+ *   o        [T, H, dv] act out.
+ * T >= 1, prefix_len >= 0.  Workspace: mla_workspace_size(cfg, MLA_FN_PREFILL_ATTN_PAGED, T,
+ * max_blocks * bs). */
+mla_status mla_prefill_attn_paged(const mla_config* cfg, const mla_weights* w, const void* q, int32_t T,
+                                  const void* kv_cache, int64_t n_blocks, const int32_t* block_table,
+                                  int32_t max_blocks, int32_t prefix_len, void* o, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Output projection y = o @ wo ([NeMo-MLA] o_proj; [MlaWeights] wo).
  *   o [M, H*dv] act; y [M, D] act out.  M >= 1. */
 mla_status mla_out_proj(const mla_config* cfg, const mla_weights* w, const void* o, int32_t M,
                         void* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes entry point `fn` (MLA_FN_*) needs for n rows (T or B or M) and,
- * for MLA_FN_DECODE_ATTN, contexts up to max_context tokens.  Returns 0 for an
+ * for MLA_FN_DECODE_ATTN and MLA_FN_PREFILL_ATTN_PAGED, contexts up to max_context tokens.  Returns 0 for an
  * invalid config or fn.  The value depends only on the arguments. */
 size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t max_context);
 

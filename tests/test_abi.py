@@ -105,3 +105,23 @@ def test_rope_score_scale_host_function():
     assert lib.mla_rope_score_scale(None, 128, 0) == 0.0
     cfg = mla.config(7168, 128, 1536, 512, 128, 64, 128, rope=mla.rope(factor=40.0))
     assert cfg.softmax_scale == pytest.approx(O.softmax_scale(128, 64, 40.0, 1.0), rel=1e-7)
+
+
+def test_prefill_attn_paged_validation():
+    lib = mla.load()
+    cfg = _cfg()
+    W = B.MlaWeights()
+    W.wkv_b = B.MlaWeight(1, None)
+
+    def call(T=4, prefix=0, max_blocks=2, q=1, bt=1, ws_bytes=1 << 30, w=W):
+        return lib.mla_prefill_attn_paged(ctypes.byref(cfg), ctypes.byref(w), q, T, 1, 4, bt, max_blocks, prefix, 1,
+                                          1, ws_bytes, None)
+    assert call(T=0) == -1
+    assert call(prefix=-1) == -1
+    assert call(q=None) == -1
+    assert call(bt=None) == -1
+    assert call(prefix=30, T=3) == -1            # prefix + T beyond max_blocks * bs = 32
+    assert call(w=B.MlaWeights()) == -1          # wkv_b missing
+    assert call(ws_bytes=8) == -3
+    assert B.workspace_size(cfg, B.FN_PREFILL_ATTN_PAGED, 8, 64) > B.workspace_size(cfg, B.FN_DECODE_ATTN, 8, 64)
+    assert B.workspace_size(cfg, B.FN_PREFILL_ATTN_PAGED, 8, 0) == 0
