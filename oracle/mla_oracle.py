@@ -34,6 +34,11 @@ Readings where the pages are silent (each listed in the design notes too):
     0.1*m*ln(factor)+1 enters the score scale squared and leaves cos/sin unscaled.
   * The optional layer-input RMSNorm (input_norm_w) uses the same formula and eps
     as the two latent norms and is applied to x before the stage-1 projection.
+  * fp8 activation quantisation (when dims["act_quant"] is set): every activation
+    entering a projection (x, the normed q latent, the normed kv latent, the
+    attention output) is quantised per token and per group of 128 columns to E4M3FN
+    codes times a power-of-two scale 2^e, e the smallest integer with
+    max|group| <= 448 * 2^e, codes rounded to nearest, ties to even.
 
 Parity pins: every function here is checked in tests/test_oracle_*.py against
 closed forms, textbook special cases, torch's CPU float8 decoding, or
@@ -47,9 +52,9 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "e4m3fn_value", "decode_tensor", "rms_norm", "rope_angles", "rope_interleaved",
+    "e4m3fn_value", "e4m3fn_round", "quantize_mx_fp8", "decode_tensor", "rms_norm", "rope_angles", "rope_interleaved",
     "softmax_scale", "yarn_inv_freq", "yarn_mscale", "input_norm", "project", "project_rows", "expand_kv", "attention", "mla_prefill", "mla_decode", "decode_attention", "chunk_attention",
-    "place_rows", "cache_read_dense", "decode_weights", "dims_of",
+    "out_proj", "place_rows", "cache_read_dense", "decode_weights", "dims_of",
 ]
 
 
@@ -71,6 +76,62 @@ def e4m3fn_value(code: int) -> float:
 
 
 _E4M3FN_TABLE = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3fn_round(v: np.ndarray) -> np.ndarray:
+    """E4M3FN code of the representable value nearest to each v (|v| <= 448), ties to the
+    code with an even mantissa (round to nearest even); the sign of zero is kept."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.abs(v) > 448.0) or np.any(np.isnan(v)):
+        raise ValueError("value outside the E4M3FN range")
+    mags = np.array([e4m3fn_value(c) for c in range(0x7F)])          # codes 0x00..0x7E, increasing
+    a = np.abs(v).reshape(-1)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)     # first magnitude >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a == mags[hi], hi, np.where(pick_hi, hi, lo))
+    sign = np.signbit(v.reshape(-1)).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8).reshape(v.shape)
+
+
+def quantize_mx_fp8(x: np.ndarray, group: int = 128):
+    """Per-row, per-group fp8 quantisation with power-of-two scales.
+
+    [NKI-CTE] quantises activations to MX fp8 with 8-bit power-of-two (compact) scales;
+    the group is 128 columns of one token (the weights' 128 block size along K).  For
+    each group the exponent e is the smallest integer with max|x| <= 448 * 2^e (0 for an
+    all-zero group) and codes = E4M3FN(x * 2^-e).  Returns (codes uint8 [M, K],
+    exponents int [M, ceil(K/group)], dequantised float64 [M, K])."""
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    G = -(-K // group)
+    exps = np.zeros((M, G), dtype=np.int64)
+    codes = np.zeros((M, K), dtype=np.uint8)
+    for gi in range(G):
+        blk = x[:, gi * group:(gi + 1) * group]
+        for m in range(M):
+            amax = float(np.max(np.abs(blk[m])))
+            if amax == 0.0:
+                continue
+            mant, ex = math.frexp(amax)           # amax = mant * 2^ex, mant in [0.5, 1)
+            e = ex - 9                            # 448 = 0.875 * 2^9
+            if amax > 448.0 * 2.0 ** e:
+                e += 1
+            exps[m, gi] = e
+        codes[:, gi * group:(gi + 1) * group] = e4m3fn_round(blk * 2.0 ** (-exps[:, gi:gi + 1]))
+    table = np.array([e4m3fn_value(c) for c in range(256)])
+    deq = table[codes] * 2.0 ** np.repeat(exps, group, axis=1)[:, :K]
+    return codes, exps, deq
+
+
+def _act(a: np.ndarray, dims: dict) -> np.ndarray:
+    """An activation as a projection consumes it: fp8-quantised and dequantised when the
+    layer quantises activations (dims["act_quant"]), else unchanged."""
+    if not dims.get("act_quant"):
+        return a
+    shape = a.shape
+    return quantize_mx_fp8(a.reshape(-1, shape[-1]))[2].reshape(shape)
 
 
 def decode_tensor(kind: str, data: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
@@ -203,10 +264,10 @@ def project(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, dims
     eps = dims["norm_eps"]
     ang = rope_angles(positions, dr, dims.get("rope_theta", 10000.0), dims.get("inv_freq"))
     rows = project_rows(W, x, positions, dims)
-    x = input_norm(W, x, dims)
+    x = _act(input_norm(W, x, dims), dims)
     if "wq_a" in W:
         cq = rms_norm(x @ W["wq_a"], W["q_norm_w"], eps)
-        q = cq @ W["wq_b"]
+        q = _act(cq, dims) @ W["wq_b"]
     else:
         q = x @ W["wq_b"]
     q = q.reshape(x.shape[0], H, dn + dr)
@@ -223,7 +284,7 @@ def project_rows(W: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray,
     first put through the layer-input RMSNorm when W holds input_norm_w."""
     Lkv, dr = dims["kv_lora_rank"], dims["qk_rope"]
     ang = rope_angles(positions, dr, dims.get("rope_theta", 10000.0), dims.get("inv_freq"))
-    kva = input_norm(W, x, dims) @ W["wkv_a"]
+    kva = _act(input_norm(W, x, dims), dims) @ W["wkv_a"]
     c = rms_norm(kva[:, :Lkv], W["kv_norm_w"], dims["norm_eps"])
     p = rope_interleaved(kva[:, Lkv:], ang)
     return np.concatenate([c, p], axis=-1)
@@ -237,7 +298,7 @@ def expand_kv(W: Dict[str, np.ndarray], rows: np.ndarray, dims: dict):
     Returns K [T, H, dqk], V [T, H, dv]."""
     H, dn, dv, Lkv = dims["n_heads"], dims["qk_nope"], dims["v_dim"], dims["kv_lora_rank"]
     T = rows.shape[0]
-    kv = (rows[:, :Lkv] @ W["wkv_b"]).reshape(T, H, dn + dv)
+    kv = (_act(rows[:, :Lkv], dims) @ W["wkv_b"]).reshape(T, H, dn + dv)
     p = np.broadcast_to(rows[:, None, Lkv:], (T, H, rows.shape[1] - Lkv))
     return np.concatenate([kv[..., :dn], p], axis=-1), kv[..., dn:].copy()
 
@@ -259,6 +320,12 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
     return np.matmul(p, V.transpose(1, 0, 2)).transpose(1, 0, 2)          # [Tq, H, dv]
 
 
+def out_proj(W: Dict[str, np.ndarray], o: np.ndarray, dims: dict) -> np.ndarray:
+    """y = concat_h(o) @ wo ([NeMo-MLA] o_proj), o quantised first when the layer quantises
+    activations."""
+    return _act(o.reshape(o.shape[0], -1), dims) @ W["wo"]
+
+
 # ----------------------------------------------------------------------------- whole layer
 def mla_prefill(W: Dict[str, np.ndarray], x: np.ndarray, dims: dict) -> dict:
     """Causal prefill of T tokens at positions 0..T-1 of one sequence.
@@ -271,7 +338,7 @@ def mla_prefill(W: Dict[str, np.ndarray], x: np.ndarray, dims: dict) -> dict:
     q, rows = project(W, x, pos, dims)
     K, V = expand_kv(W, rows, dims)
     o = attention(q, K, V, dims["softmax_scale"], pos)
-    y = o.reshape(T, -1) @ W["wo"]
+    y = out_proj(W, o, dims)
     return dict(q=q, k=K, v=V, rows=rows, o=o, y=y)
 
 
@@ -289,7 +356,7 @@ def mla_decode(W: Dict[str, np.ndarray], x: np.ndarray, history: Sequence[np.nda
     seqs = [np.concatenate([np.asarray(history[b], dtype=np.float64).reshape(-1, rows.shape[1]),
                             rows[b:b + 1]], axis=0) for b in range(B)]
     o = decode_attention(W, q, seqs, dims, head_chunk)
-    y = o.reshape(B, -1) @ W["wo"]
+    y = out_proj(W, o, dims)
     return dict(q=q, rows=rows, o=o, y=y)
 
 
@@ -300,7 +367,8 @@ def decode_attention(W: Dict[str, np.ndarray], q: np.ndarray, seqs: Sequence[np.
     q [B, H, dqk] (q_pe already roped); seqs[b] = rows [n_b, R] of sequence b
     (the query's own row last).  Keys and values are expanded per head through
     wkv_b ([NKI-CTE] KV path stage 2 and final assembly), head_chunk heads at a
-    time.  Returns o [B, H, dv]."""
+    time; the latent rows are not quantised (absorbed attention has no projection
+    input).  Returns o [B, H, dv]."""
     H, dv = dims["n_heads"], dims["v_dim"]
     B = q.shape[0]
     o = np.zeros((B, H, dv))
@@ -309,7 +377,7 @@ def decode_attention(W: Dict[str, np.ndarray], q: np.ndarray, seqs: Sequence[np.
         for h0 in range(0, H, head_chunk):
             hs = slice(h0, min(H, h0 + head_chunk))
             sub = _head_slice(W, dims, hs)
-            K, V = expand_kv(sub, rows, dict(dims, n_heads=hs.stop - hs.start))
+            K, V = expand_kv(sub, rows, dict(dims, n_heads=hs.stop - hs.start, act_quant=False))
             o[b, hs] = attention(q[b:b + 1, hs], K, V, dims["softmax_scale"], np.array([len(rows) - 1]))[0]
     return o
 
@@ -331,7 +399,7 @@ def chunk_attention(W: Dict[str, np.ndarray], q: np.ndarray, prefix_rows: np.nda
     for h0 in range(0, H, head_chunk):
         hs = slice(h0, min(H, h0 + head_chunk))
         sub = _head_slice(W, dims, hs)
-        K, V = expand_kv(sub, rows, dict(dims, n_heads=hs.stop - hs.start))
+        K, V = expand_kv(sub, rows, dict(dims, n_heads=hs.stop - hs.start, act_quant=False))
         o[:, hs] = attention(q[:, hs], K, V, dims["softmax_scale"], P + np.arange(T))
     return o
 
@@ -379,7 +447,8 @@ def dims_of(shape) -> dict:
              kv_lora_rank=shape.kv_lora_rank, qk_nope=shape.qk_nope, qk_rope=shape.qk_rope,
              v_dim=shape.v_dim, norm_eps=shape.norm_eps, rope_theta=shape.rope_theta,
              softmax_scale=softmax_scale(shape.qk_nope, shape.qk_rope, factor,
-                                         getattr(shape, "rope_mscale_all_dim", 1.0)))
+                                         getattr(shape, "rope_mscale_all_dim", 1.0)),
+             act_quant=bool(getattr(shape, "act_quant", False)))
     if factor > 1.0:
         d["inv_freq"] = yarn_inv_freq(shape.qk_rope, shape.rope_theta, factor, shape.rope_original_max,
                                       shape.rope_beta_fast, shape.rope_beta_slow)

@@ -49,6 +49,7 @@ class MlaShape:
     rope_beta_slow: float = 1.0
     rope_mscale_all_dim: float = 1.0
     input_norm: bool = False  # the layer-input RMSNorm gamma input_norm_w is given
+    act_quant: bool = False   # activations entering the projections are fp8-quantised
 
     @property
     def qk_head(self) -> int:

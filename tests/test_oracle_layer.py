@@ -44,8 +44,12 @@ def _rms_loops(v, g, eps):
 
 
 def _layer_loops(W, x, d):
-    """Scalar-loop MLA prefill written from the definitions, for tiny shapes only."""
+    """Scalar-loop MLA prefill written from the definitions, for tiny shapes only.  With
+    d["act_quant"] each projection input row goes through the (separately pinned) fp8
+    quantiser first."""
     T, D = x.shape
+    qz = (lambda v: list(O.quantize_mx_fp8(np.array([v], dtype=np.float64))[2][0])) if d.get("act_quant") \
+        else (lambda v: v)
     H, Lq, Lkv, dn, dr, dv = (d[k] for k in ("n_heads", "q_lora_rank", "kv_lora_rank", "qk_nope", "qk_rope", "v_dim"))
     dqk = dn + dr
     q = [[[0.0] * dqk for _ in range(H)] for _ in range(T)]
@@ -57,9 +61,10 @@ def _layer_loops(W, x, d):
         xt = [x[t, i] for i in range(D)]
         if "input_norm_w" in W:
             xt = _rms_loops(xt, W["input_norm_w"], d["norm_eps"])
+        xt = qz(xt)
         if Lq:
             cq = [sum(xt[i] * W["wq_a"][i, j] for i in range(D)) for j in range(Lq)]
-            qin = _rms_loops(cq, W["q_norm_w"], d["norm_eps"])
+            qin = qz(_rms_loops(cq, W["q_norm_w"], d["norm_eps"]))
         else:
             qin = xt
         qf = [sum(qin[j] * W["wq_b"][j, c] for j in range(len(qin))) for c in range(H * dqk)]
@@ -70,8 +75,9 @@ def _layer_loops(W, x, d):
         cn = _rms_loops(kva[:Lkv], W["kv_norm_w"], d["norm_eps"])
         p = _rope_pair_loops(kva[Lkv:], t, inv_freq=f)
         rows.append(cn + p)
+        cq_ = qz(cn)
         for h in range(H):
-            e = [sum(cn[c] * W["wkv_b"][c, h * (dn + dv) + j] for c in range(Lkv)) for j in range(dn + dv)]
+            e = [sum(cq_[c] * W["wkv_b"][c, h * (dn + dv) + j] for c in range(Lkv)) for j in range(dn + dv)]
             K[t][h] = e[:dn] + p
             V[t][h] = e[dn:]
     o = [[[0.0] * dv for _ in range(H)] for _ in range(T)]
@@ -83,24 +89,31 @@ def _layer_loops(W, x, d):
             z = sum(e)
             for k in range(dv):
                 o[t][h][k] = sum(e[j] * V[j][h][k] for j in range(t + 1)) / z
-    y = [[sum(o[t][h][k] * W["wo"][h * dv + k, n] for h in range(H) for k in range(dv)) for n in range(D)]
+    oq = [qz([o[t][h][k] for h in range(H) for k in range(dv)]) for t in range(T)]
+    y = [[sum(oq[t][h * dv + k] * W["wo"][h * dv + k, n] for h in range(H) for k in range(dv)) for n in range(D)]
          for t in range(T)]
     return dict(q=np.array(q), k=np.array(K), v=np.array(V), rows=np.array(rows), o=np.array(o), y=np.array(y))
 
 
-@pytest.mark.parametrize("Lq,extras", [(5, False), (0, False), (5, True), (0, True)])
-def test_prefill_matches_scalar_loops(Lq, extras):
+@pytest.mark.parametrize("Lq,extras,aq", [(5, False, False), (0, False, False), (5, True, False), (0, True, False),
+                                          (5, True, True), (0, False, True)])
+def test_prefill_matches_scalar_loops(Lq, extras, aq):
     """extras: the layer-input RMSNorm, a given two-pair frequency table in place of
     theta^(-2i/dr), and the score scale with YaRN's factor-4 magnitude."""
     W, d = _tiny_weights(11 + Lq, D=7, H=2, Lq=Lq, Lkv=6, dn=3, dr=4, dv=2, input_norm=extras)
     if extras:
         d["inv_freq"] = np.array([0.9, 0.004])
         d["softmax_scale"] = O.softmax_scale(3, 4, 4.0, 1.0)
+    d["act_quant"] = aq
     x = synth.rng(12, "x").standard_normal((4, 7))
     ref = _layer_loops(W, x, d)
     got = O.mla_prefill(W, x, d)
     for k in ("q", "k", "v", "rows", "o", "y"):
         np.testing.assert_allclose(got[k], ref[k], rtol=1e-11, atol=1e-12, err_msg=k)
+    if aq:  # quantisation changes the result, within the E4M3 error scale
+        plain = O.mla_prefill(W, x, dict(d, act_quant=False))
+        rel = np.abs(plain["y"] - got["y"]).max() / np.abs(plain["y"]).max()
+        assert 1e-4 < rel < 0.2, rel
 
 
 def test_decode_equals_prefill_last_token():

@@ -91,6 +91,52 @@ def test_rmsnorm_closed_forms():
     np.testing.assert_allclose(O.rms_norm(z * 1e6, g[0], eps), O.rms_norm(z * 2e6, g[0], eps), rtol=1e-9)
 
 
+# ----------------------------------------------------------------------------- fp8 activation quantisation
+def test_e4m3fn_round_matches_torch_cast():
+    """Round-to-nearest-even into E4M3FN against torch's CPU float8 cast, on float32 values:
+    every representable value, every midpoint between neighbours (the ties), and random
+    values over the normal and subnormal ranges."""
+    mags = np.array([O.e4m3fn_value(c) for c in range(0x7F)])
+    mids = (mags[1:] + mags[:-1]) / 2
+    r = synth.rng(5, "e4m3-round")
+    rnd = np.concatenate([r.uniform(-448, 448, 4000), r.uniform(-2.0 ** -5, 2.0 ** -5, 2000),
+                          r.uniform(-1, 1, 2000)])
+    v = np.concatenate([mags, -mags, mids, -mids, rnd]).astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3fn_round(v)
+    assert (got == want).all(), np.nonzero(got != want)[0][:10]
+
+
+def test_quantize_mx_fp8_closed_forms():
+    K = 300  # two full groups and a partial one of 44 columns
+    x = np.zeros((5, K))
+    x[0, :128] = np.linspace(-448.0, 448.0, 128) * 2.0 ** 3      # amax = 448 * 2^3 exactly -> e = 3
+    x[0, 128:256] = 448.0 * 2.0 ** -7 * (1 + 2.0 ** -20)          # just above 448 * 2^-7 -> e = -6
+    x[1, :128] = 1.0                                              # amax 1 -> e = -8 (448 * 2^-9 < 1 <= 448 * 2^-8)
+    x[2, 256:] = 3.0                                              # partial group
+    codes, exps, deq = O.quantize_mx_fp8(x)
+    assert exps.shape == (5, 3)
+    assert exps[0, 0] == 3 and exps[0, 1] == -6 and exps[1, 0] == -8 and exps[2, 2] == -7
+    assert (exps[3] == 0).all() and (codes[3] == 0).all() and (deq[3] == 0).all()   # all-zero groups
+    # values already of the form code * 2^e come back exactly
+    table = np.array([O.e4m3fn_value(c) for c in range(256)])
+    r = synth.rng(6, "mx")
+    cs = r.integers(0, 256, (4, 256))
+    cs[(cs & 0x7F) == 0x7F] = 0x38                                 # no NaN codes
+    cs[:, 0] = 0x7E                                                # each group holds the largest code
+    cs[:, 128] = 0xFE
+    e_true = r.integers(-12, 6, (4, 2))
+    xv = table[cs] * 2.0 ** np.repeat(e_true, 128, axis=1)
+    c2, e2, d2 = O.quantize_mx_fp8(xv)
+    assert (e2 == e_true).all() and (d2 == xv).all()
+    # error bound: half a unit of E4M3's 3-bit mantissa, or of the subnormal step 2^(e-9)
+    z = r.standard_normal((6, 384)) * np.array([1e-3, 1.0, 50.0, 1e4, 1e-8, 3.0])[:, None]
+    c3, e3, d3 = O.quantize_mx_fp8(z)
+    sc = 2.0 ** np.repeat(e3, 128, axis=1)
+    assert (np.abs(d3 - z) <= np.maximum(np.abs(z) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-12)).all()
+    assert (np.abs(z / sc) <= 448).all()
+
+
 # ----------------------------------------------------------------------------- RoPE
 def test_rope_golden_points():
     for row in _golden_rows("rope_points.txt"):
