@@ -101,7 +101,7 @@ def quantize_mx_fp8(x: np.ndarray, group: int = 128):
     [NKI-CTE] quantises activations to MX fp8 with 8-bit power-of-two (compact) scales;
     the group is 128 columns of one token (the weights' 128 block size along K).  For
     each group the exponent e is the smallest integer with max|x| <= 448 * 2^e (0 for an
-    all-zero group) and codes = E4M3FN(x * 2^-e).  Returns (codes uint8 [M, K],
+    all-zero group, clamped to [-127, 127]) and codes = E4M3FN(x * 2^-e).  Returns (codes uint8 [M, K],
     exponents int [M, ceil(K/group)], dequantised float64 [M, K])."""
     x = np.asarray(x, dtype=np.float64)
     M, K = x.shape
@@ -118,7 +118,7 @@ def quantize_mx_fp8(x: np.ndarray, group: int = 128):
             e = ex - 9                            # 448 = 0.875 * 2^9
             if amax > 448.0 * 2.0 ** e:
                 e += 1
-            exps[m, gi] = e
+            exps[m, gi] = min(max(e, -127), 127)   # the range of an 8-bit power-of-two (E8M0) scale
         codes[:, gi * group:(gi + 1) * group] = e4m3fn_round(blk * 2.0 ** (-exps[:, gi:gi + 1]))
     table = np.array([e4m3fn_value(c) for c in range(256)])
     deq = table[codes] * 2.0 ** np.repeat(exps, group, axis=1)[:, :K]
