@@ -36,9 +36,9 @@ Readings where the pages are silent (each listed in the design notes too):
     as the two latent norms and is applied to x before the stage-1 projection.
   * fp8 activation quantisation (when dims["act_quant"] is set): every activation
     entering a projection (x, the normed q latent, the normed kv latent, the
-    attention output) is quantised per token and per group of 128 columns to E4M3FN
-    codes times a power-of-two scale 2^e, e the smallest integer with
-    max|group| <= 448 * 2^e, codes rounded to nearest, ties to even.
+    attention output), as the bf16 value the layer stores, is quantised per token and
+    per group of 128 columns to E4M3FN codes times a power-of-two scale 2^e, e the
+    smallest integer with max|group| <= 448 * 2^e, codes rounded to nearest, ties to even.
 
 Parity pins: every function here is checked in tests/test_oracle_*.py against
 closed forms, textbook special cases, torch's CPU float8 decoding, or
@@ -52,7 +52,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "e4m3fn_value", "e4m3fn_round", "quantize_mx_fp8", "decode_tensor", "rms_norm", "rope_angles", "rope_interleaved",
+    "e4m3fn_value", "e4m3fn_round", "bf16_round", "quantize_mx_fp8", "decode_tensor", "rms_norm", "rope_angles", "rope_interleaved",
     "softmax_scale", "yarn_inv_freq", "yarn_mscale", "input_norm", "project", "project_rows", "expand_kv", "attention", "mla_prefill", "mla_decode", "decode_attention", "chunk_attention",
     "out_proj", "place_rows", "cache_read_dense", "decode_weights", "dims_of",
 ]
@@ -95,6 +95,13 @@ def e4m3fn_round(v: np.ndarray) -> np.ndarray:
     return (code | sign).astype(np.uint8).reshape(v.shape)
 
 
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value (8-bit mantissa), ties to even, of each float64 v (finite)."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                       # v = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0), e - 8)   # np.round rounds halves to even
+
+
 def quantize_mx_fp8(x: np.ndarray, group: int = 128):
     """Per-row, per-group fp8 quantisation with power-of-two scales.
 
@@ -127,11 +134,13 @@ def quantize_mx_fp8(x: np.ndarray, group: int = 128):
 
 def _act(a: np.ndarray, dims: dict) -> np.ndarray:
     """An activation as a projection consumes it: fp8-quantised and dequantised when the
-    layer quantises activations (dims["act_quant"]), else unchanged."""
+    layer quantises activations (dims["act_quant"]), else unchanged.  The quantiser sees the
+    activation as the layer stores it, a bfloat16 value: each code is a decision taken in
+    floating point, made here in the same precision as on the device."""
     if not dims.get("act_quant"):
         return a
     shape = a.shape
-    return quantize_mx_fp8(a.reshape(-1, shape[-1]))[2].reshape(shape)
+    return quantize_mx_fp8(bf16_round(a.reshape(-1, shape[-1])))[2].reshape(shape)
 
 
 def decode_tensor(kind: str, data: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:

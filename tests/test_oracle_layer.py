@@ -45,11 +45,11 @@ def _rms_loops(v, g, eps):
 
 def _layer_loops(W, x, d):
     """Scalar-loop MLA prefill written from the definitions, for tiny shapes only.  With
-    d["act_quant"] each projection input row goes through the (separately pinned) fp8
-    quantiser first."""
+    d["act_quant"] each projection input row is rounded to bf16 and goes through the fp8
+    quantiser first (both separately pinned)."""
     T, D = x.shape
-    qz = (lambda v: list(O.quantize_mx_fp8(np.array([v], dtype=np.float64))[2][0])) if d.get("act_quant") \
-        else (lambda v: v)
+    qz = (lambda v: list(O.quantize_mx_fp8(O.bf16_round(np.array([v], dtype=np.float64)))[2][0])) \
+        if d.get("act_quant") else (lambda v: v)
     H, Lq, Lkv, dn, dr, dv = (d[k] for k in ("n_heads", "q_lora_rank", "kv_lora_rank", "qk_nope", "qk_rope", "v_dim"))
     dqk = dn + dr
     q = [[[0.0] * dqk for _ in range(H)] for _ in range(T)]

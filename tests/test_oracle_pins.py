@@ -107,6 +107,18 @@ def test_e4m3fn_round_matches_torch_cast():
     assert (got == want).all(), np.nonzero(got != want)[0][:10]
 
 
+def test_bf16_round_matches_torch_cast():
+    """Round to nearest even into bfloat16 against torch's CPU cast of float32 values (every
+    float32 is exact in float64, and bf16 rounding of a float32 is a single rounding)."""
+    r = synth.rng(8, "bf16-round")
+    v = np.concatenate([r.standard_normal(20000) * 10.0 ** r.integers(-30, 30, 20000),
+                        (1 + (2 * np.arange(1, 200) + 1) * 2.0 ** -9),      # exact ties
+                        -(1 + (2 * np.arange(1, 200) + 1) * 2.0 ** -9), [0.0, -0.0]]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(v.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
 def test_quantize_mx_fp8_closed_forms():
     K = 300  # two full groups and a partial one of 44 columns
     x = np.zeros((5, K))
