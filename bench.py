@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2516.6
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -145,7 +146,7 @@ def run_prefill(w, reps):
     dw = mla.Weights({k: torch_io.to_device(v) for k, v in host.items()},
                      {k: torch_io.scale_to_device(v) for k, v in host.items() if v.scale is not None})
     cfg = mla.config(s.hidden, s.n_heads, s.q_lora_rank, s.kv_lora_rank, s.qk_nope, s.qk_rope, s.v_dim,
-                     act=s.act, weight=s.weight, block_size=s.block_size)
+                     act=s.act, weight=s.weight, block_size=s.block_size, act_quant=s.act_quant)
     x = torch_io.to_device(synth.make_x(w, T))
     cos, sin = mla.rope_cos_sin(np.arange(T), s.qk_rope)
     n_blocks = -(-T // s.block_size)
@@ -192,7 +193,8 @@ def run_prefill(w, reps):
     tq, ta, to = tq / reps, ta / reps, to / reps
     return dict(tflops=(f_qkv + f_attn + f_out) / ((tq + ta + to) * 1e-3) / 1e12,
                 attn_tflops=f_attn / (ta * 1e-3) / 1e12, ms=tq + ta + to, ms_qkv=tq, ms_attn=ta, ms_out=to,
-                wall_ms=wall * 1e3, flops=f_qkv + f_attn + f_out)
+                wall_ms=wall * 1e3, flops=f_qkv + f_attn + f_out,
+                proj_tflops=(f_qkv + f_out) / ((tq + to) * 1e-3) / 1e12)
 
 
 def run_chunked(w, prefix, T, reps):
@@ -296,6 +298,7 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -398,6 +401,17 @@ def main():
                           "ms_out_proj": round(pf["ms_out"], 3), "attn_TFLOPs": round(pf["attn_tflops"], 2),
                           "frac_bf16_peak": round(pf["tflops"] / BF16_PEAK_TFLOPS, 4),
                           "causal_counted_flops": pf["flops"]}
+    if not args.no_fp8:
+        log("[bench] V3 prefill, T=8192, fp8 weights and MX fp8 activations")
+        w8 = synth.custom(synth.WORKLOADS[4], 4, "v3-prefill-8192-fp8", weight="fp8", act_quant=True)
+        p8 = run_prefill(w8, args.prefill_reps)
+        out["prefill_fp8"] = {"workload": "v3-prefill-8192-fp8: E4M3 weights (power-of-two 128x128 block scales), "
+                                          "MX fp8 activations (1x128 groups) into every projection; bf16 attention",
+                              "ms": round(p8["ms"], 3), "ms_qkv": round(p8["ms_qkv"], 3),
+                              "ms_attn": round(p8["ms_attn"], 3), "ms_out_proj": round(p8["ms_out"], 3),
+                              "TFLOPs": round(p8["tflops"], 2),
+                              "projection_TFLOPs": round(p8["proj_tflops"], 2),
+                              "projection_frac_fp8_peak": round(p8["proj_tflops"] / FP8_PEAK_TFLOPS, 4)}
     if not args.no_chunk:
         prefix, T = 7168, 1024
         log(f"[bench] V3 chunked prefill, {T} tokens after {prefix}")

@@ -22,9 +22,9 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 FN_QKV_PREFILL, FN_PREFILL_ATTN, FN_DECODE_QKV, FN_DECODE_ATTN, FN_OUT_PROJ, FN_PREFILL_ATTN_PAGED = range(6)
 _DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 SYMBOLS = ("mla_qkv_prefill", "mla_prefill_attn", "mla_decode_qkv_and_scatter", "mla_decode_attn_absorbed",
-           "mla_out_proj", "mla_prefill_attn_paged", "mla_rope_inv_freq", "mla_rope_tables", "mla_workspace_size",
-           "mla_status_string", "mla_rope_score_scale")
-_STATUS_FNS = SYMBOLS[:8]
+           "mla_out_proj", "mla_prefill_attn_paged", "mla_quantize_fp8", "mla_rope_inv_freq", "mla_rope_tables",
+           "mla_workspace_size", "mla_status_string", "mla_rope_score_scale")
+_STATUS_FNS = SYMBOLS[:9]
 
 
 class MlaError(RuntimeError):
@@ -34,7 +34,8 @@ class MlaError(RuntimeError):
 class MlaConfig(Structure):
     _fields_ = [("hidden", c_int32), ("n_heads", c_int32), ("q_lora_rank", c_int32), ("kv_lora_rank", c_int32),
                 ("qk_nope", c_int32), ("qk_rope", c_int32), ("v_dim", c_int32), ("softmax_scale", c_float),
-                ("norm_eps", c_float), ("block_size", c_int32), ("act_dtype", c_int32), ("weight_dtype", c_int32)]
+                ("norm_eps", c_float), ("block_size", c_int32), ("act_dtype", c_int32), ("weight_dtype", c_int32),
+                ("act_quant", c_int32)]
 
 
 class MlaWeight(Structure):
@@ -76,6 +77,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_attn_absorbed.argtypes = [C, W, P, I32, P, I64, P, I32, P, P, P, SZ, P]
     lib.mla_out_proj.argtypes = [C, W, P, I32, P, P, SZ, P]
     lib.mla_prefill_attn_paged.argtypes = [C, W, P, I32, P, I64, P, I32, I32, P, P, SZ, P]
+    lib.mla_quantize_fp8.argtypes = [P, I32, I32, I64, P, P, P]
     lib.mla_rope_inv_freq.argtypes = [POINTER(MlaRope), I32, P, P]
     lib.mla_rope_tables.argtypes = [I32, I32, P, I32, P, P, P, P]
     lib.mla_rope_score_scale.argtypes = [POINTER(MlaRope), I32, I32]
@@ -91,14 +93,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 def config(hidden, n_heads, q_lora_rank, kv_lora_rank, qk_nope, qk_rope, v_dim, *, act="bf16",
-           weight="bf16", block_size=64, softmax_scale=None, norm_eps=1e-6, rope: Optional[MlaRope] = None) -> MlaConfig:
+           weight="bf16", block_size=64, softmax_scale=None, norm_eps=1e-6, rope: Optional[MlaRope] = None,
+           act_quant: bool = False) -> MlaConfig:
     """The layer's config; the score scale defaults to mla_rope_score_scale(rope) (1/sqrt(dqk)
     times YaRN's magnitude squared when rope has factor > 1)."""
     if softmax_scale is None:
         softmax_scale = load().mla_rope_score_scale(ctypes.byref(rope) if rope is not None else None,
                                                     qk_nope, qk_rope)
     return MlaConfig(hidden, n_heads, q_lora_rank or 0, kv_lora_rank, qk_nope, qk_rope, v_dim, softmax_scale,
-                     norm_eps, block_size, _DTYPES[act], _DTYPES[weight])
+                     norm_eps, block_size, _DTYPES[act], _DTYPES[weight], int(bool(act_quant)))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -152,6 +155,15 @@ def _ws(ws, cfg, fn, n, max_context=0, device="cuda"):
     if ws is None:
         ws = workspace(cfg, fn, n, max_context, device)
     return ws, ws.numel()
+
+
+def mla_quantize_fp8(x, stream=None):
+    """MX fp8 codes [M, K] (uint8) and exponent bytes [ceil(K/128), M] (e + 127) of bf16 rows x."""
+    M, K = x.shape
+    codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    exps = torch.empty(((K + 127) // 128, M), dtype=torch.uint8, device=x.device)
+    _check(load().mla_quantize_fp8(_ptr(x), M, K, x.stride(0), _ptr(codes), _ptr(exps), _stream(stream)))
+    return codes, exps
 
 
 def mla_rope_inv_freq(rope: MlaRope, qk_rope: int, device="cuda", stream=None) -> torch.Tensor:

@@ -47,6 +47,8 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
   if (!ok_pair) return MLA_ERR_UNSUPPORTED;
   // limits of the general kernels' per-thread arrays and LDS tiles
   if (c->kv_lora_rank > 1024 || c->qk_nope + c->qk_rope > 256 || c->v_dim > 256) return MLA_ERR_UNSUPPORTED;
+  if (c->act_quant != 0 && c->act_quant != 1) return MLA_ERR_INVALID_ARG;
+  if (c->act_quant == 1 && !(c->act_dtype == MLA_BF16 && c->weight_dtype == MLA_FP8_E4M3)) return MLA_ERR_UNSUPPORTED;
   d->D = c->hidden;
   d->H = c->n_heads;
   d->Lq = c->q_lora_rank;
@@ -59,6 +61,7 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
   d->bs = c->block_size;
   d->act = c->act_dtype == MLA_F32 ? 0 : 1;
   d->wk = c->weight_dtype == MLA_F32 ? W_F32 : (c->weight_dtype == MLA_BF16 ? W_BF16 : W_FP8);
+  d->aq = c->act_quant;
   return MLA_OK;
 }
 
@@ -85,10 +88,22 @@ size_t proj_out_bytes(const Dims& d, int M, int N, int K) {
   return (size_t)M * N * sizeof(float);
 }
 
+// Quantised activations of one projection (act_quant): codes + exponents for the fp8 kernel,
+// or dequantised bf16 rows for the other kernels.
+size_t quant_bytes(const Dims& d, int M, int N, int K, int n_split) {
+  if (!d.aq) return 0;
+  if (fast_gemm_f8_ok(d, M, N, K, n_split)) {
+    const size_t m_pad = (size_t)f8_rows_pad(M);
+    return align_up((size_t)M * K) + align_up((size_t)((K + 127) / 128) * m_pad);
+  }
+  return align_up((size_t)M * K * 2);
+}
+
 // output columns of the stage-1 projection: [q latent (Lq) or query (H*dqk) | c_kv | k_pe]
 int stage1_q_cols(const Dims& d) { return d.Lq > 0 ? d.Lq : d.H * d.dqk(); }
 
 struct QkvWs {
+  void* qz;    // quantised activations of the projection in flight (act_quant)
   void* xn;    // [n, D]                  x after the layer-input RMSNorm (act), when input_norm_w is given
   float* P1;   // [n, stage1_q_cols + R]  stage-1 projection
   float* P2;   // [n, H*dqk]              query up-projection (Lq > 0)
@@ -102,6 +117,10 @@ size_t qkv_ws(const Dims& d, int n, bool prefill, void* base, QkvWs* out) {
   QkvWs w;
   const int HQ = d.H * d.dqk();
   const int NKV = d.H * (d.dn + d.dv);
+  size_t qz = quant_bytes(d, n, stage1_q_cols(d) + d.R(), d.D, stage1_q_cols(d));
+  if (d.Lq > 0) qz = std::max(qz, quant_bytes(d, n, HQ, d.Lq, HQ));
+  if (prefill) qz = std::max(qz, quant_bytes(d, n, NKV, d.Lkv, NKV));
+  w.qz = c.take<char>(qz);
   w.xn = c.take<char>((size_t)n * d.D * act_bytes(d));
   w.P1 = (float*)c.take<char>(proj_out_bytes(d, n, stage1_q_cols(d) + d.R(), d.D));
   // results handed straight to their consumer need no buffer
@@ -162,11 +181,13 @@ size_t chunk_attn_ws(const Dims& d, int T, int max_context, void* base, DecodeAt
   return c.used;
 }
 
-size_t out_proj_ws(const Dims& d, int M, void* base, float** Y) {
+size_t out_proj_ws(const Dims& d, int M, void* base, float** Y, void** qz = nullptr) {
   Carver c(base);
   const bool fused = fast_gemm_fusable(d, M, d.D, d.H * d.dv, d.D, GemmEpilogue::STORE);
   float* y = (float*)c.take<char>(fused ? 0 : proj_out_bytes(d, M, d.D, d.H * d.dv));
+  void* q = c.take<char>(quant_bytes(d, M, d.D, d.H * d.dv, d.D));
   if (Y) *Y = y;
+  if (qz) *qz = q;
   return c.used;
 }
 
@@ -189,8 +210,22 @@ mla_status hip_status(hipError_t e) {
 // its own consumer kernel).
 mla_status project(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split, const WeightView& W1,
                    int M, int N, int K, float* out, Partials* res, hipStream_t s, const GemmEpilogue* epi = nullptr,
-                   bool* fused = nullptr) {
+                   bool* fused = nullptr, void* qz = nullptr) {
   if (fused) *fused = false;
+  if (d.aq) {
+    // MX fp8 activations: the fp8 matrix-core kernel when the shape allows, otherwise the same
+    // quantised values, dequantised exactly to bf16, through the usual kernels
+    if (fast_gemm_f8_ok(d, M, N, K, n_split)) {
+      uint8_t* codes = (uint8_t*)qz;
+      uint8_t* exps = codes + align_up((size_t)M * K);
+      HIP_TRY(quant_mx((const bf16_t*)A, lda, M, K, codes, exps, true, nullptr, s));
+      HIP_TRY(fast_gemm_f8(d, codes, exps, W0, n_split, W1, M, N, K, out, res, epi, fused, s));
+      return MLA_OK;
+    }
+    HIP_TRY(quant_mx((const bf16_t*)A, lda, M, K, nullptr, nullptr, false, (bf16_t*)qz, s));
+    A = qz;
+    lda = K;
+  }
   if (fast_proj_supported(d)) {
     HIP_TRY(fast_gemm(d, A, lda, W0, n_split, W1, M, N, K, out, res, epi, fused, s));
     return MLA_OK;
@@ -217,7 +252,8 @@ mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, 
   }
   Partials P1;
   const WeightView w1q = d.Lq > 0 ? view(d, w->wq_a, d.Lq) : view(d, w->wq_b, HQ);
-  mla_status st = project(d, x, d.D, w1q, NQ1, view(d, w->wkv_a, d.R()), n, NQ1 + d.R(), d.D, ws.P1, &P1, s);
+  mla_status st = project(d, x, d.D, w1q, NQ1, view(d, w->wkv_a, d.R()), n, NQ1 + d.R(), d.D, ws.P1, &P1, s, nullptr,
+                          nullptr, ws.qz);
   if (st != MLA_OK) return st;
   HIP_TRY(row_builder(d, P1, P1.offset(NQ1), n, w->q_norm_w, w->kv_norm_w, cosT, sinT, ws.cqn, ws.cn, kv_cache,
                       n_slots, slot_mapping, kbuf, s));
@@ -230,7 +266,7 @@ mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, 
     epi.cosT = cosT;
     epi.sinT = sinT;
     bool fused = false;
-    st = project(d, ws.cqn, d.Lq, wqb, HQ, wqb, n, HQ, d.Lq, ws.P2, &PQ, s, &epi, &fused);
+    st = project(d, ws.cqn, d.Lq, wqb, HQ, wqb, n, HQ, d.Lq, ws.P2, &PQ, s, &epi, &fused, ws.qz);
     if (st != MLA_OK) return st;
     if (fused) return MLA_OK;
   }
@@ -275,6 +311,13 @@ size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t 
       return chunk_attn_ws(d, n, max_context, nullptr, nullptr, nullptr);
   }
   return 0;
+}
+
+mla_status mla_quantize_fp8(const void* x, int32_t M, int32_t K, int64_t ldx, uint8_t* codes, uint8_t* exps,
+                            void* stream) {
+  if (!x || !codes || !exps || M <= 0 || K <= 0 || ldx < K) return MLA_ERR_INVALID_ARG;
+  HIP_TRY(quant_mx((const bf16_t*)x, ldx, M, K, codes, exps, false, nullptr, (hipStream_t)stream));
+  return MLA_OK;
 }
 
 mla_status mla_rope_inv_freq(const mla_rope* r, int32_t qk_rope, double* inv_freq, void* stream) {
@@ -328,7 +371,7 @@ mla_status mla_qkv_prefill(const mla_config* cfg, const mla_weights* w, const vo
   epi.y = k;
   epi.y2 = v;
   bool fused = false;
-  st = project(d, L.cn, d.Lkv, wkvb, NKV, wkvb, T, NKV, d.Lkv, L.PKV, &PKV, s, &epi, &fused);
+  st = project(d, L.cn, d.Lkv, wkvb, NKV, wkvb, T, NKV, d.Lkv, L.PKV, &PKV, s, &epi, &fused, L.qz);
   if (st != MLA_OK) return st;
   if (!fused) HIP_TRY(kv_split(d, PKV, T, k, v, s));
   return MLA_OK;
@@ -438,7 +481,8 @@ mla_status mla_out_proj(const mla_config* cfg, const mla_weights* w, const void*
   if (st != MLA_OK) return st;
   if (M <= 0 || !w || !o || !y || !check_weight(d, w->wo)) return MLA_ERR_INVALID_ARG;
   float* Y = nullptr;
-  const size_t need = out_proj_ws(d, M, ws, &Y);
+  void* qz = nullptr;
+  const size_t need = out_proj_ws(d, M, ws, &Y, &qz);
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int K = d.H * d.dv;
@@ -448,7 +492,7 @@ mla_status mla_out_proj(const mla_config* cfg, const mla_weights* w, const void*
   epi.kind = GemmEpilogue::STORE;
   epi.y = y;
   bool fused = false;
-  st = project(d, o, K, wo, d.D, wo, M, d.D, K, Y, &P, s, &epi, &fused);
+  st = project(d, o, K, wo, d.D, wo, M, d.D, K, Y, &P, s, &epi, &fused, qz);
   if (st != MLA_OK) return st;
   if (!fused) HIP_TRY(cast_rows(d, P, M, d.D, y, s));
   return MLA_OK;

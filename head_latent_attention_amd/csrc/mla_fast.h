@@ -44,6 +44,25 @@ hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cac
                             const int32_t* block_table, int max_blocks, int64_t bt_stride, const int32_t* ctx,
                             const WeightView& wkv_b, void* o, const FastDecodeWs& ws, hipStream_t s);
 
+// fp8 projection for M > 1024 with quantised activations: A8 E4M3FN codes [M, K] (row stride
+// K), Ae E8M0 exponents (one power-of-two scale per row and 128 columns) [K/128][f8_rows_pad(M)]
+// in f8_exp_order, fp8
+// weights whose block scales are powers of two (others make the outputs NaN).  Same result
+// hand-over as fast_gemm.  fast_gemm_f8_ok tells whether the shape is supported.
+bool fast_gemm_f8_ok(const Dims& d, int M, int N, int K, int n_split);
+// Rows of the exponent array: M padded to the fp8 kernel's 256-row tile, so that every row a
+// tile addresses has a byte.
+__host__ __device__ __forceinline__ int64_t f8_rows_pad(int64_t M) { return (M + 255) / 256 * 256; }
+// Byte index of the exponent of row m, 128-column group kg, rows padded to m_pad
+// (f8_rows_pad): per group, per block of 128 rows, row 16 mt + j at 8 j + mt.
+__host__ __device__ __forceinline__ int64_t f8_exp_order(int64_t kg, int64_t m, int64_t m_pad) {
+  const int64_t r = m & 127;
+  return kg * m_pad + (m - r) + 8 * (r & 15) + (r >> 4);
+}
+hipError_t fast_gemm_f8(const Dims& d, const uint8_t* A8, const uint8_t* Ae, const WeightView& W0, int n_split,
+                        const WeightView& W1, int M, int N, int K, float* out, Partials* res,
+                        const GemmEpilogue* epi, bool* fused, hipStream_t s);
+
 // Causal prefill flash attention.
 bool fast_prefill_attn_supported(const Dims& d);
 size_t fast_prefill_attn_ws_bytes(const Dims& d, int T);

@@ -309,6 +309,76 @@ __device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, 
       acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
 }
 
+// Epilogue of the 256 x 256 tile kernels (8 waves of 128 x 64; acc[mt][nt][i] is tile row
+// 128*wm + 4*g + 16*mt + i, column 64*wn + 16*nt + j).  PARTIALS stores fp32 sums; the bf16
+// consumers stage the tile in LDS (row-major, 512-byte rows, 16-byte chunks XOR-swizzled by
+// row; `st` is 128 KB of stage buffers no wave reads any more) so that global stores are
+// whole 16-byte chunks of 8 consecutive columns; the query's RoPE is applied on the way (the
+// partner column of a pair sits in lane j ^ 1).
+__device__ __forceinline__ void big_epilogue(const EpiArgs& E, f32x4 (&acc)[8][4], bf16_t* st, int M, int N,
+                                             float* C, int64_t ldc, int64_t split_off, int m0, int n0, int w,
+                                             int lane) {
+  const int tid = threadIdx.x, g = lane >> 4, j = lane & 15, wm = w >> 2, wn = w & 3;
+  const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
+  const int mb = 128 * wm + 4 * g;  // tile row of acc[mt][.][i]: mb + 16 mt + i
+  if (E.kind == GemmEpilogue::PARTIALS) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = n0 + 64 * wn + 16 * nt + j;
+      if (n >= N) continue;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + mb + 16 * mt + i;
+          if (m < M) C[split_off + (int64_t)m * ldc + n] = acc[mt][nt][i];
+        }
+    }
+    return;
+  }
+  lds_barrier();  // every wave is done with the stage buffers
+  auto chunk_of = [](int r, int c) { return 32 * r + (c ^ (r & 31)); };  // 16-byte chunk slot
+  const bool query = E.kind == GemmEpilogue::QUERY;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int c = 64 * wn + 16 * nt + j;
+    const int u = (n0 + c) % dqk;
+    const bool rope = query && u >= E.dn, odd = (u - E.dn) & 1;
+    const int p = (u - E.dn) >> 1;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mb + 16 * mt + i;
+        float y = acc[mt][nt][i];
+        if (query) {
+          const float other = __shfl_xor(y, 1);  // every lane takes part
+          if (rope) {
+            const int m = min(m0 + r, M - 1);
+            const float cs = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
+            y = odd ? other * sn + y * cs : y * cs - other * sn;
+          }
+        }
+        st[chunk_of(r, c >> 3) * 8 + (c & 7)] = f32_to_bf16(y);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's part of the tile is in LDS
+  lds_barrier();
+  for (int e = tid; e < kBigM * kBigN / 8; e += 512) {
+    const int r = e >> 5, c8 = e & 31;
+    const int m = m0 + r, n = n0 + 8 * c8;
+    if (m >= M || n >= N) continue;
+    const uint4 v = *(const uint4*)&st[chunk_of(r, c8) * 8];
+    if (E.kind == GemmEpilogue::KV) {
+      const int h = n / dkv, u = n - h * dkv;
+      bf16_t* dst = u < E.dn ? E.y + ((int64_t)m * E.H + h) * dqk + u : E.y2 + ((int64_t)m * E.H + h) * E.dv + (u - E.dn);
+      *(uint4*)dst = v;
+    } else {
+      *(uint4*)&E.y[(int64_t)m * N + n] = v;
+    }
+  }
+}
+
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) {
   __shared__ __attribute__((aligned(16))) uint4 As[kBigStages][kBigM * 4];
   __shared__ __attribute__((aligned(16))) uint4 Ws[kBigStages][2 * kBigK * 16];
@@ -348,69 +418,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
     big_step(G, W, m0, wn0, wn_end, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
              (uint4*)a_nx, (uint4*)w_nx, acc, w, lane);
   }
-  // ---- epilogue (same consumers as gemm_kernel)
-  const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
-  const int mb = 128 * wm + 4 * g;  // tile row of acc[mt][.][i]: mb + 16 mt + i
-  if (E.kind == GemmEpilogue::PARTIALS) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = n0 + 64 * wn + 16 * nt + j;
-      if (n >= G.N) continue;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + mb + 16 * mt + i;
-          if (m < G.M) G.C[(int64_t)blockIdx.z * G.split_stride + (int64_t)m * G.ldc + n] = acc[mt][nt][i];
-        }
-    }
-    return;
-  }
-  // bf16 consumers: the tile is staged in LDS (row-major, 512-byte rows, 16-byte chunks XOR-
-  // swizzled by row) so that global stores are whole 16-byte chunks of 8 consecutive columns;
-  // the query's RoPE is applied on the way (the partner column of a pair sits in lane j ^ 1)
-  lds_barrier();  // every wave is done with the stage buffers
-  bf16_t* st = (bf16_t*)&As[0][0];  // 256 x 256 bf16 = the 128 KB of stage buffers
-  auto chunk_of = [](int r, int c) { return 32 * r + (c ^ (r & 31)); };  // 16-byte chunk slot
-  const bool query = E.kind == GemmEpilogue::QUERY;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int c = 64 * wn + 16 * nt + j;
-    const int u = (n0 + c) % dqk;
-    const bool rope = query && u >= E.dn, odd = (u - E.dn) & 1;
-    const int p = (u - E.dn) >> 1;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mb + 16 * mt + i;
-        float y = acc[mt][nt][i];
-        if (query) {
-          const float other = __shfl_xor(y, 1);  // every lane takes part
-          if (rope) {
-            const int m = min(m0 + r, G.M - 1);
-            const float cs = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
-            y = odd ? other * sn + y * cs : y * cs - other * sn;
-          }
-        }
-        st[chunk_of(r, c >> 3) * 8 + (c & 7)] = f32_to_bf16(y);
-      }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's part of the tile is in LDS
-  lds_barrier();
-  for (int e = tid; e < kBigM * kBigN / 8; e += 512) {
-    const int r = e >> 5, c8 = e & 31;
-    const int m = m0 + r, n = n0 + 8 * c8;
-    if (m >= G.M || n >= G.N) continue;
-    const uint4 v = *(const uint4*)&st[chunk_of(r, c8) * 8];
-    if (E.kind == GemmEpilogue::KV) {
-      const int h = n / dkv, u = n - h * dkv;
-      bf16_t* dst = u < E.dn ? E.y + ((int64_t)m * E.H + h) * dqk + u : E.y2 + ((int64_t)m * E.H + h) * E.dv + (u - E.dn);
-      *(uint4*)dst = v;
-    } else {
-      *(uint4*)&E.y[(int64_t)m * G.N + n] = v;
-    }
-  }
+  big_epilogue(E, acc, (bf16_t*)&As[0][0], G.M, G.N, G.C, G.ldc, (int64_t)blockIdx.z * G.split_stride, m0, n0, w,
+               lane);
 }
 
 bool big_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda) {
@@ -470,6 +479,182 @@ hipError_t launch_plan(const Plan& p, const Dims& d, const void* A, int64_t lda,
                     : launch<128, 2, 2>(d, A, lda, W0, W1, n_split, C, ldc, M, N, K, p.k_split, p.splits, stride, E, s);
 }
 
+// ---------------------------------------------------------------------------------------------
+// fp8 variant of the large-M kernel: A holds E4M3FN codes with one power-of-two (E8M0) scale
+// per row and 128 columns, W E4M3FN codes with fp32 128 x 128 block scales that must be powers
+// of two (the compact 8-bit exponent scales of the NKI context-encoding kernel's MX fp8
+// weights).  Each K step of 128 is one 16x16x128 fp8 matrix op per output block, which applies
+// both scales itself (a per-lane E8M0 operand: the row's activation exponent, the block's
+// weight exponent).  Same 256 x 256 tile and 8-wave layout as gemm_big_kernel, hence the
+// same epilogue; two 64 KB stages.
+//   Operand layout (probed on gfx950): the op sums A[r][kappa(g, t)] * B[kappa(g, t)][c] over
+//   the 32 bytes t of lane group g = lane / 16 with one bijection kappa for both operands, so
+//   any k order works as long as A and B use the same one: here k = 32 g + t.  A lane (row
+//   lane % 16) reads its 32 bytes as two 16-byte chunks; a B lane (column lane % 16) gets
+//   k = 32 g + 8 q + b from four ds_read_b64_tr_b8 (lanes 2b, 2b + 1 of a group address row b
+//   of an 8 x 16-byte tile, lane i receives its column i).  The scale of row r for the
+//   op's k block b comes from lane 16 b + r, so every lane passes its own row's exponent.
+constexpr int kF8K = 128;
+constexpr int kF8Copies = 8;  // per wave per stage: 4 activation + 4 weight copies of 1 KB
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// A stage [256 rows][8 chunks of 16 B]: chunk c of row r at slot 8r + (c ^ ((r >> 1) & 5));
+// W stage [128 k][16 chunks]: chunk c of row k at slot 16k + (c ^ f8w_swz(k)).  Both keep the
+// operand reads' lane passes on distinct banks.
+__device__ __forceinline__ int f8a_swz(int r) { return (r >> 1) & 5; }
+__device__ __forceinline__ int f8w_swz(int k) { return (k & 7) | (((k >> 5) & 1) << 3); }
+
+// Activation exponents (f8_exp_order) are grouped so that the 8 rows a lane needs, 16 mt + j
+// for mt = 0..7 of one 128-row half of the tile, are one 8-byte load.
+struct F8Args {
+  const uint8_t* A;  // E4M3FN codes [M, K] (row stride lda bytes)
+  int64_t lda;
+  const uint8_t* Ae;  // E8M0 exponents [K / 128][f8_rows_pad(M)], f8_exp_order
+  WeightView W0, W1;
+  int n_split;
+  float* C;
+  int64_t ldc;
+  int M, N, K;
+  int k_split;
+  int64_t split_stride;
+};
+
+// acc += (A * 2^(byte SEL of sa - 127)) (B * 2^(sb - 127)) for one 16x16x128 E4M3 block
+template <int SEL>
+__device__ __forceinline__ f32x4 f8_mma(const i32x8& a, const i32x8& b, const f32x4& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, SEL, sa, 0, sb);
+}
+
+__device__ __forceinline__ void f8_issue(const F8Args& G, const WeightView& W, int m0, int wn0, int wn_end, int k0,
+                                         uint4* __restrict__ as, uint4* __restrict__ ws, int w, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 64 * (4 * w + i) + l, r = e >> 3, c = (e & 7) ^ f8a_swz(r);
+    const int m = min(m0 + r, G.M - 1);
+    dma16_buf(G.A, 0x7FFFFFF0u, (uint32_t)(m * G.lda + k0 + 16 * c), as + 64 * (4 * w + i));
+  }
+  const uint8_t* wb = (const uint8_t*)W.w + (int64_t)k0 * W.ld;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 64 * (4 * w + i) + l, k = e >> 4, c = (e & 15) ^ f8w_swz(k);
+    const int n = min(wn0 + 16 * c, wn_end - 16);
+    dma16_buf(wb, 0x7FFFFFF0u, (uint32_t)(k * W.ld + n), ws + 64 * (4 * w + i));
+  }
+}
+
+__device__ __forceinline__ void f8_step(const F8Args& G, const WeightView& W, int m0, int wn0, int wn_end, bool copy,
+                                        int k_pf, const uint4* __restrict__ as, const uint4* __restrict__ ws,
+                                        uint4* __restrict__ as_nx, uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4],
+                                        uint2 sa, int sb, uint2& sa_nx, uint32_t& sw_nx, int nb, int w, int lane) {
+  const int g = lane >> 4, j = lane & 15, wm = w >> 2, wn = w & 3;
+  if (copy) {
+    // exponents of the next step, a step ahead of their use: 8 activation rows of the lane
+    // (4 per register) and the weight block scale of the wave
+    const int kg = k_pf / kF8K;
+    const int64_t m_pad = f8_rows_pad(G.M);
+    sa_nx = *(const uint2*)(G.Ae + f8_exp_order(kg, m0 + 128 * wm + j, m_pad));
+    sw_nx = __float_as_uint(W.scale[(int64_t)kg * W.scale_ld + nb]);
+    f8_issue(G, W, m0, wn0, wn_end, k_pf, as_nx, ws_nx, w, lane);
+  }
+  i32x8 bfr[4];
+  const char* wsb = (const char*)ws;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int c = 4 * wn + nt;
+    i32x2 p[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = 32 * g + 8 * q + (j >> 1);
+      p[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(wsb + (16 * k + (c ^ f8w_swz(k))) * 16 + 8 * (j & 1)));
+    }
+    bfr[nt] = i32x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const int r = 128 * wm + 16 * mt + j;
+    const uint4 lo = as[8 * r + ((2 * g) ^ f8a_swz(r))], hi = as[8 * r + ((2 * g + 1) ^ f8a_swz(r))];
+    const i32x8 af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    const int sreg = mt < 4 ? (int)sa.x : (int)sa.y;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      switch (mt & 3) {  // byte of the exponent register: an immediate of the instruction
+        case 0: acc[mt][nt] = f8_mma<0>(af, bfr[nt], acc[mt][nt], sreg, sb); break;
+        case 1: acc[mt][nt] = f8_mma<1>(af, bfr[nt], acc[mt][nt], sreg, sb); break;
+        case 2: acc[mt][nt] = f8_mma<2>(af, bfr[nt], acc[mt][nt], sreg, sb); break;
+        default: acc[mt][nt] = f8_mma<3>(af, bfr[nt], acc[mt][nt], sreg, sb); break;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_f8_kernel(F8Args G, EpiArgs E) {
+  __shared__ __attribute__((aligned(16))) uint4 smem[2][4096];  // per stage: A 2048 + W 2048 chunks
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 2, wn = w & 3;
+  const int n0 = blockIdx.x * kBigN, m0 = blockIdx.y * kBigM;
+  const bool seg1 = n0 >= G.n_split;
+  const WeightView W = seg1 ? G.W1 : G.W0;
+  const int wn0 = seg1 ? n0 - G.n_split : n0, wn_end = seg1 ? G.N - G.n_split : G.n_split;
+  const int kbeg = blockIdx.z * G.k_split;
+  const int nsteps = (min(G.K, kbeg + G.k_split) - kbeg) / kF8K;
+  // the wave's 64 columns lie in one 128-column scale block (waves past the segment's end,
+  // whose columns are not stored, read the last block's scale)
+  const int nb = min((wn0 + 64 * wn) / 128, W.scale_ld - 1);
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned bad = 0;  // a weight scale that is not a positive power of two
+  uint2 sa = make_uint2(0, 0), sa_nx = make_uint2(0, 0);
+  uint32_t sw = 0, sw_nx = 0;
+  if (nsteps > 0) {
+    typedef __attribute__((address_space(3))) uint4 lds_uint4;
+    lds_uint4 *a0 = (lds_uint4*)&smem[0][0], *w0 = (lds_uint4*)&smem[0][2048];
+    asm volatile("" : "+s"(a0), "+s"(w0));
+    const int kg = kbeg / kF8K;
+    const int64_t m_pad = f8_rows_pad(G.M);
+    sa = *(const uint2*)(G.Ae + f8_exp_order(kg, m0 + 128 * wm + j, m_pad));
+    sw = __float_as_uint(W.scale[(int64_t)kg * W.scale_ld + nb]);
+    f8_issue(G, W, m0, wn0, wn_end, kbeg, (uint4*)a0, (uint4*)w0, w, lane);
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of step s
+    lds_barrier();                       // every wave's copies landed; stage (s + 1) % 2 is free
+    const bool more = s + 1 < nsteps;
+    typedef __attribute__((address_space(3))) uint4 lds_uint4;
+    lds_uint4 *a_cur = (lds_uint4*)&smem[s & 1][0], *w_cur = (lds_uint4*)&smem[s & 1][2048];
+    lds_uint4 *a_nx = (lds_uint4*)&smem[(s + 1) & 1][0], *w_nx = (lds_uint4*)&smem[(s + 1) & 1][2048];
+    asm volatile("" : "+s"(a_cur), "+s"(w_cur), "+s"(a_nx), "+s"(w_nx));
+    const int sb = (int)((sw >> 23) & 0xFF);
+    bad |= (sw & 0x807FFFFFu) | (sb == 0 || sb == 0xFF);
+    f8_step(G, W, m0, wn0, wn_end, more, kbeg + (s + 1) * kF8K, (const uint4*)a_cur, (const uint4*)w_cur,
+            (uint4*)a_nx, (uint4*)w_nx, acc, sa, sb, sa_nx, sw_nx, nb, w, lane);
+    sa = sa_nx;
+    sw = sw_nx;
+  }
+  if (bad) {  // weight scales outside the supported form poison the tile instead of giving wrong numbers
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{NAN, NAN, NAN, NAN};
+  }
+  big_epilogue(E, acc, (bf16_t*)&smem[0][0], G.M, G.N, G.C, G.ldc, (int64_t)blockIdx.z * G.split_stride, m0, n0, w,
+               lane);
+}
+
+bool f8_ok(const Dims& d, int M, int N, int K, int n_split, int k_split) {
+  return d.wk == W_FP8 && M > 1024 && K % kF8K == 0 && k_split % kF8K == 0 &&
+         (n_split >= N || n_split % kBigN == 0) && N % 16 == 0 && (n_split >= N || (N - n_split) % 16 == 0) &&
+         (int64_t)M * K + K < 0x7FFFFFF0LL;
+}
+
 }  // namespace
 
 bool fast_proj_supported(const Dims& d) {
@@ -524,6 +709,33 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
   hipError_t e = launch_plan(p, d, A, lda, W0, W0, n_split, out, N, M, n_split, K, stride, E, s);
   if (e != hipSuccess) return e;
   return launch_plan(p, d, A, lda, W1, W1, N - n_split, out + n_split, N, M, N - n_split, K, stride, E, s);
+}
+
+bool fast_gemm_f8_ok(const Dims& d, int M, int N, int K, int n_split) {
+  if (!fast_proj_supported(d) || M <= 0 || N <= 0 || K <= 0) return false;
+  return f8_ok(d, M, N, K, n_split, plan(M, N, K).k_split);
+}
+
+hipError_t fast_gemm_f8(const Dims& d, const uint8_t* A8, const uint8_t* Ae, const WeightView& W0, int n_split,
+                        const WeightView& W1, int M, int N, int K, float* out, Partials* res,
+                        const GemmEpilogue* epi, bool* fused, hipStream_t s) {
+  const Plan p = plan(M, N, K);
+  const int64_t stride = (int64_t)M * N;
+  *res = Partials{out, p.splits, stride, N};
+  if (fused) *fused = false;
+  if (!fast_gemm_f8_ok(d, M, N, K, n_split)) return hipErrorInvalidValue;
+  EpiArgs E{GemmEpilogue::PARTIALS, nullptr, nullptr, nullptr, nullptr, d.H, d.dn, d.dr, d.dv};
+  if (epi && fast_gemm_fusable(d, M, N, K, n_split, epi->kind)) {
+    E.kind = epi->kind;
+    E.y = (bf16_t*)epi->y;
+    E.y2 = (bf16_t*)epi->y2;
+    E.cosT = epi->cosT;
+    E.sinT = epi->sinT;
+    if (fused) *fused = true;
+  }
+  F8Args G{A8, K, Ae, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, p.k_split, stride};
+  gemm_f8_kernel<<<dim3((N + kBigN - 1) / kBigN, (M + kBigM - 1) / kBigM, p.splits), 512, 0, s>>>(G, E);
+  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -14,6 +14,7 @@ struct Dims {
   int bs;
   int act;      // 0 f32, 1 bf16
   int wk;       // WeightKind
+  int aq = 0;   // 1: activations entering the projections are MX fp8-quantised
   int dqk() const { return dn + dr; }
   int R() const { return Lkv + dr; }
 };
@@ -57,6 +58,14 @@ hipError_t rope_tables(int n, int dr, const int32_t* positions, int pos_offset, 
                        float* sinT, hipStream_t s);
 // y [n, D] act = x * rsqrt(mean(x^2) + eps) * gamma per row.
 hipError_t input_norm(const Dims& d, const void* x, int n, const float* gamma, void* y, hipStream_t s);
+
+// ---- MX fp8 activation quantisation -------------------------------------------------
+// Rows of x (bf16 [M, K], row stride ldx) per 128-column group: exponent e (E8M0 byte e+127)
+// and E4M3FN codes of x * 2^-e.  With deq null: codes [M, K] and exps, either [ceil(K/128)][M]
+// or, with exp_order, in the fp8 GEMM's f8_exp_order (rows padded to f8_rows_pad(M)).  With deq: only
+// the dequantised bf16 values [M, K] (row stride K).
+hipError_t quant_mx(const bf16_t* x, int64_t ldx, int M, int K, uint8_t* codes, uint8_t* exps, bool exp_order,
+                    bf16_t* deq, hipStream_t s);
 
 // ---- general (any shape) kernels: SIMT fp32 arithmetic ------------------------------
 // C[M, N] fp32 (row stride ldc) = A[M, K] (act, row stride lda) @ W[K, N]

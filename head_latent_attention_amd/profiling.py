@@ -101,8 +101,30 @@ def summary_md(stats_csv: str, title: str, command: str) -> str:
         short = short[5:] if short.startswith("void ") else short
         short = short if len(short) <= 80 else short[:77] + "..."
         lines.append(f"| `{short}` | {calls} | {avg_us:.1f} | {pct:.2f}% |")
+    trace = os.path.join(os.path.dirname(stats_csv), os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    if os.path.exists(trace):
+        lines += ["", "Library kernels by launch grid (one row per distinct launch shape, from the kernel trace):", "",
+                  "| kernel | grid (x, y, z) | launches | average (us) |", "|---|---|---:|---:|"]
+        for (name, grid), durs in by_grid(trace):
+            lines.append(f"| `{name}` | {grid} | {len(durs)} | {sum(durs) / len(durs):.1f} |")
     lines.append("")
     return "\n".join(lines)
+
+
+def by_grid(trace_csv: str):
+    """Durations (us) of the library's kernels grouped by (name, launch grid), in launch order."""
+    groups = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "mla::" not in name:
+                continue
+            short = name.replace("(anonymous namespace)::", "").split("(")[0]
+            short = short[5:] if short.startswith("void ") else short
+            grid = f"{r['Grid_Size_X']}, {r['Grid_Size_Y']}, {r['Grid_Size_Z']}"
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            groups.setdefault((short, grid), []).append(dur)
+    return list(groups.items())
 
 
 if __name__ == "__main__":

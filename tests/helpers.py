@@ -34,7 +34,7 @@ def lib_config(shape: synth.MlaShape):
     import head_latent_attention_amd as mla
     return mla.config(shape.hidden, shape.n_heads, shape.q_lora_rank, shape.kv_lora_rank, shape.qk_nope,
                       shape.qk_rope, shape.v_dim, act=shape.act, weight=shape.weight,
-                      block_size=shape.block_size, norm_eps=shape.norm_eps)
+                      block_size=shape.block_size, norm_eps=shape.norm_eps, act_quant=shape.act_quant)
 
 
 def device_weights(host: dict):

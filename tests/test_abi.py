@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -125,3 +125,21 @@ def test_prefill_attn_paged_validation():
     assert call(ws_bytes=8) == -3
     assert B.workspace_size(cfg, B.FN_PREFILL_ATTN_PAGED, 8, 64) > B.workspace_size(cfg, B.FN_DECODE_ATTN, 8, 64)
     assert B.workspace_size(cfg, B.FN_PREFILL_ATTN_PAGED, 8, 0) == 0
+
+
+def test_act_quant_config_and_quantize_validation():
+    lib = mla.load()
+    # act_quant needs bf16 activations with fp8 weights, and is 0 or 1
+    assert B.workspace_size(_cfg(act="bf16", weight="fp8", act_quant=True), 0, 8) > 0
+    assert B.workspace_size(_cfg(act="bf16", weight="bf16", act_quant=True), 0, 8) == 0
+    bad = _cfg(act="bf16", weight="fp8")
+    bad.act_quant = 2
+    assert B.workspace_size(bad, 0, 8) == 0
+    assert _call_decode_attn(_cfg(act="bf16", weight="bf16", act_quant=True)) == -2
+    # quantised activations take workspace of their own
+    assert B.workspace_size(_cfg(act="bf16", weight="fp8", act_quant=True), B.FN_OUT_PROJ, 8) > \
+        B.workspace_size(_cfg(act="bf16", weight="fp8"), B.FN_OUT_PROJ, 8)
+    assert lib.mla_quantize_fp8(None, 4, 128, 128, 1, 1, None) == -1
+    assert lib.mla_quantize_fp8(1, 0, 128, 128, 1, 1, None) == -1
+    assert lib.mla_quantize_fp8(1, 4, 128, 100, 1, 1, None) == -1   # row stride below K
+    assert lib.mla_quantize_fp8(1, 4, 128, 128, None, 1, None) == -1
