@@ -345,22 +345,39 @@ __device__ __forceinline__ void big_epilogue(const EpiArgs& E, f32x4 (&acc)[8][4
     const int u = (n0 + c) % dqk;
     const bool rope = query && u >= E.dn, odd = (u - E.dn) & 1;
     const int p = (u - E.dn) >> 1;
+    // cos/sin of this lane's pair for 16 rows at a time, all in flight before the first use
+    // (the barriers keep the next batch's loads from being hoisted above this one's uses)
+    const uint32_t tbytes = (uint32_t)min((int64_t)M * half * 4, (int64_t)0x7FFFFFF0);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int hm = 0; hm < 2; ++hm) {
+      __builtin_amdgcn_sched_barrier(0);
+      float cs[4][4], sn[4][4];
+      if (rope) {
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)E.cosT, 0, (int)tbytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)E.sinT, 0, (int)tbytes, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mb + 16 * mt + i;
-        float y = acc[mt][nt][i];
-        if (query) {
-          const float other = __shfl_xor(y, 1);  // every lane takes part
-          if (rope) {
-            const int m = min(m0 + r, M - 1);
-            const float cs = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
-            y = odd ? other * sn + y * cs : y * cs - other * sn;
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (uint32_t)((min(m0 + mb + 16 * (4 * hm + mt) + i, M - 1) * half + p) * 4);
+            cs[mt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0));
+            sn[mt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
           }
-        }
-        st[chunk_of(r, c >> 3) * 8 + (c & 7)] = f32_to_bf16(y);
       }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mb + 16 * (4 * hm + mt) + i;
+          float y = acc[4 * hm + mt][nt][i];
+          if (query) {
+            // the pair partner's value from lane j ^ 1 (DPP quad permutation [1, 0, 3, 2])
+            const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xF, 0xF, true));
+            if (rope) y = odd ? other * sn[mt][i] + y * cs[mt][i] : y * cs[mt][i] - other * sn[mt][i];
+          }
+          st[chunk_of(r, c >> 3) * 8 + (c & 7)] = f32_to_bf16(y);
+        }
+    }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's part of the tile is in LDS
   lds_barrier();
