@@ -365,18 +365,30 @@ __device__ __forceinline__ void big_epilogue(const EpiArgs& E, f32x4 (&acc)[8][4
           }
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) {
+        float y[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = mb + 16 * (4 * hm + mt) + i;
-          float y = acc[4 * hm + mt][nt][i];
+          y[i] = acc[4 * hm + mt][nt][i];
           if (query) {
             // the pair partner's value from lane j ^ 1 (DPP quad permutation [1, 0, 3, 2])
-            const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xF, 0xF, true));
-            if (rope) y = odd ? other * sn[mt][i] + y * cs[mt][i] : y * cs[mt][i] - other * sn[mt][i];
+            const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[i]), 0xB1, 0xF, 0xF, true));
+            if (rope) y[i] = odd ? other * sn[mt][i] + y[i] * cs[mt][i] : y[i] * cs[mt][i] - other * sn[mt][i];
           }
-          st[chunk_of(r, c >> 3) * 8 + (c & 7)] = f32_to_bf16(y);
         }
+        // lanes j and j ^ 1 hold columns c and c ^ 1 of the same 4 rows: swapping one value per
+        // row pair gives the even lane both columns of row i, the odd lane both of row i + 1,
+        // stored as one 4-byte write each
+        const int c0 = c & ~1;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float send = (j & 1) ? y[i] : y[i + 1];
+          const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+          const int r = mb + 16 * (4 * hm + mt) + i + (j & 1);
+          const uint32_t pk = (j & 1) ? pack_bf16x2(recv, y[i + 1]) : pack_bf16x2(y[i], recv);
+          *(uint32_t*)&st[chunk_of(r, c0 >> 3) * 8 + (c0 & 7)] = pk;
+        }
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's part of the tile is in LDS
