@@ -171,23 +171,26 @@ __global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q,
     if (blockIdx.y == 0 && blockIdx.z == 0) plan_block(ctx, B, P, info, zero_row, scan, Ps, Cs);
     return;
   }
+  __shared__ __attribute__((aligned(16))) uint4 tile[64 * 16];  // 64 rows x 128 columns, bf16
   const int h = blockIdx.x, cg = blockIdx.y, b0 = blockIdx.z * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
   constexpr int qs = kH * (kDn + kDr);
   const int c0 = 128 * cg + 32 * w;
   uint4 a[kDn / 32][4], bw[kDn / 32][2];
+  // every load is issued unconditionally (rows past B repeat row B - 1 and are never stored),
+  // so all of them are in flight together
 #pragma unroll
   for (int ks = 0; ks < kDn / 32; ++ks) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int b = b0 + 16 * mt + j;
-      a[ks][mt] = b < B ? *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + 32 * ks + 8 * g)
-                        : make_uint4(0, 0, 0, 0);
+      const int b = min(b0 + 16 * mt + j, B - 1);
+      a[ks][mt] = *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + 32 * ks + 8 * g);
     }
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
       bw[ks][nt] = load_w8<WK>(W, c0 + 16 * nt + j, (int64_t)h * (kDn + kDv) + 32 * ks + 8 * g);
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load above the first matrix op
   f32x4 acc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -201,16 +204,26 @@ __global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q,
       for (int nt = 0; nt < 2; ++nt)
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks][mt]), as_bf16x8(bw[ks][nt]),
                                                               acc[mt][nt], 0, 0, 0);
+  // the 64 x 128 result through LDS (16-byte chunks, chunk c of row r at slot 16r + (c ^ (r & 15)))
+  // so that each row goes out as 16-byte stores
+  bf16_t* tb = (bf16_t*)tile;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int b = b0 + 16 * mt + 4 * g + i;
-      if (b >= B) continue;
-      bf16_t* dst = Qabs + ((size_t)b * kH + h) * kR + c0 + j;
+      const int r = 16 * mt + 4 * g + i;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) dst[16 * nt] = f32_to_bf16(acc[mt][nt][i]);
+      for (int nt = 0; nt < 2; ++nt) {
+        const int c = 32 * w + 16 * nt + j;
+        tb[(16 * r + ((c >> 3) ^ (r & 15))) * 8 + (c & 7)] = f32_to_bf16(acc[mt][nt][i]);
+      }
     }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int e = it * 256 + tid, r = e >> 4, ch = e & 15, b = b0 + r;
+    if (b < B) *(uint4*)(Qabs + ((size_t)b * kH + h) * kR + 128 * cg + 8 * ch) = tile[16 * r + (ch ^ (r & 15))];
+  }
   // rope part of the query is carried over unchanged
   if (cg == 0) {
     for (int e = tid; e < 64 * kDr / 8; e += 256) {
@@ -554,8 +567,8 @@ __device__ __forceinline__ bool wg_nonempty(int w, int N) {
 // Grid (H, ceil(B/16)).  Merges the partials of 16 sequences for one head, then
 // o[b][h] = o_lat[b][h] @ W_UV[h] on the matrix cores (W_UV[h][c][j] = wkv_b[c][h*256 + 128 + j]).
 // A share's weight in the merge is 2^(m - M) * l (its normalised output times its own sum),
-// accumulated online (running max M) in share order.  The first 128 rows of W_UV[h] are
-// loaded before the merge so that their latency overlaps it.
+// accumulated online (running max M) in share order.  All of W_UV[h] is loaded into registers
+// before the merge, so that its latency overlaps the merge's loads.
 template <int WK>
 __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, const int32_t* __restrict__ P,
@@ -566,15 +579,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
   const int N = P[B];
   const int64_t col0 = (int64_t)h * (kDn + kDv) + kDn;
-  uint4 wr[8];
-  auto load_w_chunk = [&](int cc) {
+  uint4 wr[kLkv / 128][8];
+#pragma unroll
+  for (int cc = 0; cc < kLkv / 128; ++cc)
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
-      wr[it] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
+      wr[cc][it] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
     }
-  };
-  load_w_chunk(0);
+  __builtin_amdgcn_sched_barrier(0);  // the weight loads stay ahead of the merge
   // ---- merge: wave w handles local rows 4w..4w+3, each lane 8 latent columns
   for (int r = 0; r < 4; ++r) {
     const int lb = 4 * w + r, b = b0 + lb;
@@ -626,10 +639,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
-      *(uint4*)&Ws[r][8 * ch] = wr[it];
+      *(uint4*)&Ws[r][8 * ch] = wr[cc][it];
     }
     __syncthreads();
-    if (cc + 1 < kLkv / 128) load_w_chunk(cc + 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 a = as_bf16x8(*(const uint4*)&As[j][128 * cc + 32 * ks + 8 * g]);
