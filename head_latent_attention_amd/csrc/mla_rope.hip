@@ -4,9 +4,10 @@
 //   rope_inv_freq_kernel   per-pair inverse frequencies, plain or YaRN (atlas docs,
 //                          Struct MlaWeights, fields yarn_inv_freq / main_inv_freq),
 //                          evaluated in fp64
-//   rope_tables_kernel     cos/sin [n, dr/2] of angle = position * inv_freq[i], angle and
-//                          cos/sin in fp64, stored as fp32 (AWS Neuron NKI, "MLA Decode
-//                          QKV Kernel API Reference", cos/sin parameters)
+//   rope_tables_kernel     cos/sin [n, dr/2] of angle = position * inv_freq[i]: angle and
+//                          its reduction to a quadrant in fp64, cos/sin of the reduced
+//                          angle in fp32 (AWS Neuron NKI, "MLA Decode QKV Kernel API
+//                          Reference", cos/sin parameters)
 //   input_norm_kernel      x * rsqrt(mean(x^2) + eps) * gamma per row (same reference,
 //                          input_norm_w parameter), one workgroup per row
 #include <hip/hip_runtime.h>
@@ -56,10 +57,19 @@ __global__ void rope_tables_kernel(int n, int half, const int32_t* __restrict__ 
     const int t = (int)(e / half), i = (int)(e - (int64_t)t * half);
     const int64_t pos = (int64_t)(positions ? positions[t] : t) + pos_offset;
     const double f = inv_freq ? inv_freq[i] : pow(10000.0, -2.0 * i / (2 * half));
-    double s, c;
-    sincos((double)pos * f, &s, &c);
-    cosT[e] = (float)c;
-    sinT[e] = (float)s;
+    // the angle and its reduction to a quadrant, a = q pi/2 + r with |r| <= pi/4, in fp64
+    // (exact to ~1e-11 rad up to 1e5 rad); then fp32 cos/sin of r (rounding r to fp32 costs
+    // <= 3e-8 rad) rotated by the quadrant: a few fp32 ulps, at a fraction of fp64 sincos's cost
+    const double a = (double)pos * f;
+    const double half_pi = 1.5707963267948966192313216916398;
+    const double qd = rint(a / half_pi);
+    float sr, cr;
+    sincosf((float)(a - qd * half_pi), &sr, &cr);
+    const int quad = (int)((int64_t)qd & 3);
+    const float c = quad == 0 ? cr : quad == 1 ? -sr : quad == 2 ? -cr : sr;
+    const float sn = quad == 0 ? sr : quad == 1 ? cr : quad == 2 ? -sr : -cr;
+    cosT[e] = c;
+    sinT[e] = sn;
   }
 }
 

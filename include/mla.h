@@ -145,7 +145,8 @@ double mla_rope_score_scale(const mla_rope* rope, int32_t qk_nope, int32_t qk_ro
 
 /* cos/sin tables for the projection entry points: for token t < n and pair i < qk_rope/2,
  *   angle = (positions[t] + pos_offset) * inv_freq[i],  cos[t][i] = cos(angle), sin[t][i] = sin(angle)
- * with the angle, cos and sin evaluated in fp64 and stored as fp32.
+ * with the angle and its reduction to a quadrant (|remainder| <= pi/4) evaluated in fp64 and
+ * cos/sin of the remainder in fp32 (results within about 1e-7 of the exact values).
  *   positions  int32 [n] device, or NULL for positions 0..n-1 (e.g. context_lens with
  *              pos_offset -1 gives each decode token's position).
  *   inv_freq   fp64 [qk_rope/2] device (mla_rope_inv_freq), or NULL for theta = 10000.
