@@ -128,8 +128,7 @@ __device__ void plan_block(const int32_t* __restrict__ ctx, int B, int32_t* __re
     carry += scan[kPlanThreads - 1];
     __syncthreads();
   }
-  __threadfence();
-  __syncthreads();
+  __syncthreads();  // P (global) and Ps are read by other threads of this workgroup below
   const int32_t* PP = in_lds ? Ps : P;
   const int32_t* CC = in_lds ? Cs : ctx;
   const int N = carry;
@@ -356,11 +355,22 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
 constexpr int kSPre = 4;  // score operand reads in flight per wave
 constexpr int kVPre = 4;  // value operand reads in flight per wave
 
+// V^T operand of latent tile mt (16 latent rows x 32 tokens) by two transposing reads.
+__device__ __forceinline__ bf16x8 v_read(const char* bbase, const LaneOffsets& LO, int mt) {
+  const char* q = bbase + LO.v[mt & 7] + 256 * (mt >> 3);
+  const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
+  const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(q + 16 * 64 * 16));
+  return __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Scores of one sub-tile for this wave's 16 heads, then the online softmax (log2 domain,
 // lazy rescale of the running output).  Returns P^T as the B operand of the value product.
+// The first two value operand reads are issued before the softmax, which reads no LDS, so
+// that their latency is hidden behind it (more would not fit in the registers).
 __device__ __forceinline__ bf16x8 scores_softmax(const AttnArgs& A, int tok0, int tok_hi, const char* bbase,
                                                  const LaneOffsets& LO, const bf16x8 (&qf)[kR / 32],
-                                                 f32x4 (&o)[kLkv / 16], float& m_run, float& l_run, int lane) {
+                                                 f32x4 (&o)[kLkv / 16], float& m_run, float& l_run,
+                                                 bf16x8 (&vring)[kVPre], int lane) {
   const int g = lane >> 4;
   // ---- S^T[token][head]: 2 token tiles of 16; k-steps 0..15 latent, 16..17 rope
   auto s_read = [&](int it) -> bf16x8 {
@@ -381,6 +391,9 @@ __device__ __forceinline__ bf16x8 scores_softmax(const AttnArgs& A, int tok0, in
     if (it + kSPre < kSIt) ring[it % kSPre] = s_read(it + kSPre);
     __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) vring[mt] = v_read(bbase, LO, mt);
+  __builtin_amdgcn_sched_barrier(0);
   // ---- online softmax; the lane's head is 16*w + j, its tokens 16*mt + 4*g + i
   float x[8];
 #pragma unroll
@@ -421,22 +434,16 @@ __device__ __forceinline__ bf16x8 scores_softmax(const AttnArgs& A, int tok0, in
 }
 
 // O^T[latent][head] += V^T P^T over one sub-tile's 32 tokens (one k-step per latent tile).
+// vring holds the operands of latent tiles 0 and 1 on entry.
 __device__ __forceinline__ void value_product(const char* bbase, const LaneOffsets& LO, const bf16x8& pb,
-                                              f32x4 (&o)[kLkv / 16]) {
-  auto v_read = [&](int mt) -> bf16x8 {
-    const char* q = bbase + LO.v[mt & 7] + 256 * (mt >> 3);
-    const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
-    const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(q + 16 * 64 * 16));
-    return __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  bf16x8 vring[kVPre];
+                                              f32x4 (&o)[kLkv / 16], bf16x8 (&vring)[kVPre]) {
 #pragma unroll
-  for (int mt = 0; mt < kVPre; ++mt) vring[mt] = v_read(mt);
+  for (int mt = 2; mt < kVPre; ++mt) vring[mt] = v_read(bbase, LO, mt);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mt = 0; mt < kLkv / 16; ++mt) {
     o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vring[mt % kVPre], pb, o[mt], 0, 0, 0);
-    if (mt + kVPre < kLkv / 16) vring[mt % kVPre] = v_read(mt + kVPre);
+    if (mt + kVPre < kLkv / 16) vring[mt % kVPre] = v_read(bbase, LO, mt + kVPre);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -452,8 +459,9 @@ __device__ __forceinline__ void attn_step(const AttnArgs& A, int tok0, int tok_h
                                           f32x4 (&o)[kLkv / 16], float& m_run, float& l_run, int w, int lane) {
   if (copy) issue_tile_copy(A, blk_pf, tok_pf, tok_hi_pf, nxt, w, lane);
   if (!compute) return;
-  const bf16x8 pb = scores_softmax(A, tok0, tok_hi, (const char*)cur, LO, qf, o, m_run, l_run, lane);
-  value_product((const char*)cur, LO, pb, o);
+  bf16x8 vring[kVPre];
+  const bf16x8 pb = scores_softmax(A, tok0, tok_hi, (const char*)cur, LO, qf, o, m_run, l_run, vring, lane);
+  value_product((const char*)cur, LO, pb, o, vring);
 }
 
 constexpr int kPf = 3;  // sub-tiles whose copies are issued ahead of the one being computed
@@ -588,49 +596,62 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
       wr[cc][it] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
     }
   __builtin_amdgcn_sched_barrier(0);  // the weight loads stay ahead of the merge
-  // ---- merge: wave w handles local rows 4w..4w+3, each lane 8 latent columns
-  for (int r = 0; r < 4; ++r) {
-    const int lb = 4 * w + r, b = b0 + lb;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (b < B && P[b + 1] > P[b]) {
-      const int wf = (int)(((int64_t)(P[b] + 1) * kAttnWGs - 1) / N);
-      const int wl = (int)(((int64_t)P[b + 1] * kAttnWGs - 1) / N);
-      float M = -INFINITY, L = 0.f;
-      // four shares per round, all loads of a round issued together
-      for (int wq0 = wf; wq0 <= wl; wq0 += 4) {
-        float2 ml[4];
-        uint4 v[4];
-        bool ok[4];
+  // ---- merge: the 16 lanes of quarter g of wave w handle local row 4w + g, each lane 32 latent
+  // columns, so the four rows of a wave run their shares side by side (two shares per round)
+  {
+    const int lb = 4 * w + g, b = b0 + lb;
+    float acc[32];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int wq = wq0 + u;
-          ok[u] = wq <= wl && wg_nonempty(wq, N);
-          const size_t ps = ((size_t)(ok[u] ? wq : wf) + b) * kH + h;
-          ml[u] = *(const float2*)(part_ml + ps * 2);
-          v[u] = *(const uint4*)(part_o + ps * kLkv + 8 * lane);
-        }
+    for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+    int wf = 0, wl = -1;
+    if (b < B) {
+      const int p0 = P[b], p1 = P[b + 1];
+      if (p1 > p0) {
+        wf = (int)(((int64_t)(p0 + 1) * kAttnWGs - 1) / N);
+        wl = (int)(((int64_t)p1 * kAttnWGs - 1) / N);
+      }
+    }
+    float M = -INFINITY, L = 0.f;
+    for (int wq0 = wf; wq0 <= wl; wq0 += 2) {
+      float2 ml[2];
+      uint4 v[2][4];
+      bool ok[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (!ok[u]) continue;  // an empty share's slot was never written
-          const float Mn = fmaxf(M, ml[u].x);
-          const float sa = M == -INFINITY ? 0.f : exp2f(M - Mn);
-          const float f = exp2f(ml[u].x - Mn) * ml[u].y;
-          L = L * sa + f;
-          M = Mn;
-          const uint32_t wds[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      for (int u = 0; u < 2; ++u) {
+        const int wq = wq0 + u;
+        ok[u] = wq <= wl && wg_nonempty(wq, N);
+        const size_t ps = ((size_t)(ok[u] ? wq : wf) + b) * kH + h;
+        ml[u] = *(const float2*)(part_ml + ps * 2);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) v[u][q4] = *(const uint4*)(part_o + ps * kLkv + 32 * j + 8 * q4);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (!ok[u]) continue;  // an empty share's slot was never written
+        const float Mn = fmaxf(M, ml[u].x);
+        const float sa = M == -INFINITY ? 0.f : exp2f(M - Mn);
+        const float f = exp2f(ml[u].x - Mn) * ml[u].y;
+        L = L * sa + f;
+        M = Mn;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint32_t wds[4] = {v[u][q4].x, v[u][q4].y, v[u][q4].z, v[u][q4].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = acc[2 * e] * sa + f * __uint_as_float(wds[e] << 16);
-            acc[2 * e + 1] = acc[2 * e + 1] * sa + f * __uint_as_float(wds[e] & 0xFFFF0000u);
+            acc[8 * q4 + 2 * e] = acc[8 * q4 + 2 * e] * sa + f * __uint_as_float(wds[e] << 16);
+            acc[8 * q4 + 2 * e + 1] = acc[8 * q4 + 2 * e + 1] * sa + f * __uint_as_float(wds[e] & 0xFFFF0000u);
           }
         }
       }
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] *= inv;
     }
-    *(uint4*)&As[lb][8 * lane] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                           pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *(uint4*)&As[lb][32 * j + 8 * q4] =
+          make_uint4(pack_bf16x2(acc[8 * q4] * inv, acc[8 * q4 + 1] * inv),
+                     pack_bf16x2(acc[8 * q4 + 2] * inv, acc[8 * q4 + 3] * inv),
+                     pack_bf16x2(acc[8 * q4 + 4] * inv, acc[8 * q4 + 5] * inv),
+                     pack_bf16x2(acc[8 * q4 + 6] * inv, acc[8 * q4 + 7] * inv));
   }
   // ---- o[16 x 128] = As[16 x 512] @ W_UV[512 x 128]; wave w owns columns [32w, 32w + 32)
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
