@@ -267,7 +267,7 @@ struct AttnArgs {
   const int32_t* info;  // per share: first sequence, number of sub-tiles
   int B;
   float scale_log2;
-  bf16_t* part_o;  // [(G + B)][H][Lkv]  latent output of a share, normalised by its own sum
+  bf16_t* part_o;  // [(G + B)][Lkv/64][H][64]  latent output of a share, normalised by its own sum
   float* part_ml;  // [(G + B)][H][2]    (running max in log2 units, sum)
 };
 
@@ -448,20 +448,51 @@ __device__ __forceinline__ void value_product(const char* bbase, const LaneOffse
   }
 }
 
+// Writes this wave's partial result (16 heads x 512 latents, normalised by l_run) as rows of
+// 64 latents: lane (g, j) holds latents 16mt + 4g .. + 3 of head j; each quarter of 64 latents
+// (tiles 4q .. 4q + 3) goes through the wave's LDS stage (row = head, 128 bytes; the 16-byte
+// chunk c of row r at slot 8r + (c ^ (r & 7))) and out as two 1 KB stores of eight whole rows.
+__device__ __forceinline__ void store_partial(bf16_t* part_o, size_t ps, int w, int lane, float l_run,
+                                              const f32x4 (&o)[kLkv / 16], uint4* __restrict__ st) {
+  int l = lane;
+  asm volatile("" : "+v"(l));  // keeps the address arithmetic here, out of the main loop
+  const int g = l >> 4, j = l & 15, hh = l >> 3, k = l & 7;
+  const float inv_l = 1.f / l_run;
+  char* stb = (char*)st;
+#pragma unroll
+  for (int q = 0; q < kLkv / 64; ++q) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int mt = 4 * q + t, c = 2 * t + (g >> 1);
+      *(uint2*)(stb + (8 * j + (c ^ (j & 7))) * 16 + 8 * (g & 1)) =
+          make_uint2(pack_bf16x2(o[mt][0] * inv_l, o[mt][1] * inv_l), pack_bf16x2(o[mt][2] * inv_l, o[mt][3] * inv_l));
+    }
+    const uint4 v0 = st[8 * hh + (k ^ (hh & 7))];
+    const uint4 v1 = st[8 * (8 + hh) + (k ^ (hh & 7))];
+    bf16_t* dq = part_o + ((ps * (kLkv / 64) + q) * kH + 16 * w) * 64 + 8 * k;
+    *(uint4*)(dq + 64 * hh) = v0;
+    *(uint4*)(dq + 64 * (8 + hh)) = v1;
+  }
+}
+
 // One step: the copies of a later sub-tile go into `nxt`; then, when `compute` is set, this
-// wave takes sub-tile `cur` (tokens from tok0): scores, softmax and value product.  Both
+// wave takes sub-tile `cur` (tokens from tok0): scores, softmax and value product, and when
+// `last` is set it writes the partial result of the sequence (pair slot ps) through `st`.  The
 // buffers are restrict-qualified so that, once inlined, the copies into `nxt` carry alias
-// scopes disjoint from the reads of `cur`; every copy is issued by this one inlined call
-// site, so the compiler never makes the score/value reads wait for copies in flight.
+// scopes disjoint from the reads of `cur` and the accesses of `st`; every copy is issued by
+// this one inlined call site, so the compiler never makes those LDS accesses wait for copies
+// in flight.
 __device__ __forceinline__ void attn_step(const AttnArgs& A, int tok0, int tok_hi, bool copy, int blk_pf, int tok_pf,
                                           int tok_hi_pf, bool compute, const uint4* __restrict__ cur,
                                           uint4* __restrict__ nxt, const LaneOffsets& LO, const bf16x8 (&qf)[kR / 32],
-                                          f32x4 (&o)[kLkv / 16], float& m_run, float& l_run, int w, int lane) {
+                                          f32x4 (&o)[kLkv / 16], float& m_run, float& l_run, int w, int lane,
+                                          bool last, size_t ps, uint4* __restrict__ st) {
   if (copy) issue_tile_copy(A, blk_pf, tok_pf, tok_hi_pf, nxt, w, lane);
   if (!compute) return;
   bf16x8 vring[kVPre];
   const bf16x8 pb = scores_softmax(A, tok0, tok_hi, (const char*)cur, LO, qf, o, m_run, l_run, vring, lane);
   value_product((const char*)cur, LO, pb, o, vring);
+  if (last) store_partial(A.part_o, ps, w, lane, l_run, o, st);
 }
 
 constexpr int kPf = 3;  // sub-tiles whose copies are issued ahead of the one being computed
@@ -484,9 +515,14 @@ __device__ __forceinline__ bool share_of(const AttnArgs& A, int b, int t_lo, int
 }
 
 // Moves c to the first sub-tile of the next non-empty sequence of the share (b = B when none).
+// The walk stops at the first sequence that starts at or past the share's end, so that the
+// end of a share costs one probe rather than a walk over the rest of the batch.
 __device__ __forceinline__ void next_segment(const AttnArgs& A, int t_lo, int t_hi, Cursor& c) {
-  for (++c.b; c.b < A.B; ++c.b)
+  for (++c.b; c.b < A.B; ++c.b) {
+    if (sload(A.P + c.b) >= t_hi) break;
     if (share_of(A, c.b, t_lo, t_hi, &c.tok, &c.tok_hi)) return;
+  }
+  c.b = A.B;
 }
 
 __device__ __forceinline__ void advance(const AttnArgs& A, int t_lo, int t_hi, Cursor& c) {
@@ -500,6 +536,8 @@ __device__ __forceinline__ void advance(const AttnArgs& A, int t_lo, int t_hi, C
 // finished sequence's partial result is written and the next sequence's query loaded.
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void decode_attn_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) uint4 kv[kNBuf][kBufSlots];
+  // per wave: 16 heads x 64 latents of a partial result on its way out (the rest of the LDS)
+  __shared__ __attribute__((aligned(16))) uint4 stage[kAttnWaves][16 * 8];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = sload(A.P + A.B);
@@ -539,22 +577,18 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void decode_attn_kernel(AttnArg
       wait_copies(w, min(total - 1 - s, kPf - 1));
       lds_barrier();
     }
+    const bool last = s >= 0 && cc.tok + kSub >= cc.tok_hi;  // last sub-tile of sequence cc.b
     attn_step(A, cc.tok, cc.tok_hi, copy, blk_pf, pc.tok, pc.tok_hi, s >= 0, kv[s < 0 ? 0 : s % kNBuf],
-              kv[(s + kPf + kNBuf) % kNBuf], LO, qf, o, m_run, l_run, w, lane);
+              kv[(s + kPf + kNBuf) % kNBuf], LO, qf, o, m_run, l_run, w, lane, last, (size_t)wg + cc.b, stage[w]);
     if (copy) advance(A, t_lo, t_hi, pc);
     if (s < 0) continue;
     if (cc.tok + kSub < cc.tok_hi) {
       cc.tok += kSub;
       continue;
     }
-    // ---- last sub-tile of sequence cc.b: its partial result, normalised by its own sum
+    // ---- last sub-tile of sequence cc.b: its partial result went out in the step; the
+    // running max and sum follow
     const size_t ps = (size_t)wg + cc.b;
-    bf16_t* dst = A.part_o + (ps * kH + head) * kLkv + 4 * g;
-    const float inv_l = 1.f / l_run;
-#pragma unroll
-    for (int mt = 0; mt < kLkv / 16; ++mt)
-      *(uint2*)(dst + 16 * mt) = make_uint2(pack_bf16x2(o[mt][0] * inv_l, o[mt][1] * inv_l),
-                                            pack_bf16x2(o[mt][2] * inv_l, o[mt][3] * inv_l));
     if (g == 0) *(float2*)(A.part_ml + (ps * kH + head) * 2) = make_float2(m_run, l_run);
     next_segment(A, t_lo, t_hi, cc);
     if (cc.b >= A.B) break;
@@ -620,10 +654,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
       for (int u = 0; u < 2; ++u) {
         const int wq = wq0 + u;
         ok[u] = wq <= wl && wg_nonempty(wq, N);
-        const size_t ps = ((size_t)(ok[u] ? wq : wf) + b) * kH + h;
+        const size_t pp = (size_t)(ok[u] ? wq : wf) + b;
+        const size_t ps = pp * kH + h;
+        // latents 32j .. 32j + 31 of head h: half (j & 1) of row h in quarter j / 2
+        const size_t pq = ((pp * (kLkv / 64) + (j >> 1)) * kH + h) * 64 + 32 * (j & 1);
         ml[u] = *(const float2*)(part_ml + ps * 2);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) v[u][q4] = *(const uint4*)(part_o + ps * kLkv + 32 * j + 8 * q4);
+        for (int q4 = 0; q4 < 4; ++q4) v[u][q4] = *(const uint4*)(part_o + pq + 8 * q4);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
