@@ -267,7 +267,7 @@ struct AttnArgs {
   const int32_t* info;  // per share: first sequence, number of sub-tiles
   int B;
   float scale_log2;
-  bf16_t* part_o;  // [(G + B)][Lkv/64][H][64]  latent output of a share, normalised by its own sum
+  bf16_t* part_o;  // [(G + B)][H/16][Lkv/64][16][64]  latent output of a share, normalised by its own sum
   float* part_ml;  // [(G + B)][H][2]    (running max in log2 units, sum)
 };
 
@@ -449,7 +449,8 @@ __device__ __forceinline__ void value_product(const char* bbase, const LaneOffse
 }
 
 // Writes this wave's partial result (16 heads x 512 latents, normalised by l_run) as rows of
-// 64 latents: lane (g, j) holds latents 16mt + 4g .. + 3 of head j; each quarter of 64 latents
+// 64 latents, the wave's 16 heads contiguous per quarter (part_o layout [pair][head group]
+// [quarter][16][64]): lane (g, j) holds latents 16mt + 4g .. + 3 of head j; each quarter
 // (tiles 4q .. 4q + 3) goes through the wave's LDS stage (row = head, 128 bytes; the 16-byte
 // chunk c of row r at slot 8r + (c ^ (r & 7))) and out as two 1 KB stores of eight whole rows.
 __device__ __forceinline__ void store_partial(bf16_t* part_o, size_t ps, int w, int lane, float l_run,
@@ -469,7 +470,7 @@ __device__ __forceinline__ void store_partial(bf16_t* part_o, size_t ps, int w, 
     }
     const uint4 v0 = st[8 * hh + (k ^ (hh & 7))];
     const uint4 v1 = st[8 * (8 + hh) + (k ^ (hh & 7))];
-    bf16_t* dq = part_o + ((ps * (kLkv / 64) + q) * kH + 16 * w) * 64 + 8 * k;
+    bf16_t* dq = part_o + ((ps * (kH / 16) + w) * (kLkv / 64) + q) * 16 * 64 + 8 * k;
     *(uint4*)(dq + 64 * hh) = v0;
     *(uint4*)(dq + 64 * (8 + hh)) = v1;
   }
@@ -656,8 +657,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
         ok[u] = wq <= wl && wg_nonempty(wq, N);
         const size_t pp = (size_t)(ok[u] ? wq : wf) + b;
         const size_t ps = pp * kH + h;
-        // latents 32j .. 32j + 31 of head h: half (j & 1) of row h in quarter j / 2
-        const size_t pq = ((pp * (kLkv / 64) + (j >> 1)) * kH + h) * 64 + 32 * (j & 1);
+        // latents 32j .. 32j + 31 of head h: half (j & 1) of its row in quarter j / 2
+        const size_t pq = (((pp * (kH / 16) + (h >> 4)) * (kLkv / 64) + (j >> 1)) * 16 + (h & 15)) * 64 + 32 * (j & 1);
         ml[u] = *(const float2*)(part_ml + ps * 2);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) v[u][q4] = *(const uint4*)(part_o + pq + 8 * q4);

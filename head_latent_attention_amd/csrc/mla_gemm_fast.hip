@@ -58,6 +58,63 @@ struct EpiArgs {
   int H, dn, dr, dv;
 };
 
+// Epilogue of the BM x 128 tile kernels (4 waves; acc[mt][nt][i] is tile row
+// wm*(BM/WM) + 16*mt + 4*g + i, column wn*(128/WN) + 16*nt + j).
+template <int BM, int WM, int WN>
+__device__ __forceinline__ void small_epilogue(const EpiArgs& E, f32x4 (&acc)[BM / WM / 16][BN / WN / 16], float* C,
+                                               int64_t ldc, int M, int N, int m0, int n0, int wm, int wn, int lane) {
+  using G = Gemm<BM, WM, WN, W_BF16>;
+  const int g = lane >> 4, j = lane & 15;
+  const int wcol0 = wn * (BN / WN);
+  if (E.kind == GemmEpilogue::PARTIALS) {
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * (BM / WM) + 16 * mt + 4 * g + i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt) {
+          const int n = n0 + wcol0 + 16 * nt + j;
+          if (n < N) C[(int64_t)m * ldc + n] = acc[mt][nt][i];
+        }
+      }
+    return;
+  }
+  // consumers: column n of the lane (j) and its RoPE partner n ^ 1 (lane j ^ 1, same rows)
+  const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const int n = n0 + wcol0 + 16 * nt + j;
+    int h = 0, u = 0;
+    if (E.kind == GemmEpilogue::QUERY) { h = n / dqk; u = n - h * dqk; }
+    if (E.kind == GemmEpilogue::KV) { h = n / dkv; u = n - h * dkv; }
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * (BM / WM) + 16 * mt + 4 * g + i;
+        const float x = acc[mt][nt][i];
+        const float other = __shfl_xor(x, 1);  // every lane takes part
+        if (m >= M || n >= N) continue;
+        if (E.kind == GemmEpilogue::STORE) {
+          E.y[(int64_t)m * N + n] = f32_to_bf16(x);
+        } else if (E.kind == GemmEpilogue::QUERY) {
+          float yv = x;
+          if (u >= E.dn) {
+            const int p = (u - E.dn) >> 1;
+            const float c = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
+            yv = (u - E.dn) & 1 ? other * sn + x * c : x * c - other * sn;
+          }
+          E.y[(int64_t)m * N + n] = f32_to_bf16(yv);
+        } else {
+          if (u < E.dn) E.y[((int64_t)m * E.H + h) * dqk + u] = f32_to_bf16(x);
+          else E.y2[((int64_t)m * E.H + h) * E.dv + (u - E.dn)] = f32_to_bf16(x);
+        }
+      }
+  }
+}
+
 template <int BM, int WM, int WN, int WK>
 __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda, WeightView W0,
                                                    WeightView W1, int n_split, float* __restrict__ C, int64_t ldc,
@@ -184,53 +241,151 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
     __syncthreads();
     cur ^= 1;
   }
+  small_epilogue<BM, WM, WN>(E, acc, C, ldc, M, N, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode variant (M <= 64, bf16 weights): the 64 x 128 tile and 4-wave layout of gemm_kernel, but
+// the K steps are copied global->LDS by buffer_load ... lds three stages deep (two steps in
+// flight while one is multiplied), so that the weight stream of a workgroup is not one load
+// latency per step.  Each K range must be a whole number of 64-wide steps.
+constexpr int kDecStages = 3;
+constexpr int kDecCopies = 6;  // per wave per step: 2 activation + 4 weight copies of 1 KB
+
+struct DecArgs {
+  const bf16_t* A;
+  int64_t lda;
+  WeightView W0, W1;
+  int n_split;
+  float* C;
+  int64_t ldc;
+  int M, N, K;
+  int k_split;
+  int64_t split_stride;
+};
+
+// Copies of K step k0 into one stage (A: [64][8 chunks], W: [64][16 chunks], swizzled as
+// a_slot / w_slot, so each lane fetches the global chunk that belongs at its LDS slot).  Rows
+// past M and columns past the segment are clamped to valid memory; they only feed outputs
+// that are not stored.
+__device__ __forceinline__ void dec_issue(const DecArgs& G, const WeightView& W, int wn0, int wn_end, int k0,
+                                          uint4* __restrict__ as, uint4* __restrict__ ws, int w, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = 64 * (2 * w + i) + l, r = e >> 3, c = (e & 7) ^ ((r >> 1) & 7);
+    const int m = min(r, G.M - 1);
+    dma16_buf(G.A + k0, 0x7FFFFFF0u, (uint32_t)((m * G.lda + 8 * c) * 2), as + 64 * (2 * w + i));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 64 * (4 * w + i) + l, kr = e >> 4, c = (e & 15) ^ (((kr & 3) << 1) ^ (((kr >> 3) & 1) << 3));
+    const int n = min(wn0 + 8 * c, wn_end - 8);
+    dma16_buf((const bf16_t*)W.w + (int64_t)k0 * W.ld, 0x7FFFFFF0u, (uint32_t)((kr * W.ld + n) * 2),
+              ws + 64 * (4 * w + i));
+  }
+}
+
+// One step: copies of a later step into (as_nx, ws_nx), then the matrix ops of the step in
+// (as, ws).  All LDS accesses of the loop are made here through restrict-qualified pointers,
+// so the operand reads never wait for the copies in flight.
+__device__ __forceinline__ void dec_step(const DecArgs& G, const WeightView& W, int wn0, int wn_end, bool copy, int k_pf,
+                                         bool compute, const uint4* __restrict__ as, const uint4* __restrict__ ws,
+                                         uint4* __restrict__ as_nx, uint4* __restrict__ ws_nx, f32x4 (&acc)[4][2],
+                                         int w, int lane) {
+  if (copy) dec_issue(G, W, wn0, wn_end, k_pf, as_nx, ws_nx, w, lane);
+  if (!compute) return;
+  const int g = lane >> 4, j = lane & 15;
+  const char* wsb = (const char*)ws;
+#pragma unroll
+  for (int ks = 0; ks < BK / 32; ++ks) {
+    bf16x8 af[4], bfr[2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) af[mt] = as_bf16x8(as[a_slot(16 * mt + j, 4 * ks + g)]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int col = 32 * w + 16 * nt + 4 * (j & 3);
+      const int c = col >> 3, byte_in = (col & 7) * 2;
+      const int k = 32 * ks + 8 * g + (j >> 2);
+      const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k, c) * 16 + byte_in));
+      const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k + 4, c) * 16 + byte_in));
+      bfr[nt] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs G, EpiArgs E) {
+  __shared__ __attribute__((aligned(16))) uint4 As[kDecStages][64 * 8];
+  __shared__ __attribute__((aligned(16))) uint4 Ws[kDecStages][BK * 16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * BN;
+  const bool seg1 = n0 >= G.n_split;
+  const WeightView W = seg1 ? G.W1 : G.W0;
+  const int wn0 = seg1 ? n0 - G.n_split : n0, wn_end = seg1 ? G.N - G.n_split : G.n_split;
+  const int kbeg = blockIdx.z * G.k_split;
+  const int nsteps = (min(G.K, kbeg + G.k_split) - kbeg) / BK;
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = -(kDecStages - 1); s < nsteps; ++s) {
+    if (s >= 0) {
+      // copies issued after step s's: those of the next step, if any
+      if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F70 | kDecCopies);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      lds_barrier();
+    }
+    const int s_pf = s + kDecStages - 1;
+    const int b_pf = (s_pf + kDecStages) % kDecStages, b_cur = s < 0 ? 0 : s % kDecStages;
+    // opaque copies of the stage pointers keep the restrict scopes of dec_step's parameters
+    typedef __attribute__((address_space(3))) uint4 lds_uint4;
+    lds_uint4 *a_cur = (lds_uint4*)As[b_cur], *w_cur = (lds_uint4*)Ws[b_cur];
+    lds_uint4 *a_nx = (lds_uint4*)As[b_pf], *w_nx = (lds_uint4*)Ws[b_pf];
+    asm volatile("" : "+s"(a_cur), "+s"(w_cur), "+s"(a_nx), "+s"(w_nx));
+    dec_step(G, W, wn0, wn_end, s_pf < nsteps, kbeg + s_pf * BK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
+             (uint4*)a_nx, (uint4*)w_nx, acc, w, lane);
+  }
   if (E.kind == GemmEpilogue::PARTIALS) {
+    // the fp32 tile through the idle stage buffers (rows of 128 floats padded to 132), so that
+    // every store is 16 bytes and every wave writes two whole 512-byte rows at a time
+    lds_barrier();  // every wave is done with the last step's operands
+    float* st = (float*)&Ws[0][0];
+    static_assert(sizeof(Ws) >= 64 * 132 * 4, "the weight stages hold the tile");
+    const int g = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * (BM / WM) + 16 * mt + 4 * g + i;
-        if (m >= M) continue;
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < G::NT; ++nt) {
-          const int n = n0 + wcol0 + 16 * nt + j;
-          if (n < N) C[(int64_t)m * ldc + n] = acc[mt][nt][i];
-        }
-      }
+        for (int i = 0; i < 4; ++i) st[(16 * mt + 4 * g + i) * 132 + 32 * w + 16 * nt + j] = acc[mt][nt][i];
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    lds_barrier();
+    float* C = G.C + (int64_t)blockIdx.z * G.split_stride;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int e = it * 256 + tid, r = e >> 5, c4 = e & 31;
+      const int n = n0 + 4 * c4;
+      if (r < G.M && n < G.N) *(float4*)&C[(int64_t)r * G.ldc + n] = *(const float4*)&st[r * 132 + 4 * c4];
+    }
     return;
   }
-  // consumers: column n of the lane (j) and its RoPE partner n ^ 1 (lane j ^ 1, same rows)
-  const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
-#pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) {
-    const int n = n0 + wcol0 + 16 * nt + j;
-    int h = 0, u = 0;
-    if (E.kind == GemmEpilogue::QUERY) { h = n / dqk; u = n - h * dqk; }
-    if (E.kind == GemmEpilogue::KV) { h = n / dkv; u = n - h * dkv; }
-#pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * (BM / WM) + 16 * mt + 4 * g + i;
-        const float x = acc[mt][nt][i];
-        const float other = __shfl_xor(x, 1);  // every lane takes part
-        if (m >= M || n >= N) continue;
-        if (E.kind == GemmEpilogue::STORE) {
-          E.y[(int64_t)m * N + n] = f32_to_bf16(x);
-        } else if (E.kind == GemmEpilogue::QUERY) {
-          float yv = x;
-          if (u >= E.dn) {
-            const int p = (u - E.dn) >> 1;
-            const float c = E.cosT[(int64_t)m * half + p], sn = E.sinT[(int64_t)m * half + p];
-            yv = (u - E.dn) & 1 ? other * sn + x * c : x * c - other * sn;
-          }
-          E.y[(int64_t)m * N + n] = f32_to_bf16(yv);
-        } else {
-          if (u < E.dn) E.y[((int64_t)m * E.H + h) * dqk + u] = f32_to_bf16(x);
-          else E.y2[((int64_t)m * E.H + h) * E.dv + (u - E.dn)] = f32_to_bf16(x);
-        }
-      }
-  }
+  small_epilogue<64, 1, 4>(E, acc, G.C + (int64_t)blockIdx.z * G.split_stride, G.ldc, G.M, G.N, 0, n0, 0, w, lane);
+}
+
+bool dec_ok(const Dims& d, int M, int N, int K, int k_split, int n_split, int64_t lda, const float* C, int64_t ldc,
+            int64_t split_stride) {
+  // every K range a whole number of steps; byte offsets of a step fit 32 bits
+  return d.wk == W_BF16 && M <= 64 && K % BK == 0 && k_split % BK == 0 && N % 8 == 0 && ldc % 4 == 0 &&
+         split_stride % 4 == 0 && ((uintptr_t)C & 15) == 0 &&
+         (n_split >= N || (n_split % BN == 0 && (N - n_split) % 8 == 0)) && (int64_t)64 * lda * 2 < 0x7FFFFFF0LL;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -492,6 +647,11 @@ hipError_t launch(const Dims& d, const void* A, int64_t lda, const WeightView& W
                   float* C, int64_t ldc, int M, int N, int K, int k_split, int splits, int64_t split_stride,
                   const EpiArgs& E, hipStream_t s) {
   dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, splits);
+  if (BM == 64 && dec_ok(d, M, N, K, k_split, n_split, lda, C, ldc, split_stride)) {
+    DecArgs G{(const bf16_t*)A, lda, W0, W1, n_split, C, ldc, M, N, K, k_split, split_stride};
+    gemm_dec_kernel<<<grid, 256, 0, s>>>(G, E);
+    return hipGetLastError();
+  }
   if (d.wk == W_FP8)
     gemm_kernel<BM, WM, WN, W_FP8><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, W0, W1, n_split, C, ldc, M, N, K,
                                                         k_split, split_stride, E);
