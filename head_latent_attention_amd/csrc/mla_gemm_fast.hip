@@ -634,9 +634,11 @@ Plan plan(int M, int N, int K) {
   }
   p.bm = M <= 64 ? 64 : 128;
   const int tiles = ((N + BN - 1) / BN) * ((M + p.bm - 1) / p.bm);
-  int splits = 1;
-  // skinny shapes: spread K over more workgroups until every CU has one, keeping >= 256 k per split
-  while (tiles * splits < 256 && K / (splits * 2) >= 256) splits *= 2;
+  // skinny shapes: spread K over as many workgroups as there are CUs, one each (a workgroup that
+  // streams a longer K range beats two sharing a CU, and fewer splits mean fewer partial sums),
+  // keeping >= 128 k per split; with one split the consumer's epilogue runs in the GEMM itself
+  int splits = max(1, 256 / tiles);
+  while (splits > 1 && K / splits < 128) --splits;
   p.k_split = ((K + splits - 1) / splits + BK - 1) / BK * BK;
   p.splits = (K + p.k_split - 1) / p.k_split;
   return p;
