@@ -320,6 +320,73 @@ __device__ __forceinline__ void dec_step(const DecArgs& G, const WeightView& W, 
   }
 }
 
+// bf16 epilogue of the 64 x 128 decode tile (STORE, or QUERY with RoPE on the query's rope
+// columns): the tile is staged in LDS (`st`, 16 KB of idle stage buffers; 256-byte rows of
+// 16-byte chunks, chunk c of row r at slot 16r + (c ^ (r & 15))) so that every global store is
+// a whole 16-byte chunk of 8 columns.  acc[mt][nt][i] is tile row 16mt + 4g + i, column
+// 32w + 16nt + j; the cos/sin of a lane's 16 rows are all loaded before the first use, and the
+// pair partner of a rope column sits in lane j ^ 1.
+__device__ __forceinline__ void dec_store_epilogue(const EpiArgs& E, f32x4 (&acc)[4][2], bf16_t* st, int M, int N,
+                                                   int n0, int w, int lane) {
+  const int tid = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const int dqk = E.dn + E.dr, half = E.dr >> 1;
+  auto chunk_of = [](int r, int c) { return 16 * r + (c ^ (r & 15)); };
+  const bool query = E.kind == GemmEpilogue::QUERY;
+  lds_barrier();  // every wave is done with the stage buffers
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int c = 32 * w + 16 * nt + j;
+    const int u = (n0 + c) % dqk;
+    const bool rope = query && u >= E.dn, odd = (u - E.dn) & 1;
+    const int p = (u - E.dn) >> 1;
+    float cs[4][4], sn[4][4];
+    if (rope) {
+      const uint32_t tbytes = (uint32_t)min((int64_t)M * half * 4, (int64_t)0x7FFFFFF0);
+      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)E.cosT, 0, (int)tbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)E.sinT, 0, (int)tbytes, 0x00020000);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t off = (uint32_t)((min(16 * mt + 4 * g + i, M - 1) * half + p) * 4);
+          cs[mt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0));
+          sn[mt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] = acc[mt][nt][i];
+        if (query) {
+          const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[i]), 0xB1, 0xF, 0xF, true));
+          if (rope) y[i] = odd ? other * sn[mt][i] + y[i] * cs[mt][i] : y[i] * cs[mt][i] - other * sn[mt][i];
+        }
+      }
+      // lanes j and j ^ 1 hold columns c and c ^ 1 of the same 4 rows: swapping one value per row
+      // pair gives the even lane both columns of row i, the odd lane both of row i + 1
+      const int c0 = c & ~1;
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float send = (j & 1) ? y[i] : y[i + 1];
+        const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+        const int r = 16 * mt + 4 * g + i + (j & 1);
+        const uint32_t pk = (j & 1) ? pack_bf16x2(recv, y[i + 1]) : pack_bf16x2(y[i], recv);
+        *(uint32_t*)&st[chunk_of(r, c0 >> 3) * 8 + (c0 & 7)] = pk;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's part of the tile is in LDS
+  lds_barrier();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int e = it * 256 + tid, r = e >> 4, c8 = e & 15;
+    const int n = n0 + 8 * c8;
+    if (r < M && n < N) *(uint4*)&E.y[(int64_t)r * N + n] = *(const uint4*)&st[chunk_of(r, c8) * 8];
+  }
+}
+
 __global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs G, EpiArgs E) {
   __shared__ __attribute__((aligned(16))) uint4 As[kDecStages][64 * 8];
   __shared__ __attribute__((aligned(16))) uint4 Ws[kDecStages][BK * 16];
@@ -375,6 +442,10 @@ __global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs G, EpiArgs E) {
       const int n = n0 + 4 * c4;
       if (r < G.M && n < G.N) *(float4*)&C[(int64_t)r * G.ldc + n] = *(const float4*)&st[r * 132 + 4 * c4];
     }
+    return;
+  }
+  if (E.kind == GemmEpilogue::STORE || E.kind == GemmEpilogue::QUERY) {
+    dec_store_epilogue(E, acc, (bf16_t*)&Ws[0][0], G.M, G.N, n0, w, lane);
     return;
   }
   small_epilogue<64, 1, 4>(E, acc, G.C + (int64_t)blockIdx.z * G.split_stride, G.ldc, G.M, G.N, 0, n0, 0, w, lane);
