@@ -177,6 +177,52 @@ def test_decode_attn_absorbed(w):
     assert_close(torch_io.to_f64(o)[bs_], ref, s.act, f"o (sequences {bs_.tolist()})")
 
 
+# Many short sequences: several whole sequences inside one attention workgroup's share of the
+# 64-token tile list (so partial results are written and queries reloaded several times per
+# workgroup), and more sequences than the planner keeps in LDS (its global-memory path).
+SHORT_MANY = synth.custom(W[3], 107, "short-many-h128", B=700, ctx_lo=1, ctx_hi=150)
+SHORT_HUGE_B = synth.custom(W[3], 108, "short-b2100-h128", B=2100, ctx_lo=1, ctx_hi=40)
+ATTN_SHARES = 256  # workgroups of the decode attention: the tile list is cut into this many shares
+
+
+def _share_sample(ctx, n_pick=10):
+    """Sequences at interesting places of the share split: the first and last, ones a share
+    boundary cuts, and ones that share a workgroup with other whole sequences."""
+    tiles = -(-ctx.astype(np.int64) // 64)
+    P = np.concatenate([[0], np.cumsum(tiles)])
+    N = int(P[-1])
+    bounds = [(r * N) // ATTN_SHARES for r in range(ATTN_SHARES + 1)]
+    cut = [b for b in range(len(ctx)) if any(P[b] < x < P[b + 1] for x in bounds)]
+    share_of = np.searchsorted(bounds, P[:-1], side="right") - 1
+    crowded = [b for b in range(len(ctx)) if np.count_nonzero(share_of == share_of[b]) >= 3]
+    pick = {0, len(ctx) - 1} | set(cut[:n_pick // 2]) | set(crowded[:: max(1, len(crowded) // (n_pick // 2))][:n_pick // 2])
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("w", [SHORT_MANY, SHORT_HUGE_B], ids=lambda w: w.name)
+def test_decode_attn_many_short_sequences(w):
+    need_gpu()
+    import head_latent_attention_amd as mla
+    s = w.shape
+    print(f"[decode_attn_short] {w.name} B={w.B}", flush=True)
+    host, Wd, dw = _weights(w)
+    cfg = lib_config(s)
+    ctx = synth.context_lengths(w)
+    pg, cache = _paged_cache(w, ctx)
+    qh = synth.make_normal(w, "decode.q", (w.B, s.n_heads, s.qk_head), std=0.8)
+    o = torch_io.empty_act(s.act, (w.B, s.n_heads, s.v_dim))
+    mla.mla_decode_attn_absorbed(cfg, dw, torch_io.to_device(qh), cache, torch.from_numpy(pg.block_table).cuda(),
+                                 torch.from_numpy(ctx).cuda(), o)
+    torch.cuda.synchronize()
+    bs_ = _share_sample(ctx)
+    q64 = O.decode_tensor(s.act, qh.data)
+    seqs = [O.decode_tensor(s.act, synth.history_rows(w, int(b), int(ctx[b])).data) for b in bs_]
+    ref = O.decode_attention(Wd, q64[bs_], seqs, O.dims_of(s))
+    assert_close(torch_io.to_f64(o)[bs_], ref, s.act, f"o (sequences {bs_.tolist()})")
+    # every output is finite (a share's partial written to a wrong slot would leave garbage)
+    assert torch.isfinite(o.float()).all()
+
+
 # ----------------------------------------------------------------------------- output projection
 @pytest.mark.parametrize("w,M", [(SMALL_V3, 300), (EDGE_FP8, 7), (W[2], 4096), (W[3], 64), (W[4], 8192), (W[5], 256)],
                          ids=lambda c: str(c) if isinstance(c, int) else c.name)
