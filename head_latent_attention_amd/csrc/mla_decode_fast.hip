@@ -622,17 +622,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
   const int N = P[B];
   const int64_t col0 = (int64_t)h * (kDn + kDv) + kDn;
-  uint4 wr[kLkv / 128][8];
-#pragma unroll
-  for (int cc = 0; cc < kLkv / 128; ++cc)
+  // W_UV[h] in four chunks of 128 rows: the first loads ahead of the merge, each later one while
+  // the previous one is multiplied
+  uint4 wr[8];
+  auto load_chunk = [&](int cc) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
-      wr[cc][it] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
+      wr[it] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
     }
+  };
+  load_chunk(0);
   __builtin_amdgcn_sched_barrier(0);  // the weight loads stay ahead of the merge
   // ---- merge: the 16 lanes of quarter g of wave w handle local row 4w + g, each lane 32 latent
-  // columns, so the four rows of a wave run their shares side by side (two shares per round)
+  // columns, so the four rows of a wave run their shares side by side (four shares per round)
   {
     const int lb = 4 * w + g, b = b0 + lb;
     float acc[32];
@@ -647,12 +650,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
       }
     }
     float M = -INFINITY, L = 0.f;
-    for (int wq0 = wf; wq0 <= wl; wq0 += 2) {
-      float2 ml[2];
-      uint4 v[2][4];
-      bool ok[2];
+    for (int wq0 = wf; wq0 <= wl; wq0 += 4) {
+      float2 ml[4];
+      uint4 v[4][4];
+      bool ok[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 4; ++u) {
         const int wq = wq0 + u;
         ok[u] = wq <= wl && wg_nonempty(wq, N);
         const size_t pp = (size_t)(ok[u] ? wq : wf) + b;
@@ -664,7 +667,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
         for (int q4 = 0; q4 < 4; ++q4) v[u][q4] = *(const uint4*)(part_o + pq + 8 * q4);
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 4; ++u) {
         if (!ok[u]) continue;  // an empty share's slot was never written
         const float Mn = fmaxf(M, ml[u].x);
         const float sa = M == -INFINITY ? 0.f : exp2f(M - Mn);
@@ -698,9 +701,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
-      *(uint4*)&Ws[r][8 * ch] = wr[cc][it];
+      *(uint4*)&Ws[r][8 * ch] = wr[it];
     }
     __syncthreads();
+    if (cc + 1 < kLkv / 128) load_chunk(cc + 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 a = as_bf16x8(*(const uint4*)&As[j][128 * cc + 32 * ks + 8 * g]);
