@@ -10,9 +10,9 @@
 //            into the cache's latent space; atlas "Struct MlaWeights": w_uk_t).
 //   attn     split-context attention: the concatenated tile list is cut into 256
 //            equal shares, one workgroup each.  A workgroup streams its rows of
-//            [c_kv | k_pe] (576 bf16) into LDS once (direct global->LDS copies,
-//            double buffered) for all 128 heads and keeps an unnormalised latent
-//            output, running max and sum per head.
+//            [c_kv | k_pe] (576 bf16) into LDS once (direct global->LDS copies, three
+//            sub-tiles ahead in four rotating buffers) for all 128 heads and keeps an
+//            unnormalised latent output, running max and sum per head.
 //   combine  log-sum-exp merge of the shares of each sequence, then the value
 //            extraction o = o_lat @ W_UV[h] (atlas "Struct MlaWeights": w_uv).
 //
@@ -533,8 +533,9 @@ __device__ __forceinline__ void advance(const AttnArgs& A, int t_lo, int t_hi, C
 
 // 512 threads = 8 waves; wave w owns heads [16w, 16w + 16).  The workgroup's share of the
 // work list is one stream of 32-token sub-tiles across sequence boundaries: the copies run
-// kPf sub-tiles ahead of the computation without draining at a boundary, where the
-// finished sequence's partial result is written and the next sequence's query loaded.
+// kPf sub-tiles ahead of the computation, also into the next sequence; at a boundary the
+// finished sequence's partial result is written and the next sequence's query loaded (a
+// wait that also covers the copies in flight).
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void decode_attn_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) uint4 kv[kNBuf][kBufSlots];
   // per wave: 16 heads x 64 latents of a partial result on its way out (the rest of the LDS)
