@@ -9,7 +9,8 @@ resident in HBM before the timed region.  The JSON line also carries the V3
 causal prefill (8192 tokens) TFLOP/s, the latent-cache GB/s, the roofline of the
 dominant kernel (the absorbed decode attention) and the CPU oracle baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-chunk] [--no-fp8]
+                       [--no-decode-fp8] [--no-cpu] [--no-graph]
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def decode_setup(w, device="cuda"):
+def decode_setup(w, device="cuda", device_fill=False):
     import torch
     import synth
     from synth import torch_io
@@ -50,10 +51,21 @@ def decode_setup(w, device="cuda"):
     pg = synth.make_paging(w.number, ctx, s.block_size)
     cache = torch.empty((pg.n_blocks, 1, s.block_size, s.row), dtype=torch.bfloat16, device=device)
     flat = cache.view(-1, s.row)
-    for b, n in enumerate(ctx):
-        rows = torch_io.to_device(synth.history_rows(w, b, int(n)), device)
-        slots = synth.slots_for(pg.block_table[b], np.arange(int(n)), s.block_size).astype(np.int64)
-        flat[torch.from_numpy(slots).to(device)] = rows
+    if device_fill:
+        # large caches: rows of the history distribution (c ~ N(0,1), k_pe ~ N(0, (0.02 sqrt(hidden))^2))
+        # drawn on the device from one seeded generator instead of per-sequence host streams
+        gen = torch.Generator(device=device)
+        gen.manual_seed(1000 + w.number)
+        for r0 in range(0, flat.shape[0], 1 << 20):
+            blk = flat[r0:r0 + (1 << 20)]
+            vals = torch.randn(blk.shape, generator=gen, device=device, dtype=torch.float32)
+            vals[:, s.kv_lora_rank:] *= 0.02 * float(np.sqrt(s.hidden))
+            blk.copy_(vals.to(torch.bfloat16))
+    else:
+        for b, n in enumerate(ctx):
+            rows = torch_io.to_device(synth.history_rows(w, b, int(n)), device)
+            slots = synth.slots_for(pg.block_table[b], np.arange(int(n)), s.block_size).astype(np.int64)
+            flat[torch.from_numpy(slots).to(device)] = rows
     x = torch_io.to_device(synth.make_x(w, w.B, "x.decode"), device)
     slot = torch.from_numpy(synth.decode_slot_mapping(pg)).to(device)
     bt = torch.from_numpy(pg.block_table).to(device)
@@ -290,6 +302,36 @@ def cpu_baseline(w, S, budget_s=12.0):
                       f"{el:.1f} s of float64 numpy; time scaled by total rows to the full batch"}
 
 
+def run_decode_leg(w, steps, warmup, device_fill):
+    """Graph-replayed decode steps of workload w, plus an eager pass with events per entry point."""
+    import torch
+    S = decode_setup(w, device_fill=device_fill)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        decode_step(S)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        decode_step(S, evs[i])
+    torch.cuda.synchronize()
+    t_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        decode_step(S)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    s = w.shape
+    cache_b, attn_b = attn_algorithmic_bytes(s, S["ctx"], w.B)
+    return dict(ms_step=ms_step, t_attn=t_attn, cache_b=cache_b, attn_b=attn_b, ctx=S["ctx"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,6 +341,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-decode-fp8", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -412,6 +455,19 @@ def main():
                               "TFLOPs": round(p8["tflops"], 2),
                               "projection_TFLOPs": round(p8["proj_tflops"], 2),
                               "projection_frac_fp8_peak": round(p8["proj_tflops"] / FP8_PEAK_TFLOPS, 4)}
+    if not args.no_decode_fp8:
+        w5 = synth.WORKLOADS[5]
+        log(f"[bench] {w5.name}: V3 decode, fp8 weights, B={w5.B}")
+        d8 = run_decode_leg(w5, max(3, args.steps // 5), max(1, args.warmup // 2), device_fill=True)
+        s5 = w5.shape
+        step_b = d8["attn_b"] + weight_bytes(s5, ["wq_a", "wkv_a", "wq_b", "wo"])
+        out["decode_fp8"] = {"workload": f"{w5.name}: DeepSeek-V3-shaped MLA decode step, E4M3 weights (128x128 "
+                                         f"block scales), bf16 cache, B={w5.B}, ctx~logU[{w5.ctx_lo},{w5.ctx_hi}]",
+                             "tok_per_s": round(w5.B / (d8["ms_step"] * 1e-3), 2), "ms_per_step": round(d8["ms_step"], 4),
+                             "context_tokens": int(d8["ctx"].sum()), "ms_decode_attn": round(d8["t_attn"], 4),
+                             "latent_cache_GBps": round(d8["cache_b"] / (d8["t_attn"] * 1e-3) / 1e9, 1),
+                             "attn_frac_hbm_peak": round(d8["attn_b"] / (d8["t_attn"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "step_algorithmic_GBps": round(step_b / (d8["ms_step"] * 1e-3) / 1e9, 1)}
     if not args.no_chunk:
         prefix, T = 7168, 1024
         log(f"[bench] V3 chunked prefill, {T} tokens after {prefix}")
