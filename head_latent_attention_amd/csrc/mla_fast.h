@@ -36,6 +36,10 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
                      const WeightView& W1, int M, int N, int K, float* out, Partials* res,
                      const GemmEpilogue* epi, bool* fused, hipStream_t s);
 
+// Compute units of the current device (cached per device); persistent kernels size their
+// grids with it.  Any positive grid is correct for them, so a failed query returns 256.
+int device_cu_count();
+
 // Absorbed decode: fold, split-context attention over the paged cache, combine with W_UV.
 bool fast_decode_supported(const Dims& d);
 size_t fast_decode_ws_bytes(const Dims& d, int B, int max_context);

@@ -4,15 +4,24 @@
 // (NeMo "MLA" module: forward with a causal attention mask and softmax_scale).
 //
 // Flash-style: a workgroup owns 32*NW queries of one head and streams 64-key tiles
-// of K and V through three LDS buffers (direct global->LDS buffer copies, two tiles in
-// flight, one fence-free barrier per tile).  Each wave
+// of K and V through four LDS stages (direct global->LDS buffer copies, two tiles in
+// flight, fence-free barriers).  Each wave
 // keeps 32 queries: S^T = K Q^T with keys as the M dimension, so the softmax
 // probabilities are already in the B-operand layout of O^T = V^T P^T; V^T is read
 // with the transposing LDS read.  Online softmax in the log2 domain with a lazy
 // rescale (the running max only moves when a tile exceeds it by 2^8).
-// Workgroups are ordered heaviest first (latest query tiles) and grouped so that
-// the query tiles of one head run on one XCD and share its L2.
+// The kernel is persistent: one workgroup per CU walks a fixed list of (head, query
+// tile) items.  Workgroup w runs on XCD w mod 8 (the dispatcher deals workgroups to the
+// eight XCDs in turn), so heads h = x mod 8 are given to XCD x: its workgroups take that
+// XCD's items head by head, query tiles heaviest first, dealt in serpentine order (round r
+// takes items r*J .. r*J+J-1 of the XCD's list, reversed on odd rounds).  The workgroups'
+// totals even out, and an XCD streams the K/V tiles of one or two heads at a time, which
+// its L2 then serves to all of them.  Other grid or head counts use the same serpentine
+// over the whole (query tile, head) list.
 #include "mla_fast.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace mla {
 
@@ -28,7 +37,6 @@ constexpr int KC = DQK / 8, VC = DV / 8;   // 16-byte chunks per key / value row
 constexpr int KT = 64;                     // keys per tile
 constexpr int K_SLOTS = KT * KC, V_SLOTS = KT * VC;
 constexpr float kRescaleThreshold = 8.0f;
-constexpr int kXcds = 8;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -77,98 +85,189 @@ __device__ __forceinline__ void issue_kv_copy(const PrefillArgs& P, int h, int k
   }
 }
 
+constexpr int kRing = 6;  // LDS operand reads in flight per wave in the matrix block
+
+// Matrix block of one step for one wave: first this step's share of the K/V copies into the
+// stage kn/vn, then (pv) O^T += V^T P^T for the previous tile from its probabilities pb, and
+// (qk) S^T = K Q^T for the current tile.  Every LDS access of the step is issued here, through
+// restrict pointers, so that the compiler's waits on the copies stay per access.
 template <int NW>
-__device__ __forceinline__ void prefill_tile(const PrefillArgs& P, int h, int kt, bool copy, int kt_pf, bool compute,
-                                             int qw0, const uint4* __restrict__ kb, const uint4* __restrict__ vb,
-                                             uint4* __restrict__ kn, uint4* __restrict__ vn,
-                                             const bf16x8 (&qf)[2][DQK / 32], f32x4 (&o)[DV / 16][2],
-                                             float (&m_run)[2], float (&l_run)[2], const int (&kbase)[2],
-                                             const int (&vbase)[4], int w, int lane) {
-  const int g = lane >> 4, j = lane & 15;
+__device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, bool copy, int kt_pf, bool qk, bool pv,
+                                          const uint4* __restrict__ kb, const uint4* __restrict__ vb,
+                                          uint4* __restrict__ kn, uint4* __restrict__ vn,
+                                          const bf16x8 (&qf)[2][DQK / 32], f32x4 (&s)[4][2],
+                                          const bf16x8 (&pb)[2][2], f32x4 (&o)[DV / 16][2], const int (&kbase)[2],
+                                          const int (&vbase)[4], int w, int lane) {
   if (copy) issue_kv_copy<NW>(P, h, kt_pf, kn, vn, w, lane);
-  const int k0 = kt * KT;
-  if (compute && k0 <= qw0 + 31) {  // this wave has queries that see keys of the tile
-    // ---- S^T[key][query]
-    f32x4 s[4][2];
+  if (pv) {  // O^T[d][query] += V^T P^T; operand i = 8*kk + mt, kRing reads in flight
+    const char* vbb = (const char*)vb;
+    // keys 32*kk + {0,16} + 4*g + j/4 (same swizzle), chunk 2*mt + half = (2*mt) ^ half
+    auto v_op = [&](int i) {
+      const int kk = i >> 3, mt = i & 7;
+      const char* pa = vbb + vbase[0] + (VC * 32 * kk) * 16 + ((2 * mt) ^ vbase[1]) * 16;
+      const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
+      const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + VC * 16 * 16));
+      return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 ring[kRing];
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) ring[i] = v_op(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * DV / 16; ++i) {
+      const int kk = i >> 3, mt = i & 7;
+      const bf16x8 a = ring[i % kRing];
+      if (i + kRing < 2 * DV / 16) ring[i % kRing] = v_op(i + kRing);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nt][kk], o[mt][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // S is written on every path (zeros for a tile the wave does not see), so the previous
+  // tile's scores are dead during P V
+  if (qk) {  // S^T[key][query]; operand i = 4*ks + mt, kRing reads in flight
+    // slot KC*(16*mt + j) + ((4*ks + g) ^ k_swz(j)), lane part in kbase[ks & 1]
+    auto k_op = [&](int i) {
+      const int ks = i >> 2, mt = i & 3;
+      return as_bf16x8(*(const uint4*)((const char*)kb + kbase[ks & 1] + (KC * 16 * mt + 8 * (ks >> 1)) * 16));
+    };
+    bf16x8 ring[kRing];
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) ring[i] = k_op(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4 * DQK / 32; ++i) {
+      const int ks = i >> 2, mt = i & 3;
+      const bf16x8 a = ring[i % kRing];
+      if (i + kRing < 4 * DQK / 32) ring[i % kRing] = k_op(i + kRing);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nt][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Online softmax of one tile's scores (keys k0 .. k0+63) for the wave's 32 queries (lane's
+// query: qw0 + 16*nt + j): probabilities into pb (bf16, the B-operand layout of the value
+// product), running max and sum updated, O rescaled when the max moves.  Every query sees
+// key 0 in tile 0, so the running max is finite from the first tile on.  The max is taken
+// over the raw scores and scaled afterwards (the scale is positive).
+__device__ __forceinline__ void softmax_block(const PrefillArgs& P, int k0, int qw0, const f32x4 (&s)[4][2],
+                                              bf16x8 (&pb)[2][2], f32x4 (&o)[DV / 16][2], float (&m_run)[2],
+                                              float (&l_run)[2], int g, int j) {
+  const bool diag = k0 + KT - 1 > qw0;
 #pragma unroll
-    for (int ks = 0; ks < DQK / 32; ++ks) {
+  for (int nt = 0; nt < 2; ++nt) {
+    float x[4][4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        // slot KC*(16*mt + j) + ((4*ks + g) ^ k_swz(j)), lane part in kbase[ks & 1]
-        const bf16x8 a = as_bf16x8(*(const uint4*)((const char*)kb + kbase[ks & 1] + (KC * 16 * mt + 8 * (ks >> 1)) * 16));
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nt][ks], s[mt][nt], 0, 0, 0);
-      }
-    }
-    // ---- online softmax per query (lane's query: qw0 + 16*nt + j).  Every query sees key 0 in
-    // tile 0 (computed by every wave), so the running max is finite from the first tile on.
-    const bool diag = k0 + KT - 1 > qw0;
-    bf16x8 pb[2][2];  // [nt][kk]
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float x[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[mt][i] = s[mt][nt][i] * P.scale_log2;
-      if (diag) {  // causal mask inside the diagonal tiles only
-        const int qi = qw0 + 16 * nt + j;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (k0 + 16 * mt + 4 * g + i > qi) x[mt][i] = -INFINITY;
-      }
-      float mx = x[0][0];
+      for (int i = 0; i < 4; ++i) x[mt][i] = s[mt][nt][i];
+    if (diag) {  // causal mask inside the diagonal tiles only
+      const int qi = qw0 + 16 * nt + j;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[mt][i]);
-      mx = xmax16_32(mx);
-      const float m_new = (m_run[nt] == -INFINITY || mx > m_run[nt] + kRescaleThreshold) ? mx : m_run[nt];
-      const float corr = m_run[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-      float sum = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(x[2 * kk][i] - m_new);
-          p[4 + i] = __builtin_amdgcn_exp2f(x[2 * kk + 1][i] - m_new);
-          sum += p[i] + p[4 + i];
-        }
-        pb[nt][kk] = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
-      }
-      sum = xsum16_32(sum);
-      l_run[nt] = l_run[nt] * corr + sum;
-      m_run[nt] = m_new;
-      if (__any(corr != 1.f)) {
-#pragma unroll
-        for (int mt = 0; mt < DV / 16; ++mt) o[mt][nt] *= corr;
-      }
+        for (int i = 0; i < 4; ++i)
+          if (k0 + 16 * mt + 4 * g + i > qi) x[mt][i] = -INFINITY;
     }
-    // ---- O^T[d][query] += V^T P^T
-    const char* vbb = (const char*)vb;
+    float mx = x[0][0];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[mt][i]);
+    mx = xmax16_32(mx) * P.scale_log2;
+    const float m_new = (m_run[nt] == -INFINITY || mx > m_run[nt] + kRescaleThreshold) ? mx : m_run[nt];
+    const float corr = m_run[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+    float sum = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      float p[8];
 #pragma unroll
-      for (int mt = 0; mt < DV / 16; ++mt) {
-        // keys 32*kk + {0,16} + 4*g + j/4 (same swizzle), chunk 2*mt + half = (2*mt) ^ half
-        const char* pa = vbb + vbase[0] + (VC * 32 * kk) * 16 + ((2 * mt) ^ vbase[1]) * 16;
-        const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
-        const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + VC * 16 * 16));
-        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nt][kk], o[mt][nt], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk][i], P.scale_log2, -m_new));
+        p[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk + 1][i], P.scale_log2, -m_new));
+        sum += p[i] + p[4 + i];
       }
+      pb[nt][kk] = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+    }
+    sum = xsum16_32(sum);
+    l_run[nt] = l_run[nt] * corr + sum;
+    m_run[nt] = m_new;
+    if (__any(corr != 1.f)) {
+#pragma unroll
+      for (int mt = 0; mt < DV / 16; ++mt) o[mt][nt] *= corr;
     }
   }
 }
 
-constexpr int kStages = 3;  // K/V tiles in LDS: the current one and two in flight
+// Probabilities of a tile the wave does not see: written so that pb is dead between its use
+// in the matrix block and the next softmax.
+__device__ __forceinline__ void pb_clear(bf16x8 (&pb)[2][2]) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) pb[nt][0] = pb[nt][1] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+}
 
+// K/V tiles in LDS: tile t in stage t mod 4.  Step t reads K of tile t and V of tile t-1 and
+// copies tile t+2, into the stage of tile t-2, which step t-1 finished with.
+constexpr int kStages = 4;
+
+// Steps -2 .. n_kt of one item for a wave of group GRP (see prefill_attn_kernel).
+template <int NW, int GRP>
+__device__ __forceinline__ void item_steps(const PrefillArgs& P, int h, int n_kt, int qw0, uint4 (*kbuf)[K_SLOTS],
+                                           uint4 (*vbuf)[V_SLOTS], const bf16x8 (&qf)[2][DQK / 32],
+                                           f32x4 (&o)[DV / 16][2], float (&m_run)[2], float (&l_run)[2],
+                                           const int (&kbase)[2], const int (&vbase)[4], int w, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  f32x4 s[4][2];
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  pb_clear(pb);
+  constexpr int kCopies = (K_SLOTS + V_SLOTS) / 64 / NW;  // per wave per tile
+  typedef __attribute__((address_space(3))) uint4 lds_uint4;
+  // steps -2 and -1 only put tiles 0 and 1 in flight; step n_kt only adds P V of the last tile
+  for (int kt = -2; kt <= n_kt; ++kt) {
+    if (kt >= 0 && kt < n_kt) {
+      // copies issued after tile kt's: those of tile kt+1, if any
+      if (kt + 1 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70 | kCopies);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    lds_barrier();
+    const int kt_pf = kt + 2;
+    const bool copy = kt_pf < n_kt;
+    const bool qk = kt >= 0 && kt < n_kt && kt * KT <= qw0 + 31;    // this wave's queries see tile kt
+    const bool pv = kt >= 1 && (kt - 1) * KT <= qw0 + 31;           // ... and tile kt-1
+    // opaque copies of the stage pointers keep the restrict scopes of mma_block's parameters
+    lds_uint4 *kc = (lds_uint4*)kbuf[kt & 3], *vp = (lds_uint4*)vbuf[(kt + 3) & 3];
+    lds_uint4 *kn = (lds_uint4*)kbuf[kt_pf & 3], *vn = (lds_uint4*)vbuf[kt_pf & 3];
+    asm volatile("" : "+s"(kc), "+s"(vp), "+s"(kn), "+s"(vn));
+    if constexpr (GRP == 0) {
+      mma_block<NW>(P, h, copy, kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn, qf, s,
+                    pb, o, kbase, vbase, w, lane);
+      lds_barrier();
+      if (qk) softmax_block(P, kt * KT, qw0, s, pb, o, m_run, l_run, g, j);
+      else pb_clear(pb);
+    } else {
+      if (pv) softmax_block(P, (kt - 1) * KT, qw0, s, pb, o, m_run, l_run, g, j);
+      else pb_clear(pb);
+      lds_barrier();
+      mma_block<NW>(P, h, copy, kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn, qf, s,
+                    pb, o, kbase, vbase, w, lane);
+    }
+  }
+}
+
+// Two waves share each SIMD.  Every step has two phases separated by a barrier: in the first,
+// one wave of each pair (group 0) runs its matrix block while the other (group 1) runs its
+// softmax; in the second they swap.  Group 0's step t: matrix block (S of tile t, O += P V of
+// tile t-1), barrier, softmax of tile t.  Group 1's step t: softmax of tile t-1, barrier,
+// matrix block (S of tile t, O += P V of tile t-1).  So the matrix cores and the vector ALUs
+// of a SIMD work at the same time.
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P) {
   __shared__ __attribute__((aligned(16))) uint4 kbuf[kStages][K_SLOTS];
@@ -176,17 +275,17 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
   constexpr int BQ = 32 * NW;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // block -> (head, query tile): one XCD per group of heads, heaviest query tiles first
-  const int bid = blockIdx.x;
-  const int per_xcd = (P.H * P.n_qtiles + kXcds - 1) / kXcds;
-  const int lin = (bid % kXcds) * per_xcd + bid / kXcds;
-  if (lin >= P.H * P.n_qtiles) return;
-  const int h = lin / P.n_qtiles;
-  const int qt = P.n_qtiles - 1 - (lin - h * P.n_qtiles);
-  const int q0 = qt * BQ, qw0 = q0 + 32 * w;
-  const int q_last = min(P.T, q0 + BQ) - 1;
-  const int n_kt = q_last / KT + 1;
-
+  int grp;
+  {  // group: the wave's rank, mod 2, among the waves of this workgroup on its SIMD (HW_ID bits 5:4)
+    const int simd = (int)((__builtin_amdgcn_s_getreg(0x0904)) & 3);
+    int* ids = (int*)&kbuf[0][0];
+    if (lane == 0) ids[w] = simd;
+    __syncthreads();
+    int c = 0;
+    for (int v = 0; v < w; ++v) c += ids[v] == simd;
+    grp = __builtin_amdgcn_readfirstlane(c & 1);
+    __syncthreads();
+  }
   int kbase[2], vbase[4];
   {
     const int sj = k_swz(j);
@@ -197,56 +296,76 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
     vbase[1] = half ^ v_swz(tA);            // chunk XOR
     vbase[2] = vbase[3] = 0;
   }
-  bf16x8 qf[2][DQK / 32];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int qi = min(qw0 + 16 * nt + j, P.T - 1);
-    const bf16_t* qrow = P.q + ((int64_t)qi * P.H + h) * DQK + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < DQK / 32; ++ks) qf[nt][ks] = as_bf16x8(*(const uint4*)(qrow + 32 * ks));
-  }
-  f32x4 o[DV / 16][2];
-#pragma unroll
-  for (int mt = 0; mt < DV / 16; ++mt) o[mt][0] = o[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  // the query fragments are complete before the loop, so no read in it waits for the copies
-  __builtin_amdgcn_s_waitcnt(0);
-  constexpr int kCopies = (K_SLOTS + V_SLOTS) / 64 / NW;  // per wave per tile
-  typedef __attribute__((address_space(3))) uint4 lds_uint4;
-  // steps kt < 0 only put the first kStages - 1 tiles in flight
-  for (int kt = -(kStages - 1); kt < n_kt; ++kt) {
-    if (kt >= 0) {
-      // copies issued after tile kt's: those of the next min(kStages - 2, ...) tiles
-      if (kt + 1 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70 | kCopies);
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-      lds_barrier();
+  const bool by_xcd = (gridDim.x & 7) == 0 && (P.H & 7) == 0;
+  const int J = by_xcd ? (int)gridDim.x >> 3 : (int)gridDim.x;       // workgroups sharing one list
+  const int slot = by_xcd ? (int)blockIdx.x >> 3 : (int)blockIdx.x;  // this workgroup's place in it
+  const int n_list = by_xcd ? (P.H >> 3) * P.n_qtiles : P.H * P.n_qtiles;
+  for (int r = 0; r * J < n_list; ++r) {
+    const int m = r * J + ((r & 1) ? J - 1 - slot : slot);
+    if (m >= n_list) continue;
+    int h, qt;
+    if (by_xcd) {  // XCD list: heads x, x + 8, ... one after another, query tiles heaviest first
+      const int hi = m / P.n_qtiles;
+      h = 8 * hi + ((int)blockIdx.x & 7);
+      qt = P.n_qtiles - 1 - (m - hi * P.n_qtiles);
+    } else {       // whole list: query tiles heaviest first, heads within
+      h = m % P.H;
+      qt = P.n_qtiles - 1 - m / P.H;
     }
-    const int kt_pf = kt + kStages - 1;
-    const int b_pf = (kt_pf + kStages) % kStages, b_cur = kt < 0 ? 0 : kt % kStages;
-    // opaque copies of the buffer pointers keep the restrict scopes of prefill_tile's parameters
-    lds_uint4 *kc = (lds_uint4*)kbuf[b_cur], *vc = (lds_uint4*)vbuf[b_cur];
-    lds_uint4 *kn = (lds_uint4*)kbuf[b_pf], *vn = (lds_uint4*)vbuf[b_pf];
-    asm volatile("" : "+s"(kc), "+s"(vc), "+s"(kn), "+s"(vn));
-    prefill_tile<NW>(P, h, kt < 0 ? 0 : kt, kt_pf < n_kt, kt_pf, kt >= 0, qw0, (const uint4*)kc, (const uint4*)vc,
-                     (uint4*)kn, (uint4*)vn, qf, o, m_run, l_run, kbase, vbase, w, lane);
-  }
+    const int q0 = qt * BQ, qw0 = q0 + 32 * w;
+    const int q_last = min(P.T, q0 + BQ) - 1;
+    const int n_kt = q_last / KT + 1;
+    bf16x8 qf[2][DQK / 32];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int qi = qw0 + 16 * nt + j;
-    if (qi >= P.T) continue;
-    const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
-    bf16_t* dst = P.o + ((int64_t)qi * P.H + h) * DV + 4 * g;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int qi = min(qw0 + 16 * nt + j, P.T - 1);
+      const bf16_t* qrow = P.q + ((int64_t)qi * P.H + h) * DQK + 8 * g;
 #pragma unroll
-    for (int mt = 0; mt < DV / 16; ++mt) {
-      const f32x4 v = o[mt][nt] * inv;
-      *(uint2*)(dst + 16 * mt) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      for (int ks = 0; ks < DQK / 32; ++ks) qf[nt][ks] = as_bf16x8(*(const uint4*)(qrow + 32 * ks));
     }
+    f32x4 o[DV / 16][2];
+#pragma unroll
+    for (int mt = 0; mt < DV / 16; ++mt) o[mt][0] = o[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    // the query fragments are complete before the loop, so no read in it waits for the copies
+    __builtin_amdgcn_s_waitcnt(0);
+    // one loop per group, so that each has its own register liveness
+    if (grp == 0) item_steps<NW, 0>(P, h, n_kt, qw0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
+    else item_steps<NW, 1>(P, h, n_kt, qw0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int qi = qw0 + 16 * nt + j;
+      if (qi >= P.T) continue;
+      const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
+      bf16_t* dst = P.o + ((int64_t)qi * P.H + h) * DV + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < DV / 16; ++mt) {
+        const f32x4 v = o[mt][nt] * inv;
+        *(uint2*)(dst + 16 * mt) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+    // every wave is done with the last tiles' stages before the next item's copies refill them
+    lds_barrier();
   }
 }
 
 }  // namespace
 
-bool fast_prefill_attn_supported(const Dims& d) { return d.act == 1 && d.dn + d.dr == DQK && d.dv == DV; }
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+bool fast_prefill_attn_supported(const Dims& d) {
+  return d.act == 1 && d.dn + d.dr == DQK && d.dv == DV && d.scale > 0.f;
+}
 
 size_t fast_prefill_attn_ws_bytes(const Dims&, int) { return 0; }
 
@@ -265,7 +384,8 @@ hipError_t fast_prefill_attn(const Dims& d, const void* q, const void* k, const 
   const int BQ = big ? 256 : 128;
   P.n_qtiles = (T + BQ - 1) / BQ;
   const int total = d.H * P.n_qtiles;
-  const int grid = (total + kXcds - 1) / kXcds * kXcds;
+  // one workgroup per CU (the four K/V stages take all 160 KB of a CU's LDS)
+  const int grid = std::min(total, device_cu_count());
   if (big) prefill_attn_kernel<8><<<grid, 512, 0, s>>>(P);
   else prefill_attn_kernel<4><<<grid, 256, 0, s>>>(P);
   return hipGetLastError();

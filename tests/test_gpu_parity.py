@@ -84,7 +84,10 @@ def test_qkv_prefill(w):
 
 
 # ----------------------------------------------------------------------------- causal attention
-PREFILL_ATTN_CASES = [(SMALL_V3, 1), (SMALL_V3, 17), (SMALL_V3, 300), (SMALL_V2, 129), (W[2], 4096), (W[4], 8192)]
+# T=1000 at 128 heads: 128-query tiles, 1024 items over one workgroup per CU (several rounds);
+# T=4764: 19 query tiles of 256, so the last round is reversed and half full.
+PREFILL_ATTN_CASES = [(SMALL_V3, 1), (SMALL_V3, 17), (SMALL_V3, 300), (SMALL_V2, 129), (W[4], 1000), (W[2], 4096),
+                      (W[4], 4764), (W[4], 8192)]
 
 
 @pytest.mark.parametrize("w,T", PREFILL_ATTN_CASES, ids=lambda c: str(c) if isinstance(c, int) else c.name)
