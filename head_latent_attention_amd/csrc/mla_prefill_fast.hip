@@ -57,32 +57,58 @@ struct PrefillArgs {
   int n_qtiles;
 };
 
-// Copies of key tile kt: NW waves share K_SLOTS + V_SLOTS 16-byte slots.  Keys past T
-// repeat the last key (their scores are masked).  Offsets are taken from the tile's first
-// row of head h, so they stay far below 4 GB.
+// Copies of key tile kt: NW waves share K_SLOTS + V_SLOTS 16-byte slots, KI + VI per lane.
+// Keys past T repeat the last key (their scores are masked).  Offsets are taken from the
+// tile's first row of head h, so they stay far below 4 GB; a lane's offsets within a tile
+// are the same for every tile but the last, so they are computed once (copy_offsets).
 template <int NW>
-__device__ __forceinline__ void issue_kv_copy(const PrefillArgs& P, int h, int kt, uint4* __restrict__ kb,
-                                              uint4* __restrict__ vb, int w, int lane) {
-  int l = lane;
-  asm volatile("" : "+v"(l));
-  constexpr int KI = K_SLOTS / 64 / NW, VI = V_SLOTS / 64 / NW;
+struct CopyPlan {
+  static constexpr int KI = K_SLOTS / 64 / NW, VI = V_SLOTS / 64 / NW;
+  uint32_t off[KI + VI];
+};
+
+template <int NW>
+__device__ __forceinline__ uint32_t copy_offset(const PrefillArgs& P, int i, int t_max, int w, int lane) {
+  constexpr int KI = CopyPlan<NW>::KI, VI = CopyPlan<NW>::VI;
+  if (i < KI) {
+    const int p = 64 * (KI * w + i) + lane;
+    const int t = p / KC, c = (p - t * KC) ^ k_swz(t);
+    return (uint32_t)((min(t, t_max) * P.H * DQK + 8 * c) * 2);
+  }
+  const int p = 64 * (VI * w + (i - KI)) + lane;
+  const int t = p / VC, c = (p - t * VC) ^ v_swz(t);
+  return (uint32_t)((min(t, t_max) * P.H * DV + 8 * c) * 2);
+}
+
+template <int NW>
+__device__ __forceinline__ CopyPlan<NW> copy_offsets(const PrefillArgs& P, int w, int lane) {
+  CopyPlan<NW> cp;
+#pragma unroll
+  for (int i = 0; i < CopyPlan<NW>::KI + CopyPlan<NW>::VI; ++i) cp.off[i] = copy_offset<NW>(P, i, KT - 1, w, lane);
+  return cp;
+}
+
+template <int NW>
+__device__ __forceinline__ void issue_kv_copy(const PrefillArgs& P, int h, int kt, const CopyPlan<NW>& cp,
+                                              uint4* __restrict__ kb, uint4* __restrict__ vb, int w, int lane) {
+  constexpr int KI = CopyPlan<NW>::KI, VI = CopyPlan<NW>::VI;
   const int k0 = kt * KT, t_max = P.T - 1 - k0;
   const bf16_t* kbase = P.k + ((int64_t)k0 * P.H + h) * DQK;
   const bf16_t* vbase = P.v + ((int64_t)k0 * P.H + h) * DV;
+  uint32_t off[KI + VI];
+  if (t_max >= KT - 1) {
 #pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    const int p = 64 * (KI * w + i) + l;
-    const int t = p / KC, c = (p - t * KC) ^ k_swz(t);
-    const int tt = min(t, t_max);
-    dma16_buf(kbase, 0x7FFFFFF0u, (uint32_t)((tt * P.H * DQK + 8 * c) * 2), kb + 64 * (KI * w + i));
+    for (int i = 0; i < KI + VI; ++i) off[i] = cp.off[i];
+  } else {  // the tile runs past T
+    int l = lane;
+    asm volatile("" : "+v"(l));
+#pragma unroll
+    for (int i = 0; i < KI + VI; ++i) off[i] = copy_offset<NW>(P, i, t_max, w, l);
   }
 #pragma unroll
-  for (int i = 0; i < VI; ++i) {
-    const int p = 64 * (VI * w + i) + l;
-    const int t = p / VC, c = (p - t * VC) ^ v_swz(t);
-    const int tt = min(t, t_max);
-    dma16_buf(vbase, 0x7FFFFFF0u, (uint32_t)((tt * P.H * DV + 8 * c) * 2), vb + 64 * (VI * w + i));
-  }
+  for (int i = 0; i < KI; ++i) dma16_buf(kbase, 0x7FFFFFF0u, off[i], kb + 64 * (KI * w + i));
+#pragma unroll
+  for (int i = 0; i < VI; ++i) dma16_buf(vbase, 0x7FFFFFF0u, off[KI + i], vb + 64 * (VI * w + i));
 }
 
 constexpr int kRing = 6;  // LDS operand reads in flight per wave in the matrix block
@@ -92,13 +118,15 @@ constexpr int kRing = 6;  // LDS operand reads in flight per wave in the matrix 
 // (qk) S^T = K Q^T for the current tile.  Every LDS access of the step is issued here, through
 // restrict pointers, so that the compiler's waits on the copies stay per access.
 template <int NW>
-__device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, bool copy, int kt_pf, bool qk, bool pv,
+__device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, const CopyPlan<NW>& cp, bool copy, int kt_pf,
+                                          bool qk, bool pv,
                                           const uint4* __restrict__ kb, const uint4* __restrict__ vb,
                                           uint4* __restrict__ kn, uint4* __restrict__ vn,
                                           const bf16x8 (&qf)[2][DQK / 32], f32x4 (&s)[4][2],
                                           const bf16x8 (&pb)[2][2], f32x4 (&o)[DV / 16][2], const int (&kbase)[2],
                                           const int (&vbase)[4], int w, int lane) {
-  if (copy) issue_kv_copy<NW>(P, h, kt_pf, kn, vn, w, lane);
+  __builtin_amdgcn_s_setprio(1);  // this wave's matrix ops go first on the SIMD
+  if (copy) issue_kv_copy<NW>(P, h, kt_pf, cp, kn, vn, w, lane);
   if (pv) {  // O^T[d][query] += V^T P^T; operand i = 8*kk + mt, kRing reads in flight
     const char* vbb = (const char*)vb;
     // keys 32*kk + {0,16} + 4*g + j/4 (same swizzle), chunk 2*mt + half = (2*mt) ^ half
@@ -149,6 +177,7 @@ __device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, bool copy
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Online softmax of one tile's scores (keys k0 .. k0+63) for the wave's 32 queries (lane's
@@ -218,7 +247,8 @@ constexpr int kStages = 4;
 
 // Steps -2 .. n_kt of one item for a wave of group GRP (see prefill_attn_kernel).
 template <int NW, int GRP>
-__device__ __forceinline__ void item_steps(const PrefillArgs& P, int h, int n_kt, int qw0, uint4 (*kbuf)[K_SLOTS],
+__device__ __forceinline__ void item_steps(const PrefillArgs& P, const CopyPlan<NW>& cp, int h, int n_kt, int qw0,
+                                           uint4 (*kbuf)[K_SLOTS],
                                            uint4 (*vbuf)[V_SLOTS], const bf16x8 (&qf)[2][DQK / 32],
                                            f32x4 (&o)[DV / 16][2], float (&m_run)[2], float (&l_run)[2],
                                            const int (&kbase)[2], const int (&vbase)[4], int w, int lane) {
@@ -247,7 +277,7 @@ __device__ __forceinline__ void item_steps(const PrefillArgs& P, int h, int n_kt
     lds_uint4 *kn = (lds_uint4*)kbuf[kt_pf & 3], *vn = (lds_uint4*)vbuf[kt_pf & 3];
     asm volatile("" : "+s"(kc), "+s"(vp), "+s"(kn), "+s"(vn));
     if constexpr (GRP == 0) {
-      mma_block<NW>(P, h, copy, kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn, qf, s,
+      mma_block<NW>(P, h, cp, copy, kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn, qf, s,
                     pb, o, kbase, vbase, w, lane);
       lds_barrier();
       if (qk) softmax_block(P, kt * KT, qw0, s, pb, o, m_run, l_run, g, j);
@@ -256,7 +286,7 @@ __device__ __forceinline__ void item_steps(const PrefillArgs& P, int h, int n_kt
       if (pv) softmax_block(P, (kt - 1) * KT, qw0, s, pb, o, m_run, l_run, g, j);
       else pb_clear(pb);
       lds_barrier();
-      mma_block<NW>(P, h, copy, kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn, qf, s,
+      mma_block<NW>(P, h, cp, copy, kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn, qf, s,
                     pb, o, kbase, vbase, w, lane);
     }
   }
@@ -296,6 +326,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
     vbase[1] = half ^ v_swz(tA);            // chunk XOR
     vbase[2] = vbase[3] = 0;
   }
+  const CopyPlan<NW> cp = copy_offsets<NW>(P, w, lane);
   const bool by_xcd = (gridDim.x & 7) == 0 && (P.H & 7) == 0;
   const int J = by_xcd ? (int)gridDim.x >> 3 : (int)gridDim.x;       // workgroups sharing one list
   const int slot = by_xcd ? (int)blockIdx.x >> 3 : (int)blockIdx.x;  // this workgroup's place in it
@@ -330,8 +361,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
     // the query fragments are complete before the loop, so no read in it waits for the copies
     __builtin_amdgcn_s_waitcnt(0);
     // one loop per group, so that each has its own register liveness
-    if (grp == 0) item_steps<NW, 0>(P, h, n_kt, qw0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
-    else item_steps<NW, 1>(P, h, n_kt, qw0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
+    if (grp == 0) item_steps<NW, 0>(P, cp, h, n_kt, qw0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
+    else item_steps<NW, 1>(P, cp, h, n_kt, qw0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int qi = qw0 + 16 * nt + j;
