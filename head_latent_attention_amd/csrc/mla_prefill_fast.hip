@@ -113,6 +113,23 @@ __device__ __forceinline__ void issue_kv_copy(const PrefillArgs& P, int h, int k
 
 constexpr int kRing = 6;  // LDS operand reads in flight per wave in the matrix block
 
+// Score operand i = 4*ks + mt (keys 16*mt .., dims 32*ks ..): slot KC*(16*mt + j) +
+// ((4*ks + g) ^ k_swz(j)), the lane part in kbase[ks & 1].
+__device__ __forceinline__ bf16x8 k_operand(const uint4* __restrict__ kb, const int (&kbase)[2], int i) {
+  const int ks = i >> 2, mt = i & 3;
+  return as_bf16x8(*(const uint4*)((const char*)kb + kbase[ks & 1] + (KC * 16 * mt + 8 * (ks >> 1)) * 16));
+}
+
+// Value operand i = 8*kk + mt (V^T rows 16*mt .., keys 32*kk ..): keys 32*kk + {0,16} + 4*g +
+// j/4 (same swizzle), chunk 2*mt + half = (2*mt) ^ half, read with the transposing LDS read.
+__device__ __forceinline__ bf16x8 v_operand(const uint4* __restrict__ vb, const int (&vbase)[4], int i) {
+  const int kk = i >> 3, mt = i & 7;
+  const char* pa = (const char*)vb + vbase[0] + (VC * 32 * kk) * 16 + ((2 * mt) ^ vbase[1]) * 16;
+  const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
+  const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + VC * 16 * 16));
+  return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Matrix block of one step for one wave: first this step's share of the K/V copies into the
 // stage kn/vn, then (pv) O^T += V^T P^T for the previous tile from its probabilities pb, and
 // (qk) S^T = K Q^T for the current tile.  Every LDS access of the step is issued here, through
@@ -126,26 +143,22 @@ __device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, const Cop
                                           const bf16x8 (&pb)[2][2], f32x4 (&o)[DV / 16][2], const int (&kbase)[2],
                                           const int (&vbase)[4], int w, int lane) {
   __builtin_amdgcn_s_setprio(1);  // this wave's matrix ops go first on the SIMD
-  if (copy) issue_kv_copy<NW>(P, h, kt_pf, cp, kn, vn, w, lane);
+  // the first score operands are read before the value product, which hides their latency
+  // (unconditionally: a stage holds no tile the wave does not use yet, so such reads are
+  // harmless and their results unused)
+  bf16x8 kring[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) kring[i] = k_operand(kb, kbase, i);
   if (pv) {  // O^T[d][query] += V^T P^T; operand i = 8*kk + mt, kRing reads in flight
-    const char* vbb = (const char*)vb;
-    // keys 32*kk + {0,16} + 4*g + j/4 (same swizzle), chunk 2*mt + half = (2*mt) ^ half
-    auto v_op = [&](int i) {
-      const int kk = i >> 3, mt = i & 7;
-      const char* pa = vbb + vbase[0] + (VC * 32 * kk) * 16 + ((2 * mt) ^ vbase[1]) * 16;
-      const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
-      const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + VC * 16 * 16));
-      return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
     bf16x8 ring[kRing];
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) ring[i] = v_op(i);
+    for (int i = 0; i < kRing; ++i) ring[i] = v_operand(vb, vbase, i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2 * DV / 16; ++i) {
       const int kk = i >> 3, mt = i & 7;
       const bf16x8 a = ring[i % kRing];
-      if (i + kRing < 2 * DV / 16) ring[i % kRing] = v_op(i + kRing);
+      if (i + kRing < 2 * DV / 16) ring[i % kRing] = v_operand(vb, vbase, i + kRing);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nt][kk], o[mt][nt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -154,20 +167,12 @@ __device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, const Cop
   // S is written on every path (zeros for a tile the wave does not see), so the previous
   // tile's scores are dead during P V
   if (qk) {  // S^T[key][query]; operand i = 4*ks + mt, kRing reads in flight
-    // slot KC*(16*mt + j) + ((4*ks + g) ^ k_swz(j)), lane part in kbase[ks & 1]
-    auto k_op = [&](int i) {
-      const int ks = i >> 2, mt = i & 3;
-      return as_bf16x8(*(const uint4*)((const char*)kb + kbase[ks & 1] + (KC * 16 * mt + 8 * (ks >> 1)) * 16));
-    };
-    bf16x8 ring[kRing];
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) ring[i] = k_op(i);
-    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 (&ring)[kRing] = kring;
 #pragma unroll
     for (int i = 0; i < 4 * DQK / 32; ++i) {
       const int ks = i >> 2, mt = i & 3;
       const bf16x8 a = ring[i % kRing];
-      if (i + kRing < 4 * DQK / 32) ring[i % kRing] = k_op(i + kRing);
+      if (i + kRing < 4 * DQK / 32) ring[i % kRing] = k_operand(kb, kbase, i + kRing);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
         s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nt][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][nt], 0, 0, 0);
@@ -177,6 +182,8 @@ __device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, const Cop
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // the copies go last, behind this step's LDS reads
+  if (copy) issue_kv_copy<NW>(P, h, kt_pf, cp, kn, vn, w, lane);
   __builtin_amdgcn_s_setprio(0);
 }
 
