@@ -111,7 +111,7 @@ __device__ __forceinline__ void issue_kv_copy(const PrefillArgs& P, int h, int k
   for (int i = 0; i < VI; ++i) dma16_buf(vbase, 0x7FFFFFF0u, off[KI + i], vb + 64 * (VI * w + i));
 }
 
-constexpr int kRing = 6;  // LDS operand reads in flight per wave in the matrix block
+constexpr int kRing = 4;  // LDS operand reads in flight per wave in the matrix block
 
 // Score operand i = 4*ks + mt (keys 16*mt .., dims 32*ks ..): slot KC*(16*mt + j) +
 // ((4*ks + g) ^ k_swz(j)), the lane part in kbase[ks & 1].
@@ -195,48 +195,62 @@ __device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, const Cop
 __device__ __forceinline__ void softmax_block(const PrefillArgs& P, int k0, int qw0, const f32x4 (&s)[4][2],
                                               bf16x8 (&pb)[2][2], f32x4 (&o)[DV / 16][2], float (&m_run)[2],
                                               float (&l_run)[2], int g, int j) {
-  const bool diag = k0 + KT - 1 > qw0;
+  // both query groups side by side, with short dependency chains: one wave runs this alone on
+  // its SIMD's vector ALU while the other wave's matrix ops run
+  float x[2][4][4];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    float x[4][4];
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[mt][i] = s[mt][nt][i];
-    if (diag) {  // causal mask inside the diagonal tiles only
+      for (int i = 0; i < 4; ++i) x[nt][mt][i] = s[mt][nt][i];
+  if (k0 + KT - 1 > qw0) {  // causal mask inside the diagonal tiles only
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
       const int qi = qw0 + 16 * nt + j;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (k0 + 16 * mt + 4 * g + i > qi) x[mt][i] = -INFINITY;
+          if (k0 + 16 * mt + 4 * g + i > qi) x[nt][mt][i] = -INFINITY;
     }
-    float mx = x[0][0];
+  }
+  float m_new[2], corr[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int nt = 0; nt < 2; ++nt) {
+    float mm[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[mt][i]);
-    mx = xmax16_32(mx) * P.scale_log2;
-    const float m_new = (m_run[nt] == -INFINITY || mx > m_run[nt] + kRescaleThreshold) ? mx : m_run[nt];
-    const float corr = m_run[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-    float sum = 0.f;
+    for (int mt = 0; mt < 4; ++mt) mm[mt] = fmaxf(fmaxf(x[nt][mt][0], x[nt][mt][1]), fmaxf(x[nt][mt][2], x[nt][mt][3]));
+    const float mx = xmax16_32(fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]))) * P.scale_log2;
+    m_new[nt] = (m_run[nt] == -INFINITY || mx > m_run[nt] + kRescaleThreshold) ? mx : m_run[nt];
+    corr[nt] = m_run[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new[nt]);
+  }
+  float sum[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk][i], P.scale_log2, -m_new));
-        p[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk + 1][i], P.scale_log2, -m_new));
-        sum += p[i] + p[4 + i];
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][2 * kk][i], P.scale_log2, -m_new[nt]));
+        p[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][2 * kk + 1][i], P.scale_log2, -m_new[nt]));
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[nt][i] = (kk == 0 ? 0.f : sum[nt][i]) + (p[i] + p[4 + i]);
       pb[nt][kk] = as_bf16x8(make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
     }
-    sum = xsum16_32(sum);
-    l_run[nt] = l_run[nt] * corr + sum;
-    m_run[nt] = m_new;
-    if (__any(corr != 1.f)) {
+  }
 #pragma unroll
-      for (int mt = 0; mt < DV / 16; ++mt) o[mt][nt] *= corr;
+  for (int nt = 0; nt < 2; ++nt) {
+    l_run[nt] = l_run[nt] * corr[nt] + xsum16_32((sum[nt][0] + sum[nt][1]) + (sum[nt][2] + sum[nt][3]));
+    m_run[nt] = m_new[nt];
+  }
+  if (__any(corr[0] != 1.f || corr[1] != 1.f)) {
+#pragma unroll
+    for (int mt = 0; mt < DV / 16; ++mt) {
+      o[mt][0] *= corr[0];
+      o[mt][1] *= corr[1];
     }
   }
 }
