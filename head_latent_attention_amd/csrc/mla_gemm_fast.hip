@@ -483,34 +483,52 @@ struct BigArgs {
   int64_t split_stride;  // elements between the partial sums of consecutive ranges
 };
 
-// Copies of K step k0 into one stage.  Rows past M and columns past the segment are clamped
-// to valid memory; they only feed outputs that are not stored.
-__device__ __forceinline__ void big_issue(const BigArgs& G, const WeightView& W, int m0, int wn0, int wn_end, int k0,
-                                          uint4* __restrict__ as, uint4* __restrict__ ws, int w, int lane) {
-  int l = lane;
-  asm volatile("" : "+v"(l));
+// A lane's byte offsets of its copies within a K step (two activation, two weight), the same
+// for every step of a tile.  Rows past M and columns past the segment are clamped to valid
+// memory; they only feed outputs that are not stored.
+struct BigCopyPlan {
+  uint32_t off[4];
+};
+
+__device__ __forceinline__ BigCopyPlan big_offsets(const BigArgs& G, const WeightView& W, int m0, int wn0, int wn_end,
+                                                   int w, int lane) {
+  BigCopyPlan cp;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int e = 64 * (2 * w + i) + l, r = e >> 2, c = (e & 3) ^ a4_swz(r);
+    const int e = 64 * (2 * w + i) + lane, r = e >> 2, c = (e & 3) ^ a4_swz(r);
     const int m = min(m0 + r, G.M - 1);
-    dma16_buf(G.A + k0, 0x7FFFFFF0u, (uint32_t)((m * G.lda + 8 * c) * 2), as + 64 * (2 * w + i));
+    cp.off[i] = (uint32_t)((m * G.lda + 8 * c) * 2);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int blk = 2 * w + i, hb = blk >> 3, e = 64 * (blk & 7) + l;  // half hb: columns [128hb, 128hb + 128)
+    const int blk = 2 * w + i, hb = blk >> 3, e = 64 * (blk & 7) + lane;  // half hb: columns [128hb, 128hb + 128)
     const int kr = e >> 4, c = (e & 15) ^ (((kr & 3) << 1) ^ (((kr >> 3) & 1) << 3));
     const int n = min(wn0 + 128 * hb + 8 * c, wn_end - 8);
-    dma16_buf((const bf16_t*)W.w + (int64_t)k0 * W.ld, 0x7FFFFFF0u, (uint32_t)((kr * W.ld + n) * 2),
-              ws + 512 * hb + 64 * (blk & 7));
+    cp.off[2 + i] = (uint32_t)((kr * W.ld + n) * 2);
+  }
+  return cp;
+}
+
+// Copies of K step k0 into one stage.
+__device__ __forceinline__ void big_issue(const BigArgs& G, const WeightView& W, const BigCopyPlan& cp, int k0,
+                                          uint4* __restrict__ as, uint4* __restrict__ ws, int w) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) dma16_buf(G.A + k0, 0x7FFFFFF0u, cp.off[i], as + 64 * (2 * w + i));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = 2 * w + i, hb = blk >> 3;
+    dma16_buf((const bf16_t*)W.w + (int64_t)k0 * W.ld, 0x7FFFFFF0u, cp.off[2 + i], ws + 512 * hb + 64 * (blk & 7));
   }
 }
 
-__device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, int m0, int wn0, int wn_end, bool copy,
+__device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, const BigCopyPlan& cp, bool copy,
                                          int k_pf, bool compute, const uint4* __restrict__ as,
                                          const uint4* __restrict__ ws, uint4* __restrict__ as_nx,
                                          uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4], int w, int lane) {
-  if (copy) big_issue(G, W, m0, wn0, wn_end, k_pf, as_nx, ws_nx, w, lane);
-  if (!compute) return;
+  if (!compute) {
+    if (copy) big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
+    return;
+  }
   const int g = lane >> 4, j = lane & 15, wm = w >> 2, wn = w & 3;
   bf16x8 af[8], bfr[4];
 #pragma unroll
@@ -528,6 +546,8 @@ __device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, 
     const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k + 4, c) * 16 + byte_in));
     bfr[nt] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  // the copies go behind the operand reads, which the matrix ops wait for
+  if (copy) big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -647,6 +667,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
   const int wn0 = seg1 ? n0 - G.n_split : n0, wn_end = seg1 ? G.N - G.n_split : G.n_split;
   const int kbeg = blockIdx.z * G.k_split;
   const int nsteps = (min(G.K, kbeg + G.k_split) - kbeg) / kBigK;
+  const BigCopyPlan cp = big_offsets(G, W, m0, wn0, wn_end, w, lane);
   f32x4 acc[8][4];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
@@ -670,7 +691,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
     lds_uint4 *a_cur = (lds_uint4*)As[b_cur], *w_cur = (lds_uint4*)Ws[b_cur];
     lds_uint4 *a_nx = (lds_uint4*)As[b_pf], *w_nx = (lds_uint4*)Ws[b_pf];
     asm volatile("" : "+s"(a_cur), "+s"(w_cur), "+s"(a_nx), "+s"(w_nx));
-    big_step(G, W, m0, wn0, wn_end, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
+    big_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
              (uint4*)a_nx, (uint4*)w_nx, acc, w, lane);
   }
   big_epilogue(E, acc, (bf16_t*)&As[0][0], G.M, G.N, G.C, G.ldc, (int64_t)blockIdx.z * G.split_stride, m0, n0, w,
