@@ -521,38 +521,56 @@ __device__ __forceinline__ void big_issue(const BigArgs& G, const WeightView& W,
   }
 }
 
-__device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, const BigCopyPlan& cp, bool copy,
-                                         int k_pf, bool compute, const uint4* __restrict__ as,
-                                         const uint4* __restrict__ ws, uint4* __restrict__ as_nx,
-                                         uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4], int w, int lane) {
-  if (!compute) {
-    if (copy) big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
-    return;
-  }
-  const int g = lane >> 4, j = lane & 15, wm = w >> 2, wn = w & 3;
-  bf16x8 af[8], bfr[4];
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const int r = 128 * wm + 16 * mt + j;
-    af[mt] = as_bf16x8(as[4 * r + (g ^ a4_swz(r))]);
-  }
+// Operand reads of one stage: A rows 128*wm + 16*mt + j (8 chunks of K), and B columns
+// 64*(wn & 1) + 16*nt + .. of the wave's half through the transposing read.
+__device__ __forceinline__ bf16x8 big_a(const uint4* __restrict__ as, int mt, int w, int lane) {
+  const int r = 128 * (w >> 2) + 16 * mt + (lane & 15);
+  return as_bf16x8(as[4 * r + ((lane >> 4) ^ a4_swz(r))]);
+}
+
+__device__ __forceinline__ bf16x8 big_b(const uint4* __restrict__ ws, int nt, int w, int lane) {
+  const int g = lane >> 4, j = lane & 15, wn = w & 3;
   const char* wsb = (const char*)(ws + 512 * (wn >> 1));
+  const int col = 64 * (wn & 1) + 16 * nt + 4 * (j & 3);
+  const int c = col >> 3, byte_in = (col & 7) * 2;
+  const int k = 8 * g + (j >> 2);
+  const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k, c) * 16 + byte_in));
+  const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k + 4, c) * 16 + byte_in));
+  return __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+constexpr int kBigPreA = 2;  // A operands of the next step read ahead (with all of its B operands)
+
+// One K step: the matrix ops of stage `as/ws` (compute), whose B operands and first kBigPreA A
+// operands were read during the previous step (apre, bpre), then this step's share of the
+// copies, then (pre) the first operands of the next stage `as1/ws1`, so that the next step's
+// first matrix op does not wait for LDS.  Every LDS access of a step is issued here, through
+// restrict pointers.
+__device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, const BigCopyPlan& cp, bool copy,
+                                         int k_pf, bool compute, bool pre, const uint4* __restrict__ as,
+                                         const uint4* __restrict__ as1, const uint4* __restrict__ ws1,
+                                         uint4* __restrict__ as_nx, uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4],
+                                         bf16x8 (&apre)[kBigPreA], bf16x8 (&bpre)[4], int w, int lane) {
+  if (compute) {
+    bf16x8 af[8];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int col = 64 * (wn & 1) + 16 * nt + 4 * (j & 3);
-    const int c = col >> 3, byte_in = (col & 7) * 2;
-    const int k = 8 * g + (j >> 2);
-    const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k, c) * 16 + byte_in));
-    const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wsb + w_slot(k + 4, c) * 16 + byte_in));
-    bfr[nt] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int mt = 0; mt < 8; ++mt) af[mt] = mt < kBigPreA ? apre[mt] : big_a(as, mt, w, lane);
+    // the copies go behind the operand reads, which the matrix ops wait for
+    if (copy) big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bpre[nt], acc[mt][nt], 0, 0, 0);
+  } else if (copy) {
+    big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
   }
-  // the copies go behind the operand reads, which the matrix ops wait for
-  if (copy) big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
+  if (pre) {
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+    for (int nt = 0; nt < 4; ++nt) bpre[nt] = big_b(ws1, nt, w, lane);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+    for (int mt = 0; mt < kBigPreA; ++mt) apre[mt] = big_a(as1, mt, w, lane);
+  }
 }
 
 // Epilogue of the 256 x 256 tile kernels (8 waves of 128 x 64; acc[mt][nt][i] is tile row
@@ -673,26 +691,31 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 apre[kBigPreA], bpre[4];
+#pragma unroll
+  for (int i = 0; i < kBigPreA; ++i) apre[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bpre[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+  // iteration s: matrix ops of step s (s >= 0), copies of step s+3, first operands of step s+1
   for (int s = -(kBigStages - 1); s < nsteps; ++s) {
-    if (s >= 0) {
-      // copies issued after step s's: those of the next min(kBigStages - 2, ...) steps
-      const int later = min(nsteps - 1 - s, kBigStages - 2);
-      if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kBigCopies));
-      else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kBigCopies);
+    if (s >= -1) {
+      // steps s and s+1 in LDS: the copies issued after step s+1's are those of step s+2
+      if (s + 2 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F70 | kBigCopies);
       else __builtin_amdgcn_s_waitcnt(0x0F70);
       lds_barrier();
     }
     const int s_pf = s + kBigStages - 1;
     const int b_pf = (s_pf + kBigStages) % kBigStages, b_cur = s < 0 ? 0 : s % kBigStages;
+    const int b_1 = (s + 1 + kBigStages) % kBigStages;
     // opaque copies of the stage pointers: accesses through them keep the restrict scopes of
     // big_step's parameters (pointers the compiler can trace to the __shared__ arrays lose them,
     // and every operand read would then wait for the copies in flight)
     typedef __attribute__((address_space(3))) uint4 lds_uint4;
-    lds_uint4 *a_cur = (lds_uint4*)As[b_cur], *w_cur = (lds_uint4*)Ws[b_cur];
+    lds_uint4 *a_cur = (lds_uint4*)As[b_cur], *a_1 = (lds_uint4*)As[b_1], *w_1 = (lds_uint4*)Ws[b_1];
     lds_uint4 *a_nx = (lds_uint4*)As[b_pf], *w_nx = (lds_uint4*)Ws[b_pf];
-    asm volatile("" : "+s"(a_cur), "+s"(w_cur), "+s"(a_nx), "+s"(w_nx));
-    big_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, (const uint4*)a_cur, (const uint4*)w_cur,
-             (uint4*)a_nx, (uint4*)w_nx, acc, w, lane);
+    asm volatile("" : "+s"(a_cur), "+s"(a_1), "+s"(w_1), "+s"(a_nx), "+s"(w_nx));
+    big_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s >= -1 && s + 1 < nsteps, (const uint4*)a_cur,
+             (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx, acc, apre, bpre, w, lane);
   }
   big_epilogue(E, acc, (bf16_t*)&As[0][0], G.M, G.N, G.C, G.ldc, (int64_t)blockIdx.z * G.split_stride, m0, n0, w,
                lane);
