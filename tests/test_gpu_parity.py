@@ -19,6 +19,8 @@ W = synth.WORKLOADS
 # small shapes with the V2/V3 per-head dims (kv_lora 512, nope 128, rope 64, v 128) and ragged sizes
 SMALL_V3 = synth.custom(W[4], 101, "small-v3-prefill", hidden=1024, n_heads=16, q_lora_rank=256, T=300)
 SMALL_V2 = synth.custom(W[2], 102, "small-v2-prefill", hidden=512, n_heads=16, T=177)
+# 10 heads: the prefill attention deals its items over the whole (query tile, head) list
+ODD_HEADS = synth.custom(W[4], 109, "odd-heads-prefill", hidden=1024, n_heads=10, q_lora_rank=256, T=4000)
 EDGE_DEC16 = synth.custom(W[3], 103, "edge-decode-h16", hidden=1024, n_heads=16, q_lora_rank=256, B=6)
 EDGE_DEC128 = synth.custom(W[3], 104, "edge-decode-h128", B=6)
 EDGE_FP8 = synth.custom(W[5], 105, "edge-decode-fp8", B=6)
@@ -85,9 +87,10 @@ def test_qkv_prefill(w):
 
 # ----------------------------------------------------------------------------- causal attention
 # T=1000 at 128 heads: 128-query tiles, 1024 items over one workgroup per CU (several rounds);
-# T=4764: 19 query tiles of 256, so the last round is reversed and half full.
+# T=4764: 19 query tiles of 256, so the last round is reversed and half full.  10 heads: the
+# list is not split by XCD (one round at T=700; at T=4000, 320 items, the second round partial).
 PREFILL_ATTN_CASES = [(SMALL_V3, 1), (SMALL_V3, 17), (SMALL_V3, 300), (SMALL_V2, 129), (W[4], 1000), (W[2], 4096),
-                      (W[4], 4764), (W[4], 8192)]
+                      (W[4], 4764), (W[4], 8192), (ODD_HEADS, 700), (ODD_HEADS, 4000)]
 
 
 @pytest.mark.parametrize("w,T", PREFILL_ATTN_CASES, ids=lambda c: str(c) if isinstance(c, int) else c.name)
