@@ -834,26 +834,41 @@ __device__ __forceinline__ f32x4 f8_mma(const i32x8& a, const i32x8& b, const f3
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, SEL, sa, 0, sb);
 }
 
-__device__ __forceinline__ void f8_issue(const F8Args& G, const WeightView& W, int m0, int wn0, int wn_end, int k0,
-                                         uint4* __restrict__ as, uint4* __restrict__ ws, int w, int lane) {
-  int l = lane;
-  asm volatile("" : "+v"(l));
+// A lane's byte offsets of its copies within a K step (four activation, four weight), from
+// the step's first column of A and first row of W: the same for every step of a tile.
+struct F8CopyPlan {
+  uint32_t off[8];
+};
+
+__device__ __forceinline__ F8CopyPlan f8_offsets(const F8Args& G, const WeightView& W, int m0, int wn0, int wn_end,
+                                                 int w, int lane) {
+  F8CopyPlan cp;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = 64 * (4 * w + i) + l, r = e >> 3, c = (e & 7) ^ f8a_swz(r);
+    const int e = 64 * (4 * w + i) + lane, r = e >> 3, c = (e & 7) ^ f8a_swz(r);
     const int m = min(m0 + r, G.M - 1);
-    dma16_buf(G.A, 0x7FFFFFF0u, (uint32_t)(m * G.lda + k0 + 16 * c), as + 64 * (4 * w + i));
+    cp.off[i] = (uint32_t)(m * G.lda + 16 * c);
   }
-  const uint8_t* wb = (const uint8_t*)W.w + (int64_t)k0 * W.ld;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = 64 * (4 * w + i) + l, k = e >> 4, c = (e & 15) ^ f8w_swz(k);
+    const int e = 64 * (4 * w + i) + lane, k = e >> 4, c = (e & 15) ^ f8w_swz(k);
     const int n = min(wn0 + 16 * c, wn_end - 16);
-    dma16_buf(wb, 0x7FFFFFF0u, (uint32_t)(k * W.ld + n), ws + 64 * (4 * w + i));
+    cp.off[4 + i] = (uint32_t)(k * W.ld + n);
   }
+  return cp;
 }
 
-__device__ __forceinline__ void f8_step(const F8Args& G, const WeightView& W, int m0, int wn0, int wn_end, bool copy,
+__device__ __forceinline__ void f8_issue(const F8Args& G, const WeightView& W, const F8CopyPlan& cp, int k0,
+                                         uint4* __restrict__ as, uint4* __restrict__ ws, int w) {
+  const uint8_t* ab = (const uint8_t*)G.A + k0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16_buf(ab, 0x7FFFFFF0u, cp.off[i], as + 64 * (4 * w + i));
+  const uint8_t* wb = (const uint8_t*)W.w + (int64_t)k0 * W.ld;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16_buf(wb, 0x7FFFFFF0u, cp.off[4 + i], ws + 64 * (4 * w + i));
+}
+
+__device__ __forceinline__ void f8_step(const F8Args& G, const WeightView& W, const F8CopyPlan& cp, int m0, bool copy,
                                         int k_pf, const uint4* __restrict__ as, const uint4* __restrict__ ws,
                                         uint4* __restrict__ as_nx, uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4],
                                         uint2 sa, int sb, uint2& sa_nx, uint32_t& sw_nx, int nb, int w, int lane) {
@@ -865,7 +880,7 @@ __device__ __forceinline__ void f8_step(const F8Args& G, const WeightView& W, in
     const int64_t m_pad = f8_rows_pad(G.M);
     sa_nx = *(const uint2*)(G.Ae + f8_exp_order(kg, m0 + 128 * wm + j, m_pad));
     sw_nx = __float_as_uint(W.scale[(int64_t)kg * W.scale_ld + nb]);
-    f8_issue(G, W, m0, wn0, wn_end, k_pf, as_nx, ws_nx, w, lane);
+    f8_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
   }
   i32x8 bfr[4];
   const char* wsb = (const char*)ws;
@@ -912,6 +927,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f8_kernel(F8Args G, EpiArgs E) {
   // the wave's 64 columns lie in one 128-column scale block (waves past the segment's end,
   // whose columns are not stored, read the last block's scale)
   const int nb = min((wn0 + 64 * wn) / 128, W.scale_ld - 1);
+  const F8CopyPlan cp = f8_offsets(G, W, m0, wn0, wn_end, w, lane);
   f32x4 acc[8][4];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
@@ -928,7 +944,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f8_kernel(F8Args G, EpiArgs E) {
     const int64_t m_pad = f8_rows_pad(G.M);
     sa = *(const uint2*)(G.Ae + f8_exp_order(kg, m0 + 128 * wm + j, m_pad));
     sw = __float_as_uint(W.scale[(int64_t)kg * W.scale_ld + nb]);
-    f8_issue(G, W, m0, wn0, wn_end, kbeg, (uint4*)a0, (uint4*)w0, w, lane);
+    f8_issue(G, W, cp, kbeg, (uint4*)a0, (uint4*)w0, w);
   }
   for (int s = 0; s < nsteps; ++s) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of step s
@@ -940,7 +956,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f8_kernel(F8Args G, EpiArgs E) {
     asm volatile("" : "+s"(a_cur), "+s"(w_cur), "+s"(a_nx), "+s"(w_nx));
     const int sb = (int)((sw >> 23) & 0xFF);
     bad |= (sw & 0x807FFFFFu) | (sb == 0 || sb == 0xFF);
-    f8_step(G, W, m0, wn0, wn_end, more, kbeg + (s + 1) * kF8K, (const uint4*)a_cur, (const uint4*)w_cur,
+    f8_step(G, W, cp, m0, more, kbeg + (s + 1) * kF8K, (const uint4*)a_cur, (const uint4*)w_cur,
             (uint4*)a_nx, (uint4*)w_nx, acc, sa, sb, sa_nx, sw_nx, nb, w, lane);
     sa = sa_nx;
     sw = sw_nx;
