@@ -348,8 +348,8 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration for HBM traffic)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
-                                   "not an implemented path", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; sharding across GPUs is described in "
+                                   "the design notes, not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     import synth
