@@ -88,11 +88,11 @@ def test_qkv_prefill_fp8(w):
     rows = _rows(T) if T > 1000 else np.arange(T)
     qr, rr = O.project(Wd, x64[rows], rows, dims)
     Kr, Vr = O.expand_kv(Wd, rr, dims)
-    assert_close(torch_io.to_f64(q)[rows], qr, s.act, "q")
-    assert_close(torch_io.to_f64(k)[rows], Kr, s.act, "k")
-    assert_close(torch_io.to_f64(v)[rows], Vr, s.act, "v")
+    assert_close(torch_io.to_f64(q)[rows], qr, s.act, "q", rows)
+    assert_close(torch_io.to_f64(k)[rows], Kr, s.act, "k", rows)
+    assert_close(torch_io.to_f64(v)[rows], Vr, s.act, "v", rows)
     flat = torch_io.to_f64(cache).reshape(-1, s.row)
-    assert_close(flat[slots[rows]], rr, s.act, "cache rows")
+    assert_close(flat[slots[rows]], rr, s.act, "cache rows", rows)
 
 
 @pytest.mark.parametrize("w,M", [(FP8_SMALL, 1300), (FP8_SMALL, 64), (FP8_C4, 8192)],
@@ -110,7 +110,7 @@ def test_out_proj_fp8(w, M):
     torch.cuda.synchronize()
     rows = _rows(M) if M > 1000 else np.arange(M)
     ref = O.out_proj(Wd, O.decode_tensor(s.act, oh.data)[rows], O.dims_of(s))
-    assert_close(torch_io.to_f64(y)[rows], ref, s.act, "y")
+    assert_close(torch_io.to_f64(y)[rows], ref, s.act, "y", rows)
 
 
 def test_decode_front_end_fp8():

@@ -72,14 +72,14 @@ def test_qkv_prefill(w):
     rows = _sample_rows(T) if T > 1000 else np.arange(T)
     qr, rr = O.project(Wd, x64[rows], rows, dims)
     Kr, Vr = O.expand_kv(Wd, rr, dims)
-    assert_close(torch_io.to_f64(q)[rows], qr, s.act, "q")
-    assert_close(torch_io.to_f64(k)[rows], Kr, s.act, "k")
-    assert_close(torch_io.to_f64(v)[rows], Vr, s.act, "v")
+    assert_close(torch_io.to_f64(q)[rows], qr, s.act, "q", rows)
+    assert_close(torch_io.to_f64(k)[rows], Kr, s.act, "k", rows)
+    assert_close(torch_io.to_f64(v)[rows], Vr, s.act, "v", rows)
     # every cache row: the right row in the right slot, nothing else written
     all_rows = O.project_rows(Wd, x64, np.arange(T), dims)
     flat = torch_io.to_f64(cache).reshape(-1, s.row)
     keep = slots >= 0
-    assert_close(flat[slots[keep]], all_rows[keep], s.act, "cache rows")
+    assert_close(flat[slots[keep]], all_rows[keep], s.act, "cache rows", np.arange(T)[keep])
     b = torch_io.bits(cache).reshape(-1, s.row)
     untouched = np.setdiff1d(np.arange(b.shape[0]), slots[keep])
     assert (b[untouched] == sentinel).all()
@@ -89,18 +89,23 @@ def test_qkv_prefill(w):
 # T=1000 at 128 heads: 128-query tiles, 1024 items over one workgroup per CU (several rounds);
 # T=4764: 19 query tiles of 256, so the last round is reversed and half full.  10 heads: the
 # list is not split by XCD (one round at T=700; at T=4000, 320 items, the second round partial).
-PREFILL_ATTN_CASES = [(SMALL_V3, 1), (SMALL_V3, 17), (SMALL_V3, 300), (SMALL_V2, 129), (W[4], 1000), (W[2], 4096),
-                      (W[4], 4764), (W[4], 8192), (ODD_HEADS, 700), (ODD_HEADS, 4000)]
+# q_std 8 makes the softmax peaky (score std about 8 in natural-log units): the running maximum
+# moves by more than the kernels' lazy-rescale threshold many times along a row.
+PREFILL_ATTN_CASES = [(SMALL_V3, 1, 1.0), (SMALL_V3, 17, 1.0), (SMALL_V3, 300, 1.0), (SMALL_V2, 129, 1.0),
+                      (W[4], 1000, 1.0), (W[2], 4096, 1.0), (W[4], 4764, 1.0), (W[4], 8192, 1.0), (ODD_HEADS, 700, 1.0),
+                      (ODD_HEADS, 4000, 1.0), (SMALL_V3, 300, 8.0), (W[2], 4096, 8.0), (W[4], 8192, 8.0)]
 
 
-@pytest.mark.parametrize("w,T", PREFILL_ATTN_CASES, ids=lambda c: str(c) if isinstance(c, int) else c.name)
-def test_prefill_attn(w, T):
+@pytest.mark.parametrize("w,T,q_std", PREFILL_ATTN_CASES,
+                         ids=lambda c: (c.name if not isinstance(c, (int, float)) else
+                                        (str(c) if isinstance(c, int) else f"qstd{c:g}")))
+def test_prefill_attn(w, T, q_std):
     need_gpu()
     import head_latent_attention_amd as mla
     s = w.shape
-    print(f"[prefill_attn] {w.name} T={T}", flush=True)
+    print(f"[prefill_attn] {w.name} T={T} q_std={q_std}", flush=True)
     cfg = lib_config(s)
-    qh = synth.make_normal(w, f"attn.q.{T}", (T, s.n_heads, s.qk_head))
+    qh = synth.make_normal(w, f"attn.q.{T}", (T, s.n_heads, s.qk_head), std=q_std)
     kh = synth.make_normal(w, f"attn.k.{T}", (T, s.n_heads, s.qk_head))
     vh = synth.make_normal(w, f"attn.v.{T}", (T, s.n_heads, s.v_dim))
     o = torch_io.empty_act(s.act, (T, s.n_heads, s.v_dim))
@@ -109,7 +114,7 @@ def test_prefill_attn(w, T):
     rows = _sample_rows(T) if T > 1000 else np.arange(T)
     q64, k64, v64 = (O.decode_tensor(s.act, t.data) for t in (qh, kh, vh))
     ref = O.attention(q64[rows], k64, v64, O.softmax_scale(s.qk_nope, s.qk_rope), rows)
-    assert_close(torch_io.to_f64(o)[rows], ref, s.act, "o")
+    assert_close(torch_io.to_f64(o)[rows], ref, s.act, "o", rows)
 
 
 # ----------------------------------------------------------------------------- decode front end
@@ -157,30 +162,43 @@ def _paged_cache(w, ctx):
     return pg, dev
 
 
-@pytest.mark.parametrize("w", [EDGE_DEC16, EDGE_DEC128, EDGE_FP8, W[3], W[5]], ids=lambda w: w.name)
-def test_decode_attn_absorbed(w):
+def _decode_sample(ctx):
+    """Sequences the oracle recomputes at full batch: the two shortest, the median, the longest
+    (split over the most attention shares) and two seeded random ones."""
+    order = np.argsort(ctx, kind="stable")
+    pick = {int(order[0]), int(order[1]), int(order[len(order) // 2]), int(np.argmax(ctx))}
+    pick |= set(np.random.default_rng(7).choice(len(ctx), 2, replace=False).tolist())
+    return np.array(sorted(pick))
+
+
+# q_std 6.4 (8x the usual 0.8) makes the softmax peaky: the lazy rescale runs along every long
+# sequence.
+DECODE_ATTN_CASES = [(EDGE_DEC16, 0.8), (EDGE_DEC128, 0.8), (EDGE_FP8, 0.8), (W[3], 0.8), (W[5], 0.8),
+                     (EDGE_DEC128, 6.4), (W[3], 6.4)]
+
+
+@pytest.mark.parametrize("w,q_std", DECODE_ATTN_CASES,
+                         ids=lambda c: c.name if not isinstance(c, float) else f"qstd{c:g}")
+def test_decode_attn_absorbed(w, q_std):
     need_gpu()
     import head_latent_attention_amd as mla
     s = w.shape
-    print(f"[decode_attn] {w.name} B={w.B}", flush=True)
+    print(f"[decode_attn] {w.name} B={w.B} q_std={q_std}", flush=True)
     host, Wd, dw = _weights(w)
     cfg = lib_config(s)
     ctx = EDGE_CTX if w.B == 6 else synth.context_lengths(w)
     pg, cache = _paged_cache(w, ctx)
-    qh = synth.make_normal(w, "decode.q", (w.B, s.n_heads, s.qk_head), std=0.8)
+    qh = synth.make_normal(w, "decode.q", (w.B, s.n_heads, s.qk_head), std=q_std)
     o = torch_io.empty_act(s.act, (w.B, s.n_heads, s.v_dim))
     mla.mla_decode_attn_absorbed(cfg, dw, torch_io.to_device(qh), cache, torch.from_numpy(pg.block_table).cuda(),
                                  torch.from_numpy(ctx).cuda(), o)
     torch.cuda.synchronize()
-    if w.B <= 8:
-        bs_ = np.arange(w.B)
-    else:
-        order = np.argsort(ctx)
-        bs_ = np.array(sorted({int(order[0]), int(order[1]), int(order[len(order) // 2])}))
+    bs_ = np.arange(w.B) if w.B <= 8 else _decode_sample(ctx)
     q64 = O.decode_tensor(s.act, qh.data)
     seqs = [O.decode_tensor(s.act, synth.history_rows(w, int(b), int(ctx[b])).data) for b in bs_]
     ref = O.decode_attention(Wd, q64[bs_], seqs, O.dims_of(s))
-    assert_close(torch_io.to_f64(o)[bs_], ref, s.act, f"o (sequences {bs_.tolist()})")
+    assert_close(torch_io.to_f64(o)[bs_], ref, s.act, f"o (sequences {bs_.tolist()}, contexts {ctx[bs_].tolist()})",
+                 bs_)
 
 
 # Many short sequences: several whole sequences inside one attention workgroup's share of the
@@ -224,7 +242,7 @@ def test_decode_attn_many_short_sequences(w):
     q64 = O.decode_tensor(s.act, qh.data)
     seqs = [O.decode_tensor(s.act, synth.history_rows(w, int(b), int(ctx[b])).data) for b in bs_]
     ref = O.decode_attention(Wd, q64[bs_], seqs, O.dims_of(s))
-    assert_close(torch_io.to_f64(o)[bs_], ref, s.act, f"o (sequences {bs_.tolist()})")
+    assert_close(torch_io.to_f64(o)[bs_], ref, s.act, f"o (sequences {bs_.tolist()})", bs_)
     # every output is finite (a share's partial written to a wrong slot would leave garbage)
     assert torch.isfinite(o.float()).all()
 
@@ -245,4 +263,4 @@ def test_out_proj(w, M):
     torch.cuda.synchronize()
     rows = _sample_rows(M) if M > 1000 else np.arange(M)
     ref = O.decode_tensor(s.act, oh.data)[rows] @ Wd["wo"]
-    assert_close(torch_io.to_f64(y)[rows], ref, s.act, "y")
+    assert_close(torch_io.to_f64(y)[rows], ref, s.act, "y", rows)
