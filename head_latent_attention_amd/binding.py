@@ -114,6 +114,65 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+# ---- argument checks: the C ABI takes raw pointers, so dtypes and element counts are checked
+# here, before the call (an int64 index tensor read as int32 pairs, or a buffer smaller than the
+# shapes in include/mla.h, would otherwise go unnoticed)
+_ACT_DTYPE = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
+_FP8_DTYPES = tuple(t for t in (torch.uint8, getattr(torch, "float8_e4m3fn", None)) if t is not None)
+
+
+def _act_dtype(cfg: MlaConfig):
+    return _ACT_DTYPE[cfg.act_dtype]
+
+
+def _need(t, name: str, dtype, numel: Optional[int] = None, shape=None):
+    """t must be a tensor of `dtype` (a dtype or a tuple of them) with `numel` elements, or of
+    exactly `shape` (None entries match any size)."""
+    if t is None:
+        raise MlaError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise MlaError(f"{name} must be a torch tensor")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise MlaError(f"{name} must have dtype {' or '.join(str(d) for d in dts)}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(e is not None and e != a for e, a in zip(shape, t.shape)):
+            raise MlaError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise MlaError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def _need_cache(cfg: MlaConfig, kv_cache):
+    """The paged latent cache [n_blocks, 1, block_size, kv_lora_rank + qk_rope] in the act dtype."""
+    _need(kv_cache, "kv_cache", _act_dtype(cfg),
+          shape=(None, 1, cfg.block_size, cfg.kv_lora_rank + cfg.qk_rope))
+    if kv_cache.shape[0] < 1:
+        raise MlaError("kv_cache must hold at least one block")
+
+
+def _need_tables(cfg: MlaConfig, cos, sin, n: int):
+    for name, t in (("cos", cos), ("sin", sin)):
+        _need(t, name, torch.float32, numel=n * (cfg.qk_rope // 2))
+
+
+def _need_ws(ws):
+    if ws is not None and not isinstance(ws, torch.Tensor):
+        raise MlaError("ws must be a torch tensor")
+
+
+def weight_shapes(cfg: MlaConfig) -> Dict[str, tuple]:
+    """[in, out] shape of each projection weight and [n] of each fp32 gamma (include/mla.h)."""
+    H, dqk = cfg.n_heads, cfg.qk_nope + cfg.qk_rope
+    qin = cfg.q_lora_rank if cfg.q_lora_rank else cfg.hidden
+    shp = {"wq_b": (qin, H * dqk), "wkv_a": (cfg.hidden, cfg.kv_lora_rank + cfg.qk_rope),
+           "wkv_b": (cfg.kv_lora_rank, H * (cfg.qk_nope + cfg.v_dim)), "wo": (H * cfg.v_dim, cfg.hidden),
+           "kv_norm_w": (cfg.kv_lora_rank,), "input_norm_w": (cfg.hidden,)}
+    if cfg.q_lora_rank:
+        shp["wq_a"] = (cfg.hidden, cfg.q_lora_rank)
+        shp["q_norm_w"] = (cfg.q_lora_rank,)
+    return shp
+
+
 class Weights:
     """Holds the device tensors of one layer and their MlaWeights struct."""
 
@@ -129,6 +188,29 @@ class Weights:
         s.kv_norm_w = _ptr(self.tensors.get("kv_norm_w"))
         s.input_norm_w = _ptr(self.tensors.get("input_norm_w"))
         self.struct = s
+
+    def check(self, cfg: MlaConfig, names) -> None:
+        """The weights an entry point reads match the config: dtype, shape, and for fp8 the fp32
+        block-scale grid [ceil(K/128), ceil(N/128)]; gammas fp32.  Optional ones (input_norm_w)
+        are checked only when present."""
+        shapes = weight_shapes(cfg)
+        wdt = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16, MLA_FP8_E4M3: _FP8_DTYPES}[cfg.weight_dtype]
+        for name in names:
+            if name not in shapes:
+                continue
+            t = self.tensors.get(name)
+            if t is None and name == "input_norm_w":
+                continue
+            if name.endswith("_norm_w"):
+                _need(t, name, torch.float32, numel=shapes[name][0])
+                continue
+            K, N = shapes[name]
+            _need(t, name, wdt, shape=(K, N))
+            if cfg.weight_dtype == MLA_FP8_E4M3:
+                _need(self.scales.get(name), f"{name} scale", torch.float32, shape=(-(-K // 128), -(-N // 128)))
+
+
+_FRONT = ("wq_a", "wq_b", "wkv_a", "q_norm_w", "kv_norm_w", "input_norm_w")
 
 
 def _stream(stream) -> Optional[int]:
@@ -152,13 +234,15 @@ def workspace(cfg: MlaConfig, fn: int, n: int, max_context: int = 0, device="cud
 
 
 def _ws(ws, cfg, fn, n, max_context=0, device="cuda"):
+    _need_ws(ws)
     if ws is None:
         ws = workspace(cfg, fn, n, max_context, device)
-    return ws, ws.numel()
+    return ws, ws.numel() * ws.element_size()
 
 
 def mla_quantize_fp8(x, stream=None):
     """MX fp8 codes [M, K] (uint8) and exponent bytes [ceil(K/128), M] (e + 127) of bf16 rows x."""
+    _need(x, "x", torch.bfloat16, shape=(None, None))
     M, K = x.shape
     codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     exps = torch.empty(((K + 127) // 128, M), dtype=torch.uint8, device=x.device)
@@ -201,7 +285,22 @@ def rope_cos_sin(positions, rope_dim: int, theta: float = 10000.0, device="cuda"
 def mla_qkv_prefill(cfg, w: Weights, x, cos, sin, q, k=None, v=None, kv_cache=None, slot_mapping=None, ws=None,
                     stream=None):
     """k = v = None skips the per-head K/V expansion (a chunk attended on the latent cache)."""
+    act, H, dqk = _act_dtype(cfg), cfg.n_heads, cfg.qk_nope + cfg.qk_rope
+    _need(x, "x", act, shape=(None, cfg.hidden))
     T = x.shape[0]
+    _need_tables(cfg, cos, sin, T)
+    _need(q, "q", act, numel=T * H * dqk)
+    if (k is None) != (v is None):
+        raise MlaError("k and v are given together or not at all")
+    if k is not None:
+        _need(k, "k", act, numel=T * H * dqk)
+        _need(v, "v", act, numel=T * H * cfg.v_dim)
+    if (kv_cache is None) != (slot_mapping is None):
+        raise MlaError("kv_cache and slot_mapping are given together or not at all")
+    if kv_cache is not None:
+        _need_cache(cfg, kv_cache)
+        _need(slot_mapping, "slot_mapping", torch.int32, numel=T)
+    w.check(cfg, _FRONT + (("wkv_b",) if k is not None else ()))
     ws, nb = _ws(ws, cfg, FN_QKV_PREFILL, T, device=x.device)
     n_blocks = kv_cache.shape[0] if kv_cache is not None else 0
     _check(load().mla_qkv_prefill(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(x), T, _ptr(cos), _ptr(sin),
@@ -210,14 +309,27 @@ def mla_qkv_prefill(cfg, w: Weights, x, cos, sin, q, k=None, v=None, kv_cache=No
 
 
 def mla_prefill_attn(cfg, q, k, v, o, ws=None, stream=None):
+    act, H, dqk = _act_dtype(cfg), cfg.n_heads, cfg.qk_nope + cfg.qk_rope
+    _need(q, "q", act)
     T = q.shape[0]
+    _need(q, "q", act, numel=T * H * dqk)
+    _need(k, "k", act, numel=T * H * dqk)
+    _need(v, "v", act, numel=T * H * cfg.v_dim)
+    _need(o, "o", act, numel=T * H * cfg.v_dim)
     ws, nb = _ws(ws, cfg, FN_PREFILL_ATTN, T, device=q.device)
     _check(load().mla_prefill_attn(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), T, _ptr(o), _ptr(ws), nb,
                                    _stream(stream)))
 
 
 def mla_decode_qkv_and_scatter(cfg, w: Weights, x, cos, sin, kv_cache, slot_mapping, q, ws=None, stream=None):
+    act = _act_dtype(cfg)
+    _need(x, "x", act, shape=(None, cfg.hidden))
     B = x.shape[0]
+    _need_tables(cfg, cos, sin, B)
+    _need_cache(cfg, kv_cache)
+    _need(slot_mapping, "slot_mapping", torch.int32, numel=B)
+    _need(q, "q", act, numel=B * cfg.n_heads * (cfg.qk_nope + cfg.qk_rope))
+    w.check(cfg, _FRONT)
     ws, nb = _ws(ws, cfg, FN_DECODE_QKV, B, device=x.device)
     _check(load().mla_decode_qkv_and_scatter(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(x), B, _ptr(cos),
                                              _ptr(sin), _ptr(kv_cache), kv_cache.shape[0], _ptr(slot_mapping),
@@ -225,7 +337,14 @@ def mla_decode_qkv_and_scatter(cfg, w: Weights, x, cos, sin, kv_cache, slot_mapp
 
 
 def mla_decode_attn_absorbed(cfg, w: Weights, q, kv_cache, block_table, context_lens, o, ws=None, stream=None):
+    act = _act_dtype(cfg)
+    _need(block_table, "block_table", torch.int32, shape=(None, None))
     B, max_blocks = block_table.shape
+    _need(context_lens, "context_lens", torch.int32, numel=B)
+    _need(q, "q", act, numel=B * cfg.n_heads * (cfg.qk_nope + cfg.qk_rope))
+    _need(o, "o", act, numel=B * cfg.n_heads * cfg.v_dim)
+    _need_cache(cfg, kv_cache)
+    w.check(cfg, ("wkv_b",))
     ws, nb = _ws(ws, cfg, FN_DECODE_ATTN, B, max_blocks * cfg.block_size, device=q.device)
     _check(load().mla_decode_attn_absorbed(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(q), B, _ptr(kv_cache),
                                            kv_cache.shape[0], _ptr(block_table), max_blocks, _ptr(context_lens),
@@ -235,7 +354,14 @@ def mla_decode_attn_absorbed(cfg, w: Weights, q, kv_cache, block_table, context_
 def mla_prefill_attn_paged(cfg, w: Weights, q, kv_cache, block_table, prefix_len: int, o, ws=None, stream=None):
     """Chunk of T = q.shape[0] tokens at positions prefix_len.. over one sequence's cache
     (block_table int32 [max_blocks])."""
+    act = _act_dtype(cfg)
+    _need(q, "q", act)
+    _need(block_table, "block_table", torch.int32, shape=(None,))
     T, max_blocks = q.shape[0], block_table.numel()
+    _need(q, "q", act, numel=T * cfg.n_heads * (cfg.qk_nope + cfg.qk_rope))
+    _need(o, "o", act, numel=T * cfg.n_heads * cfg.v_dim)
+    _need_cache(cfg, kv_cache)
+    w.check(cfg, ("wkv_b",))
     ws, nb = _ws(ws, cfg, FN_PREFILL_ATTN_PAGED, T, max_blocks * cfg.block_size, device=q.device)
     _check(load().mla_prefill_attn_paged(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(q), T, _ptr(kv_cache),
                                          kv_cache.shape[0], _ptr(block_table), max_blocks, int(prefix_len), _ptr(o),
@@ -243,7 +369,12 @@ def mla_prefill_attn_paged(cfg, w: Weights, q, kv_cache, block_table, prefix_len
 
 
 def mla_out_proj(cfg, w: Weights, o, y, ws=None, stream=None):
+    act = _act_dtype(cfg)
+    _need(o, "o", act)
     M = o.shape[0]
+    _need(o, "o", act, numel=M * cfg.n_heads * cfg.v_dim)
+    _need(y, "y", act, shape=(M, cfg.hidden))
+    w.check(cfg, ("wo",))
     ws, nb = _ws(ws, cfg, FN_OUT_PROJ, M, device=o.device)
     _check(load().mla_out_proj(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(o.reshape(M, -1)), M, _ptr(y),
                                _ptr(ws), nb, _stream(stream)))

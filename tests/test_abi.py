@@ -143,3 +143,88 @@ def test_act_quant_config_and_quantize_validation():
     assert lib.mla_quantize_fp8(1, 0, 128, 128, 1, 1, None) == -1
     assert lib.mla_quantize_fp8(1, 4, 128, 100, 1, 1, None) == -1   # row stride below K
     assert lib.mla_quantize_fp8(1, 4, 128, 128, None, 1, None) == -1
+
+
+# ---- the Python binding's argument checks (no GPU: every rejection happens before a pointer
+# is taken or the library is called)
+import torch  # noqa: E402
+
+
+def _host_weights(cfg, **override):
+    """A Weights holder over host tensors (its device struct is never built)."""
+    w = B.Weights.__new__(B.Weights)
+    wdt = torch.bfloat16 if cfg.weight_dtype == B.MLA_BF16 else torch.float32
+    w.tensors = {n: torch.zeros(s, dtype=torch.float32 if n.endswith("_norm_w") else wdt)
+                 for n, s in B.weight_shapes(cfg).items() if n != "input_norm_w"}
+    w.scales = {}
+    w.tensors.update(override)
+    return w
+
+
+def _bf16_cfg():
+    return mla.config(256, 4, 64, 64, 32, 16, 32, act="bf16", weight="bf16", block_size=16, softmax_scale=0.1)
+
+
+def test_binding_rejects_int64_indices():
+    cfg = _bf16_cfg()
+    Bq, H = 3, cfg.n_heads
+    q = torch.zeros(Bq, H, 48, dtype=torch.bfloat16)
+    o = torch.zeros(Bq, H, 32, dtype=torch.bfloat16)
+    cache = torch.zeros(4, 1, 16, 80, dtype=torch.bfloat16)
+    bt32 = torch.zeros(Bq, 4, dtype=torch.int32)
+    ctx32 = torch.ones(Bq, dtype=torch.int32)
+    w = _host_weights(cfg)
+    with pytest.raises(B.MlaError, match="block_table must have dtype torch.int32"):
+        B.mla_decode_attn_absorbed(cfg, w, q, cache, bt32.long(), ctx32, o)
+    with pytest.raises(B.MlaError, match="context_lens must have dtype torch.int32"):
+        B.mla_decode_attn_absorbed(cfg, w, q, cache, bt32, ctx32.long(), o)
+    x = torch.zeros(Bq, cfg.hidden, dtype=torch.bfloat16)
+    cs = torch.zeros(Bq, 8, dtype=torch.float32)
+    with pytest.raises(B.MlaError, match="slot_mapping must have dtype torch.int32"):
+        B.mla_decode_qkv_and_scatter(cfg, w, x, cs, cs, cache, torch.zeros(Bq, dtype=torch.int64), q)
+    with pytest.raises(B.MlaError, match="block_table must have dtype torch.int32"):
+        B.mla_prefill_attn_paged(cfg, w, q, cache, torch.zeros(4, dtype=torch.int64), 0, o)
+
+
+def test_binding_rejects_wrong_act_dtype_and_sizes():
+    cfg = _bf16_cfg()
+    w = _host_weights(cfg)
+    T, H = 5, cfg.n_heads
+    q = torch.zeros(T, H, 48, dtype=torch.bfloat16)
+    k = torch.zeros(T, H, 48, dtype=torch.bfloat16)
+    v = torch.zeros(T, H, 32, dtype=torch.bfloat16)
+    with pytest.raises(B.MlaError, match="q must have dtype torch.bfloat16"):
+        B.mla_prefill_attn(cfg, q.float(), k, v, v.clone())
+    with pytest.raises(B.MlaError, match="o must have 640 elements"):
+        B.mla_prefill_attn(cfg, q, k, v, v[:4].clone())
+    with pytest.raises(B.MlaError, match="y must have shape"):
+        B.mla_out_proj(cfg, w, v.reshape(T, -1), torch.zeros(T, 255, dtype=torch.bfloat16))
+    x = torch.zeros(T, cfg.hidden, dtype=torch.bfloat16)
+    cs = torch.zeros(T, 8, dtype=torch.float32)
+    with pytest.raises(B.MlaError, match="x must have dtype torch.bfloat16"):
+        B.mla_qkv_prefill(cfg, w, x.float(), cs, cs, q, k, v)
+    with pytest.raises(B.MlaError, match="cos must have 40 elements"):
+        B.mla_qkv_prefill(cfg, w, x, cs[:4], cs, q, k, v)
+    # the cache must be [n_blocks, 1, block_size, kv_lora + rope]: a flat [slots, row] view is refused
+    bt = torch.zeros(T, 2, dtype=torch.int32)
+    ctx = torch.ones(T, dtype=torch.int32)
+    flat = torch.zeros(64, 80, dtype=torch.bfloat16)
+    with pytest.raises(B.MlaError, match="kv_cache must have shape"):
+        B.mla_decode_attn_absorbed(cfg, w, q, flat, bt, ctx, v)
+    with pytest.raises(B.MlaError, match="kv_cache must have shape"):
+        B.mla_decode_attn_absorbed(cfg, w, q, torch.zeros(4, 1, 32, 80, dtype=torch.bfloat16), bt, ctx, v)
+
+
+def test_binding_rejects_mismatched_weights():
+    cfg = _bf16_cfg()
+    T, H = 5, cfg.n_heads
+    v = torch.zeros(T, H, 32, dtype=torch.bfloat16)
+    y = torch.zeros(T, cfg.hidden, dtype=torch.bfloat16)
+    with pytest.raises(B.MlaError, match="wo must have shape"):
+        B.mla_out_proj(cfg, _host_weights(cfg, wo=torch.zeros(128, 255, dtype=torch.bfloat16)), v, y)
+    with pytest.raises(B.MlaError, match="wo must have dtype"):
+        B.mla_out_proj(cfg, _host_weights(cfg, wo=torch.zeros(128, 256, dtype=torch.float32)), v, y)
+    cfg8 = mla.config(256, 4, 64, 64, 32, 16, 32, act="bf16", weight="fp8", block_size=16, softmax_scale=0.1)
+    w8 = _host_weights(cfg8, wo=torch.zeros(128, 256, dtype=torch.uint8))
+    with pytest.raises(B.MlaError, match="wo scale is required"):
+        B.mla_out_proj(cfg8, w8, v, y)
