@@ -92,6 +92,7 @@ __global__ __launch_bounds__(512) void row_builder_kernel(
     T* __restrict__ cache, int64_t n_slots, const int32_t* __restrict__ slot_mapping, T* __restrict__ kbuf, int H,
     int dn) {
   __shared__ float red[16];
+  __shared__ __attribute__((aligned(16))) float kpe_row[256];  // dr <= 256 elements (fp32 or bf16)
   const int t = blockIdx.x;
   const int R = Lkv + dr, dqk = dn + dr;
   const int nt = blockDim.x;
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(512) void row_builder_kernel(
   }
   for (int i = threadIdx.x + kRowCache * nt; i < Lkv; i += nt) put(i, part_ld(Ykv, t, i));
   const int half = dr >> 1;
+  T* kpe = (T*)kpe_row;  // the roped k_pe of this token, for the broadcast below
   for (int i = threadIdx.x; i < half; i += nt) {
     const float c = cosT[(size_t)t * half + i], sn = sinT[(size_t)t * half + i];
     const float x0 = part_ld(Ykv, t, Lkv + 2 * i), x1 = part_ld(Ykv, t, Lkv + 2 * i + 1);
@@ -159,11 +161,27 @@ __global__ __launch_bounds__(512) void row_builder_kernel(
       Act<T>::st(cache, (size_t)slot * R + Lkv + 2 * i + 1, y1);
     }
     if (kbuf) {
-      for (int h = 0; h < H; ++h) {
-        const size_t base = ((size_t)t * H + h) * dqk + dn + 2 * i;
-        Act<T>::st(kbuf, base, y0);
-        Act<T>::st(kbuf, base + 1, y1);
-      }
+      Act<T>::st(kpe, 2 * i, y0);
+      Act<T>::st(kpe, 2 * i + 1, y1);
+    }
+  }
+  if (!kbuf) return;
+  // k_pe broadcast into every head's key: k[t, h, dn : dn + dr] = k_pe.  With 16-byte aligned
+  // head slices every thread writes whole 16-byte chunks (H * dr / chunk stores per token);
+  // otherwise one element per thread and step.
+  __syncthreads();
+  constexpr int kPer = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  T* krow = kbuf + (size_t)t * H * dqk + dn;
+  if (dr % kPer == 0 && dqk % kPer == 0 && dn % kPer == 0 && ((uintptr_t)kbuf & 15) == 0) {
+    const int cpr = dr / kPer;  // chunks per head
+    for (int e = threadIdx.x; e < H * cpr; e += nt) {
+      const int h = e / cpr, c = e - h * cpr;
+      *(uint4*)(krow + (size_t)h * dqk + c * kPer) = *(const uint4*)(kpe + c * kPer);
+    }
+  } else {
+    for (int e = threadIdx.x; e < H * dr; e += nt) {
+      const int h = e / dr, i = e - h * dr;
+      krow[(size_t)h * dqk + i] = kpe[i];
     }
   }
 }
