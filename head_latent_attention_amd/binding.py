@@ -23,8 +23,9 @@ FN_QKV_PREFILL, FN_PREFILL_ATTN, FN_DECODE_QKV, FN_DECODE_ATTN, FN_OUT_PROJ, FN_
 _DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 SYMBOLS = ("mla_qkv_prefill", "mla_prefill_attn", "mla_decode_qkv_and_scatter", "mla_decode_attn_absorbed",
            "mla_out_proj", "mla_prefill_attn_paged", "mla_quantize_fp8", "mla_rope_inv_freq", "mla_rope_tables",
-           "mla_workspace_size", "mla_status_string", "mla_rope_score_scale")
-_STATUS_FNS = SYMBOLS[:9]
+           "mla_decode_attn_absorbed_noalloc", "mla_workspace_size", "mla_status_string", "mla_rope_score_scale")
+_STATUS_FNS = SYMBOLS[:10]
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_MIB of include/mla.h
 
 
 class MlaError(RuntimeError):
@@ -77,6 +78,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_attn_absorbed.argtypes = [C, W, P, I32, P, I64, P, I32, P, P, P, SZ, P]
     lib.mla_out_proj.argtypes = [C, W, P, I32, P, P, SZ, P]
     lib.mla_prefill_attn_paged.argtypes = [C, W, P, I32, P, I64, P, I32, I32, P, P, SZ, P]
+    lib.mla_decode_attn_absorbed_noalloc.argtypes = [C, W, P, I32, P, I64, P, I32, P, P, P]
     lib.mla_quantize_fp8.argtypes = [P, I32, I32, I64, P, P, P]
     lib.mla_rope_inv_freq.argtypes = [POINTER(MlaRope), I32, P, P]
     lib.mla_rope_tables.argtypes = [I32, I32, P, I32, P, P, P, P]
@@ -349,6 +351,22 @@ def mla_decode_attn_absorbed(cfg, w: Weights, q, kv_cache, block_table, context_
     _check(load().mla_decode_attn_absorbed(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(q), B, _ptr(kv_cache),
                                            kv_cache.shape[0], _ptr(block_table), max_blocks, _ptr(context_lens),
                                            _ptr(o), _ptr(ws), nb, _stream(stream)))
+
+
+def mla_decode_attn_absorbed_noalloc(cfg, w: Weights, q, kv_cache, block_table, context_lens, o, stream=None):
+    """mla_decode_attn_absorbed on the library's static scratch (no workspace argument, nothing
+    allocated); calls overlapping on one GPU race."""
+    act = _act_dtype(cfg)
+    _need(block_table, "block_table", torch.int32, shape=(None, None))
+    B, max_blocks = block_table.shape
+    _need(context_lens, "context_lens", torch.int32, numel=B)
+    _need(q, "q", act, numel=B * cfg.n_heads * (cfg.qk_nope + cfg.qk_rope))
+    _need(o, "o", act, numel=B * cfg.n_heads * cfg.v_dim)
+    _need_cache(cfg, kv_cache)
+    w.check(cfg, ("wkv_b",))
+    _check(load().mla_decode_attn_absorbed_noalloc(ctypes.byref(cfg), ctypes.byref(w.struct), _ptr(q), B,
+                                                   _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table), max_blocks,
+                                                   _ptr(context_lens), _ptr(o), _stream(stream)))
 
 
 def mla_prefill_attn_paged(cfg, w: Weights, q, kv_cache, block_table, prefix_len: int, o, ws=None, stream=None):

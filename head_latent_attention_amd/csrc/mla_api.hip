@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstdio>
+#include <mutex>
 
 #include "mla.h"
 #include "mla_kernels.h"
@@ -191,6 +192,32 @@ size_t out_proj_ws(const Dims& d, int M, void* base, float** Y, void** qz = null
   return c.used;
 }
 
+// Scratch of mla_decode_attn_absorbed_noalloc: file-scope device memory, one copy per GPU for
+// the life of the process.  Host code never uses the symbol's name as an address; the address
+// is looked up once per device (hipGetSymbolAddress with that device current) and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)MLA_NOALLOC_SCRATCH_MIB << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 mla_status hip_status(hipError_t e) {
   if (e != hipSuccess) {
     if (std::getenv("MLA_TRACE")) std::fprintf(stderr, "mla: HIP error %s\n", hipGetErrorString(e));
@@ -278,6 +305,43 @@ bool check_weights_front(const Dims& d, const mla_weights* w) {
   if (!w) return false;
   if (d.Lq > 0 && (!check_weight(d, w->wq_a) || !w->q_norm_w)) return false;
   return check_weight(d, w->wq_b) && check_weight(d, w->wkv_a) && w->kv_norm_w != nullptr;
+}
+
+// Shared by mla_decode_attn_absorbed and its no-alloc variant: validation, then the launches on
+// the given workspace, or on the static scratch when use_scratch is set (ws and ws_bytes ignored).
+mla_status decode_attn_entry(const mla_config* cfg, const mla_weights* w, const void* q, int32_t B,
+                             const void* kv_cache, int64_t n_blocks, const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* context_lens, void* o, void* ws, size_t ws_bytes, bool use_scratch,
+                             void* stream) {
+  Dims d;
+  mla_status st = check_cfg(cfg, &d);
+  if (st != MLA_OK) return st;
+  if (B <= 0 || !w || !q || !kv_cache || n_blocks <= 0 || !block_table || max_blocks <= 0 || !context_lens ||
+      !o || !check_weight(d, w->wkv_b))
+    return MLA_ERR_INVALID_ARG;
+  const int64_t max_ctx64 = (int64_t)max_blocks * d.bs;
+  if (max_ctx64 > (1 << 30)) return MLA_ERR_UNSUPPORTED;
+  const int max_ctx = (int)max_ctx64;
+  if (use_scratch) {
+    if (decode_attn_ws(d, B, max_ctx, nullptr, nullptr) > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+    HIP_TRY(scratch_address(&ws));
+    ws_bytes = kNoAllocScratchBytes;
+  }
+  DecodeAttnWs L;
+  const size_t need = decode_attn_ws(d, B, max_ctx, ws, &L);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const WeightView wkv_b = view(d, w->wkv_b, (int64_t)d.H * (d.dn + d.dv));
+  if (fast_decode_supported(d)) {
+    HIP_TRY(fast_decode_attn(d, q, B, kv_cache, n_blocks, block_table, max_blocks, max_blocks, context_lens,
+                             wkv_b, o, L.fast, s));
+    return MLA_OK;
+  }
+  HIP_TRY(fold_simt(d, q, B, wkv_b, L.Qabs, s));
+  HIP_TRY(decode_attn_simt(d, L.Qabs, B, kv_cache, n_blocks, block_table, max_blocks, max_blocks, context_lens,
+                           L.nsplit, L.chunk, L.part_o, L.part_ml, s));
+  HIP_TRY(combine_simt(d, B, L.nsplit, L.part_o, L.part_ml, wkv_b, o, s));
+  return MLA_OK;
 }
 
 }  // namespace
@@ -414,30 +478,15 @@ mla_status mla_decode_attn_absorbed(const mla_config* cfg, const mla_weights* w,
                                     const int32_t* block_table, int32_t max_blocks,
                                     const int32_t* context_lens, void* o, void* ws,
                                     size_t ws_bytes, void* stream) {
-  Dims d;
-  mla_status st = check_cfg(cfg, &d);
-  if (st != MLA_OK) return st;
-  if (B <= 0 || !w || !q || !kv_cache || n_blocks <= 0 || !block_table || max_blocks <= 0 || !context_lens ||
-      !o || !check_weight(d, w->wkv_b))
-    return MLA_ERR_INVALID_ARG;
-  const int64_t max_ctx64 = (int64_t)max_blocks * d.bs;
-  if (max_ctx64 > (1 << 30)) return MLA_ERR_UNSUPPORTED;
-  const int max_ctx = (int)max_ctx64;
-  DecodeAttnWs L;
-  const size_t need = decode_attn_ws(d, B, max_ctx, ws, &L);
-  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  const WeightView wkv_b = view(d, w->wkv_b, (int64_t)d.H * (d.dn + d.dv));
-  if (fast_decode_supported(d)) {
-    HIP_TRY(fast_decode_attn(d, q, B, kv_cache, n_blocks, block_table, max_blocks, max_blocks, context_lens,
-                             wkv_b, o, L.fast, s));
-    return MLA_OK;
-  }
-  HIP_TRY(fold_simt(d, q, B, wkv_b, L.Qabs, s));
-  HIP_TRY(decode_attn_simt(d, L.Qabs, B, kv_cache, n_blocks, block_table, max_blocks, max_blocks, context_lens,
-                           L.nsplit, L.chunk, L.part_o, L.part_ml, s));
-  HIP_TRY(combine_simt(d, B, L.nsplit, L.part_o, L.part_ml, wkv_b, o, s));
-  return MLA_OK;
+  return decode_attn_entry(cfg, w, q, B, kv_cache, n_blocks, block_table, max_blocks, context_lens, o, ws, ws_bytes,
+                           false, stream);
+}
+
+mla_status mla_decode_attn_absorbed_noalloc(const mla_config* cfg, const mla_weights* w, const void* q, int32_t B,
+                                            const void* kv_cache, int64_t n_blocks, const int32_t* block_table,
+                                            int32_t max_blocks, const int32_t* context_lens, void* o, void* stream) {
+  return decode_attn_entry(cfg, w, q, B, kv_cache, n_blocks, block_table, max_blocks, context_lens, o, nullptr, 0,
+                           true, stream);
 }
 
 mla_status mla_prefill_attn_paged(const mla_config* cfg, const mla_weights* w, const void* q, int32_t T,

@@ -229,6 +229,23 @@ mla_status mla_decode_attn_absorbed(const mla_config* cfg, const mla_weights* w,
                                     const int32_t* context_lens, void* o, void* ws,
                                     size_t ws_bytes, void* stream);
 
+/* mla_decode_attn_absorbed for callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments (minus ws / ws_bytes), same kernels and the same results bit for bit.  Scratch comes
+ * from a static device array of MLA_NOALLOC_SCRATCH_MIB MiB that the library holds on every GPU it
+ * runs on until the process ends; no call allocates or frees anything.  A call whose workspace
+ * need, mla_workspace_size(cfg, MLA_FN_DECODE_ATTN, B, max_blocks * block_size), exceeds that
+ * capacity returns MLA_ERR_WORKSPACE before any launch (at the V3 shape, 128 heads, the limit is
+ * B <= 119, for any context length).  Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and give wrong results;
+ * calls ordered on one stream are safe.  Nothing in the array has to start at any value: every
+ * byte a call reads was written earlier in the same call. */
+#define MLA_NOALLOC_SCRATCH_MIB 64
+mla_status mla_decode_attn_absorbed_noalloc(const mla_config* cfg, const mla_weights* w, const void* q,
+                                            int32_t B, const void* kv_cache, int64_t n_blocks,
+                                            const int32_t* block_table, int32_t max_blocks,
+                                            const int32_t* context_lens, void* o, void* stream);
+
 /* Chunked prefill over a paged prefix: causal attention of T new tokens of one sequence over
  * that sequence's latent cache, in the absorbed form ([MlaWeights] w_uk_block_diag /
  * w_uv_block_diag: query absorption and value extraction used for prefill too; [NKI-Decode]

@@ -228,3 +228,22 @@ def test_binding_rejects_mismatched_weights():
     w8 = _host_weights(cfg8, wo=torch.zeros(128, 256, dtype=torch.uint8))
     with pytest.raises(B.MlaError, match="wo scale is required"):
         B.mla_out_proj(cfg8, w8, v, y)
+
+
+def test_noalloc_entry_point_validates_before_launch():
+    """The no-alloc decode attention refuses bad arguments and batches beyond its static scratch
+    with a status, before touching HIP."""
+    lib = mla.load()
+    cfg = mla.config(7168, 128, 1536, 512, 128, 64, 128, softmax_scale=0.072)
+    W = B.MlaWeights()
+    W.wkv_b = B.MlaWeight(1, None)
+
+    def call(Bn=4, max_blocks=8, q=1, w=W):
+        return lib.mla_decode_attn_absorbed_noalloc(ctypes.byref(cfg), ctypes.byref(w), q, Bn, 1, 64, 1, max_blocks,
+                                                    1, 1, None)
+    assert call(Bn=0) == -1
+    assert call(q=None) == -1
+    assert call(w=B.MlaWeights()) == -1
+    assert B.workspace_size(cfg, B.FN_DECODE_ATTN, 130, 512) > B.NOALLOC_SCRATCH_BYTES
+    assert call(Bn=130) == -3
+    assert B.workspace_size(cfg, B.FN_DECODE_ATTN, 119, 1 << 20) <= B.NOALLOC_SCRATCH_BYTES
