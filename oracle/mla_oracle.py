@@ -134,9 +134,11 @@ def quantize_mx_fp8(x: np.ndarray, group: int = 128):
 
 def _act(a: np.ndarray, dims: dict) -> np.ndarray:
     """An activation as a projection consumes it: fp8-quantised and dequantised when the
-    layer quantises activations (dims["act_quant"]), else unchanged.  The quantiser sees the
-    activation as the layer stores it, a bfloat16 value: each code is a decision taken in
-    floating point, made here in the same precision as on the device."""
+    layer quantises activations (dims["act_quant"]), else unchanged.  The quantiser sees a
+    bfloat16 tensor: the MX projection of "QKV CTE MLA Kernel API Reference" (qkv_mla_mx,
+    Parameters and Returns) keeps x, the normed Q and KV intermediates (their RMSNorm gammas
+    are bf16) and every output in bf16, so each input it quantises is a bf16 value.  Each
+    code is a decision taken in floating point, made here on that same bf16 value."""
     if not dims.get("act_quant"):
         return a
     shape = a.shape
