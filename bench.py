@@ -10,7 +10,8 @@ causal prefill (8192 tokens) TFLOP/s, the latent-cache GB/s, the roofline of the
 dominant kernel (the absorbed decode attention) and the CPU oracle baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-chunk] [--no-fp8]
-                       [--no-decode-fp8] [--no-cpu] [--no-graph]
+                       [--no-decode-fp8] [--no-cpu] [--no-peaks] [--no-cold] [--no-graph]
+                       [--only peaks|decode|prefill|prefill_c2|prefill_fp8|decode_fp8|chunk|cpu]
 """
 from __future__ import annotations
 
@@ -199,7 +200,11 @@ def run_prefill(w, reps):
     wall = (time.perf_counter() - t0) / reps
     D, H, Lq, Lkv, dn, dr, dv = s.hidden, s.n_heads, s.q_lora_rank, s.kv_lora_rank, s.qk_nope, s.qk_rope, s.v_dim
     pairs = T * (T + 1) // 2
-    f_qkv = 2 * T * D * (Lq + Lkv + dr) + 2 * T * Lq * H * (dn + dr) + 2 * T * Lkv * H * (dn + dv)
+    if Lq > 0:   # x @ [wq_a | wkv_a], then the q latent @ wq_b
+        f_qkv = 2 * T * D * (Lq + Lkv + dr) + 2 * T * Lq * H * (dn + dr)
+    else:        # x @ [wq | wkv_a]: the full query projection
+        f_qkv = 2 * T * D * (H * (dn + dr) + Lkv + dr)
+    f_qkv += 2 * T * Lkv * H * (dn + dv)
     f_attn = 2 * pairs * H * (dn + dr + dv)
     f_out = 2 * T * H * dv * D
     tq, ta, to = tq / reps, ta / reps, to / reps
@@ -302,34 +307,137 @@ def cpu_baseline(w, S, budget_s=12.0):
                       f"{el:.1f} s of float64 numpy; time scaled by total rows to the full batch"}
 
 
-def run_decode_leg(w, steps, warmup, device_fill):
-    """Graph-replayed decode steps of workload w, plus an eager pass with events per entry point."""
+def attn_call(S):
+    S["mla"].mla_decode_attn_absorbed(S["cfg"], S["dw"], S["q"], S["cache"], S["bt"], S["cl"], S["o"],
+                                      ws=S["ws"]["attn"])
+
+
+def decode_parts(S):
+    """The decode step as three callables: front end (rope tables + projections + scatter),
+    absorbed attention, output projection."""
+    mla = S["mla"]
+
+    def front():
+        mla.mla_rope_tables(S["cl"], S["cl"].numel(), S["cfg"].qk_rope, None, pos_offset=-1, cos=S["cos"],
+                            sin=S["sin"])
+        mla.mla_decode_qkv_and_scatter(S["cfg"], S["dw"], S["x"], S["cos"], S["sin"], S["cache"], S["slot"], S["q"],
+                                       ws=S["ws"]["qkv"])
+
+    def out():
+        mla.mla_out_proj(S["cfg"], S["dw"], S["o"], S["y"], ws=S["ws"]["out"])
+    return front, (lambda: attn_call(S)), out
+
+
+def graph_of(fn):
     import torch
-    S = decode_setup(w, device_fill=device_fill)
-    torch.cuda.synchronize()
-    for _ in range(warmup):
-        decode_step(S)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        decode_step(S, evs[i])
-    torch.cuda.synchronize()
-    t_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        decode_step(S)
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+COLD_BYTES = 512 << 20   # written between cold steps: more than the 256 MB last-level cache
+
+
+def run_decode_leg(w, steps, warmup, device_fill, graphs=True, cold=True):
+    """Decode steps of workload w, in three timed regions of `steps` steps each:
+    1. the step as a serving loop runs it, one HIP graph replay per step (eager launches with
+       graphs=False), launched back to back and bracketed by synchronisations: the step time;
+    2. each step as three replays (front end, attention, output projection) with HIP events
+       between them on the launch stream: each part's duration;
+    3. region 2 with a 512 MB write before every step, outside the events: cold-cache medians."""
+    import torch
+    S = decode_setup(w, device_fill=device_fill)
+    parts = decode_parts(S)
     torch.cuda.synchronize()
     for _ in range(warmup):
-        g.replay()
+        decode_step(S)
+    torch.cuda.synchronize()
+    step = graph_of(lambda: decode_step(S)).replay if graphs else (lambda: decode_step(S))
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        g.replay()
+        step()
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    res = dict(S=S, ctx=S["ctx"], ms_step=(time.perf_counter() - t0) * 1e3 / steps)
+    calls = [graph_of(p).replay for p in parts] if graphs else list(parts)
+    for _ in range(warmup):
+        for c in calls:
+            c()
+
+    def timed(n, before=None):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for e in ev:
+            if before:
+                before()
+            e[0].record()
+            for j, c in enumerate(calls):
+                c()
+                e[j + 1].record()
+        torch.cuda.synchronize()
+        return np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])
+
+    per = timed(steps)
+    res.update(t_qkv=float(per[:, 0].mean()), t_attn=float(per[:, 1].mean()), t_out=float(per[:, 2].mean()))
     s = w.shape
-    cache_b, attn_b = attn_algorithmic_bytes(s, S["ctx"], w.B)
-    return dict(ms_step=ms_step, t_attn=t_attn, cache_b=cache_b, attn_b=attn_b, ctx=S["ctx"])
+    res["cache_b"], res["attn_b"] = attn_algorithmic_bytes(s, S["ctx"], w.B)
+    if cold:
+        scratch = torch.empty(COLD_BYTES // 4, dtype=torch.int32, device="cuda")
+        k = [0]
+
+        def evict():
+            k[0] += 1
+            scratch.fill_(k[0])
+        pc = timed(steps, before=evict)
+        del scratch
+        res["cold"] = dict(ms_step=float(np.median(pc.sum(axis=1))), t_qkv=float(np.median(pc[:, 0])),
+                           t_attn=float(np.median(pc[:, 1])), t_out=float(np.median(pc[:, 2])))
+    return res
+
+
+def decode_summary(w, d, peaks=None):
+    """JSON fields of a decode leg."""
+    s = w.shape
+    step_b = d["attn_b"] + weight_bytes(s, ["wq_a", "wkv_a", "wq_b", "wo"])
+    out = {"tok_per_s": round(w.B / (d["ms_step"] * 1e-3), 2), "ms_per_step": round(d["ms_step"], 4),
+           "context_tokens": int(d["ctx"].sum()),
+           "ms_decode_qkv": round(d["t_qkv"], 4), "ms_decode_attn": round(d["t_attn"], 4),
+           "ms_out_proj": round(d["t_out"], 4),
+           "latent_cache_GBps": round(d["cache_b"] / (d["t_attn"] * 1e-3) / 1e9, 1),
+           "attn_frac_hbm_peak": round(d["attn_b"] / (d["t_attn"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "step_algorithmic_GBps": round(step_b / (d["ms_step"] * 1e-3) / 1e9, 1)}
+    if "cold" in d:
+        c = d["cold"]
+        out["cold"] = {"note": f"{COLD_BYTES >> 20} MB written before every step, outside the timed events; medians",
+                       "ms_per_step": round(c["ms_step"], 4), "tok_per_s": round(w.B / (c["ms_step"] * 1e-3), 2),
+                       "ms_decode_qkv": round(c["t_qkv"], 4), "ms_decode_attn": round(c["t_attn"], 4),
+                       "ms_out_proj": round(c["t_out"], 4),
+                       "latent_cache_GBps": round(d["cache_b"] / (c["t_attn"] * 1e-3) / 1e9, 1),
+                       "attn_frac_hbm_peak": round(d["attn_b"] / (c["t_attn"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if peaks:
+        out["attn_frac_measured_read_peak"] = round(d["attn_b"] / (d["t_attn"] * 1e-3) / 1e9 / peaks["read_GBps"], 4)
+    return out
+
+
+def prefill_summary(pf, workload, peaks=None):
+    out = {"workload": workload, "ms": round(pf["ms"], 3), "ms_qkv": round(pf["ms_qkv"], 3),
+           "ms_attn": round(pf["ms_attn"], 3), "ms_out_proj": round(pf["ms_out"], 3),
+           "TFLOPs": round(pf["tflops"], 2), "attn_TFLOPs": round(pf["attn_tflops"], 2),
+           "projection_TFLOPs": round(pf["proj_tflops"], 2),
+           "frac_bf16_peak": round(pf["tflops"] / BF16_PEAK_TFLOPS, 4),
+           "attn_frac_bf16_peak": round(pf["attn_tflops"] / BF16_PEAK_TFLOPS, 4),
+           "causal_counted_flops": pf["flops"]}
+    if peaks:
+        m = max(peaks["mfma_bf16_16_TFLOPs"], peaks["mfma_bf16_32_TFLOPs"])
+        out["frac_measured_mfma_peak"] = round(pf["tflops"] / m, 4)
+    return out
+
+
+LEGS = ("peaks", "decode", "prefill", "prefill_c2", "prefill_fp8", "decode_fp8", "chunk", "cpu")
 
 
 def main():
@@ -338,12 +446,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--prefill-reps", type=int, default=3)
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the V3 and V2-Lite bf16 prefill legs")
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-decode-fp8", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--only", choices=LEGS, help="run one leg and print its JSON object (profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for HBM traffic)")
     args = ap.parse_args()
@@ -363,124 +474,135 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel() * 4}))
         return
+    want = (lambda leg: leg == args.only) if args.only else (lambda leg: {
+        "peaks": not args.no_peaks, "decode": True, "prefill": not args.no_prefill,
+        "prefill_c2": not args.no_prefill, "prefill_fp8": not args.no_fp8, "decode_fp8": not args.no_decode_fp8,
+        "chunk": not args.no_chunk, "cpu": not args.no_cpu}[leg])
+    out = {}
+    peaks = None
+    if want("peaks"):
+        from head_latent_attention_amd import measure
+        log("[bench] measured peaks: streaming read, copy, bf16 matrix-op loop")
+        peaks = measure.measure()
+        if args.only:
+            print(json.dumps({"leg": "peaks", **peaks}), flush=True)
+            return
+    graphs = not args.no_graph
     w = synth.WORKLOADS[3]
     s = w.shape
-    log(f"[bench] setting up {w.name}")
-    S = decode_setup(w)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        decode_step(S)
-    torch.cuda.synchronize()
-    # per-entry-point breakdown: eager steps with HIP events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} eager decode steps (per entry point)")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        decode_step(S, evs[i])
-    torch.cuda.synchronize()
-    wall_eager = time.perf_counter() - t0
-    t_qkv = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    t_attn = np.mean([e[1].elapsed_time(e[2]) for e in evs])
-    t_out = np.mean([e[2].elapsed_time(e[3]) for e in evs])
-    ms_eager = wall_eager * 1e3 / args.steps
-    # the step as a serving loop runs it: one HIP graph of the three entry points, replayed
-    launch = "eager"
-    ms_step = ms_eager
-    if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            decode_step(S)
-        torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            g.replay()
-        log(f"[bench] timing {args.steps} decode steps (graph replays)")
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
-        torch.cuda.synchronize()
-        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        launch = "hip graph of the three entry points, replayed once per step"
-    cache_b, attn_b = attn_algorithmic_bytes(s, S["ctx"], w.B)
-    step_bytes = attn_b + weight_bytes(s, ["wq_a", "wkv_a", "wq_b", "wo"])
-    achieved = attn_b / (t_attn * 1e-3) / 1e9
-    traffic = traffic_from_profiles("decode_attn")
-    out = {
-        "metric": "decode tok/s (V3-shaped MLA layer, B=64)",
-        "value": round(w.B / (ms_step * 1e-3), 2),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; random-init weights N(0,0.02); cache rows c~N(0,1), k_pe~N(0,1.7^2))",
-        "config": {"workload": "v3-decode-b64: DeepSeek-V3-shaped MLA decode step, bf16, B=64, "
-                               "ctx~U[1024,8192], paged cache block_size 64",
-                   "batch": w.B, "context_tokens": int(S["ctx"].sum()), "hidden": s.hidden, "heads": s.n_heads,
-                   "q_lora_rank": s.q_lora_rank, "kv_lora_rank": s.kv_lora_rank, "qk_nope": s.qk_nope,
-                   "qk_rope": s.qk_rope, "v_dim": s.v_dim, "block_size": s.block_size},
-        "launch": launch,
-        "ms_per_step_eager": round(ms_eager, 4),
-        "ms_decode_qkv": round(float(t_qkv), 4),
-        "ms_decode_attn": round(float(t_attn), 4),
-        "ms_out_proj": round(float(t_out), 4),
-        "latent_cache_GBps": round(cache_b / (t_attn * 1e-3) / 1e9, 1),
-        "step_algorithmic_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "roofline": {"kernel": "mla_decode_attn_absorbed", "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": attn_b},
-    }
-    if not args.no_prefill:
+    if want("decode") or want("cpu"):
+        log(f"[bench] {w.name}: {args.steps} decode steps")
+        d = run_decode_leg(w, args.steps, args.warmup, device_fill=False, graphs=graphs,
+                           cold=not args.no_cold)
+        S = d["S"]
+        ds = decode_summary(w, d, peaks)
+        achieved = d["attn_b"] / (d["t_attn"] * 1e-3) / 1e9
+        traffic = traffic_from_profiles("decode_attn")
+        roofline = {"kernel": "mla_decode_attn_absorbed (plan+fold, attention, combine kernels)", "bound": "hbm",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes_per_launch": d["attn_b"]}
+        if peaks:
+            roofline["measured_read_peak"] = peaks["read_GBps"]
+            roofline["frac_of_measured_read_peak"] = round(achieved / peaks["read_GBps"], 4)
+        if args.only == "decode":
+            print(json.dumps({"leg": "decode", **ds, "roofline": roofline}), flush=True)
+            return
+        out = {
+            "metric": "decode tok/s (V3-shaped MLA layer, B=64)",
+            "value": ds["tok_per_s"],
+            "unit": "tok/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ds["ms_per_step"],
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic (seeded; random-init weights N(0,0.02); cache rows c~N(0,1), k_pe~N(0,1.7^2))",
+            "config": {"workload": "v3-decode-b64: DeepSeek-V3-shaped MLA decode step, bf16, B=64, "
+                                   "ctx~U[1024,8192], paged cache block_size 64",
+                       "batch": w.B, "context_tokens": ds["context_tokens"], "hidden": s.hidden,
+                       "heads": s.n_heads, "q_lora_rank": s.q_lora_rank, "kv_lora_rank": s.kv_lora_rank,
+                       "qk_nope": s.qk_nope, "qk_rope": s.qk_rope, "v_dim": s.v_dim, "block_size": s.block_size},
+            "launch": ("one HIP graph of the three entry points, replayed once per step; the per-entry-point "
+                       "times come from a second region of three graph replays per step with HIP events between "
+                       "them on the launch stream" if graphs else "eager launches"),
+            **{k: v for k, v in ds.items() if k not in ("tok_per_s", "ms_per_step", "context_tokens")},
+            "roofline": roofline,
+        }
+        if peaks:
+            out["measured_peaks"] = peaks
+    if want("prefill"):
         log("[bench] V3 prefill, T=8192")
         pf = run_prefill(synth.WORKLOADS[4], args.prefill_reps)
-        out["prefill_TFLOPs"] = round(pf["tflops"], 2)
-        out["prefill"] = {"workload": "v3-prefill-8192", "ms": round(pf["ms"], 3),
-                          "ms_qkv": round(pf["ms_qkv"], 3), "ms_attn": round(pf["ms_attn"], 3),
-                          "ms_out_proj": round(pf["ms_out"], 3), "attn_TFLOPs": round(pf["attn_tflops"], 2),
-                          "frac_bf16_peak": round(pf["tflops"] / BF16_PEAK_TFLOPS, 4),
-                          "causal_counted_flops": pf["flops"]}
-    if not args.no_fp8:
+        ps = prefill_summary(pf, "v3-prefill-8192", peaks)
+        if args.only:
+            print(json.dumps({"leg": "prefill", **ps}), flush=True)
+            return
+        out["prefill_TFLOPs"] = ps["TFLOPs"]
+        out["prefill"] = ps
+    if want("prefill_c2"):
+        w2 = synth.WORKLOADS[2]
+        log(f"[bench] {w2.name}: V2-Lite prefill, T={w2.T}, full query projection")
+        p2 = run_prefill(w2, args.prefill_reps)
+        ps2 = prefill_summary(p2, f"{w2.name}: DeepSeek-V2-Lite-shaped MLA prefill, bf16, T={w2.T}, "
+                                  f"{w2.shape.n_heads} heads, full query projection (no q latent)", peaks)
+        if args.only:
+            print(json.dumps({"leg": "prefill_c2", **ps2}), flush=True)
+            return
+        out["prefill_c2"] = ps2
+    if want("prefill_fp8"):
         log("[bench] V3 prefill, T=8192, fp8 weights and MX fp8 activations")
         w8 = synth.custom(synth.WORKLOADS[4], 4, "v3-prefill-8192-fp8", weight="fp8", act_quant=True)
         p8 = run_prefill(w8, args.prefill_reps)
-        out["prefill_fp8"] = {"workload": "v3-prefill-8192-fp8: E4M3 weights (power-of-two 128x128 block scales), "
-                                          "MX fp8 activations (1x128 groups) into every projection; bf16 attention",
-                              "ms": round(p8["ms"], 3), "ms_qkv": round(p8["ms_qkv"], 3),
-                              "ms_attn": round(p8["ms_attn"], 3), "ms_out_proj": round(p8["ms_out"], 3),
-                              "TFLOPs": round(p8["tflops"], 2),
-                              "projection_TFLOPs": round(p8["proj_tflops"], 2),
-                              "projection_frac_fp8_peak": round(p8["proj_tflops"] / FP8_PEAK_TFLOPS, 4)}
-    if not args.no_decode_fp8:
+        p8s = {"workload": "v3-prefill-8192-fp8: E4M3 weights (power-of-two 128x128 block scales), "
+                           "MX fp8 activations (1x128 groups) into every projection; bf16 attention",
+               "ms": round(p8["ms"], 3), "ms_qkv": round(p8["ms_qkv"], 3),
+               "ms_attn": round(p8["ms_attn"], 3), "ms_out_proj": round(p8["ms_out"], 3),
+               "TFLOPs": round(p8["tflops"], 2),
+               "projection_TFLOPs": round(p8["proj_tflops"], 2),
+               "projection_frac_fp8_peak": round(p8["proj_tflops"] / FP8_PEAK_TFLOPS, 4)}
+        if args.only:
+            print(json.dumps({"leg": "prefill_fp8", **p8s}), flush=True)
+            return
+        out["prefill_fp8"] = p8s
+    if want("decode_fp8"):
         w5 = synth.WORKLOADS[5]
         log(f"[bench] {w5.name}: V3 decode, fp8 weights, B={w5.B}")
-        d8 = run_decode_leg(w5, max(3, args.steps // 5), max(1, args.warmup // 2), device_fill=True)
-        s5 = w5.shape
-        step_b = d8["attn_b"] + weight_bytes(s5, ["wq_a", "wkv_a", "wq_b", "wo"])
-        out["decode_fp8"] = {"workload": f"{w5.name}: DeepSeek-V3-shaped MLA decode step, E4M3 weights (128x128 "
-                                         f"block scales), bf16 cache, B={w5.B}, ctx~logU[{w5.ctx_lo},{w5.ctx_hi}]",
-                             "tok_per_s": round(w5.B / (d8["ms_step"] * 1e-3), 2), "ms_per_step": round(d8["ms_step"], 4),
-                             "context_tokens": int(d8["ctx"].sum()), "ms_decode_attn": round(d8["t_attn"], 4),
-                             "latent_cache_GBps": round(d8["cache_b"] / (d8["t_attn"] * 1e-3) / 1e9, 1),
-                             "attn_frac_hbm_peak": round(d8["attn_b"] / (d8["t_attn"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                             "step_algorithmic_GBps": round(step_b / (d8["ms_step"] * 1e-3) / 1e9, 1)}
-    if not args.no_chunk:
+        n5 = max(3, args.steps // 5)
+        d8 = run_decode_leg(w5, n5, max(1, args.warmup // 2), device_fill=True, graphs=graphs,
+                            cold=not args.no_cold)
+        d8s = {"workload": f"{w5.name}: DeepSeek-V3-shaped MLA decode step, E4M3 weights (128x128 block scales), "
+                           f"bf16 cache, B={w5.B}, ctx~logU[{w5.ctx_lo},{w5.ctx_hi}]", "steps": n5,
+               **decode_summary(w5, d8, peaks)}
+        del d8
+        if args.only:
+            print(json.dumps({"leg": "decode_fp8", **d8s}), flush=True)
+            return
+        out["decode_fp8"] = d8s
+    if want("chunk"):
         prefix, T = 7168, 1024
         log(f"[bench] V3 chunked prefill, {T} tokens after {prefix}")
         ch = run_chunked(synth.WORKLOADS[4], prefix, T, args.prefill_reps)
-        out["chunked_prefill"] = {"workload": f"v3-chunk-{T}-after-{prefix}", "ms": round(ch["ms"], 3),
-                                  "ms_qkv": round(ch["ms_qkv"], 3), "ms_attn": round(ch["ms_attn"], 3),
-                                  "ms_out_proj": round(ch["ms_out"], 3), "TFLOPs": round(ch["tflops"], 2),
-                                  "attn_TFLOPs": round(ch["attn_tflops"], 2),
-                                  "frac_bf16_peak": round(ch["tflops"] / BF16_PEAK_TFLOPS, 4),
-                                  "absorbed_counted_flops": ch["flops"], "query_row_pairs": ch["pairs"]}
-    if not args.no_cpu:
+        chs = {"workload": f"v3-chunk-{T}-after-{prefix}", "ms": round(ch["ms"], 3),
+               "ms_qkv": round(ch["ms_qkv"], 3), "ms_attn": round(ch["ms_attn"], 3),
+               "ms_out_proj": round(ch["ms_out"], 3), "TFLOPs": round(ch["tflops"], 2),
+               "attn_TFLOPs": round(ch["attn_tflops"], 2),
+               "frac_bf16_peak": round(ch["tflops"] / BF16_PEAK_TFLOPS, 4),
+               "absorbed_counted_flops": ch["flops"], "query_row_pairs": ch["pairs"]}
+        if args.only:
+            print(json.dumps({"leg": "chunk", **chs}), flush=True)
+            return
+        out["chunked_prefill"] = chs
+    if want("cpu"):
         log("[bench] CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(w, S)
+        cb = cpu_baseline(w, S)
+        if args.only:
+            print(json.dumps({"leg": "cpu", **cb}), flush=True)
+            return
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

@@ -1,8 +1,9 @@
 """Compile the gfx950 MLA library (libmla.so) in-tree with hipcc.
 
 Every ``csrc/*.hip`` file is compiled for gfx950 only, then linked into
-``head_latent_attention_amd/libmla.so``.  Run as ``python -m
-head_latent_attention_amd.build`` or call :func:`build`.
+``head_latent_attention_amd/libmla.so``; the measurement probes of ``peaks/`` (streaming
+read/copy and a matrix-op loop, used by the benchmark only) go into ``libmla_peaks.so``.
+Run as ``python -m head_latent_attention_amd.build`` or call :func:`build`.
 """
 from __future__ import annotations
 
@@ -16,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
+PEAKS_SRC = os.path.join(PKG, "peaks")
+PEAKS_LIB = os.path.join(PKG, "libmla_peaks.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,12 +31,12 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder: str = CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    obj = os.path.join(BUILD, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src)[:-4] + ".o")
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
@@ -44,20 +47,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libmla.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link failed for {lib}:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libmla.so and libmla_peaks.so; returns libmla.so's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, psrcs = sources(), sources(PEAKS_SRC)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(_compile, srcs + psrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PEAKS_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources and {PEAKS_LIB} from {len(psrcs)}")
     return LIB
 
 

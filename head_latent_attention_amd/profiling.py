@@ -6,6 +6,7 @@ Usage:
   python -m head_latent_attention_amd.profiling stats RUN_kernel_stats.csv
   python -m head_latent_attention_amd.profiling summary RUN_kernel_stats.csv "TITLE" "COMMAND" > OUT.md
   python -m head_latent_attention_amd.profiling traffic FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR OUT.json
+  python -m head_latent_attention_amd.profiling counters "TITLE" "COMMANDS" DIR [DIR ...] > OUT.md
 """
 from __future__ import annotations
 
@@ -127,11 +128,80 @@ def by_grid(trace_csv: str):
     return list(groups.items())
 
 
+MOPS_FLOP = 512   # flop per unit of the SQ_INSTS_VALU_MFMA_MOPS_* counters (checked against the probe loop)
+
+
+def _short(name: str) -> str:
+    short = name.replace("(anonymous namespace)::", "").split("(")[0]
+    return short[5:] if short.startswith("void ") else short
+
+
+def counter_table(dirs):
+    """{(kernel, grid threads): {"n": dispatches, "us": mean duration, counter: mean per dispatch}}
+    over the counter_collection CSVs of several rocprofv3 --pmc runs."""
+    acc = {}
+    for d in dirs:
+        for r in _counter_rows(d):
+            if "mla::" not in r["Kernel_Name"] and "peak_" not in r["Kernel_Name"]:
+                continue   # torch's own kernels (input set-up, fills)
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            e = acc.setdefault(key, {})
+            e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            e.setdefault("_dur", {})[(d, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out = {}
+    for key, e in acc.items():
+        durs = list(e.pop("_dur").values())
+        row = {"n": len(durs), "us": sum(durs) / len(durs)}
+        for c, v in e.items():
+            row[c] = sum(v) / len(v)
+        out[key] = row
+    return out
+
+
+def counters_md(dirs, title: str, commands: str) -> str:
+    tab = counter_table(dirs)
+    names = sorted({c for r in tab.values() for c in r if c not in ("n", "us")})
+    lines = [f"# {title}", "", "Commands (run from the repository root on one MI355X, one counter pass each):", "",
+             "```", "cd /tmp && export TMPDIR=/tmp", commands, "```", "",
+             "Mean per dispatch; `us` is the dispatch duration under counter collection.", ""]
+    probe = [r for (k, g), r in tab.items() if "peak_mfma" in k and "SQ_VALU_MFMA_BUSY_CYCLES" in r]
+    probe_rate = None
+    if probe and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in probe[0]:
+        p = max(probe, key=lambda r: r["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / r["us"])
+        probe_rate = (p["SQ_VALU_MFMA_BUSY_CYCLES"] / p["us"], MOPS_FLOP * p["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / p["us"] / 1e6)
+        lines += [f"Matrix-op loop probe (no memory traffic): {probe_rate[1]:.0f} TFLOP/s bf16 from "
+                  f"{MOPS_FLOP} flop per MOPS unit; its `SQ_VALU_MFMA_BUSY_CYCLES` per us is the 'busy' reference "
+                  "below (busy = a kernel's busy cycles per us over the probe's).", ""]
+    derived = []
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names or "SQ_INSTS_VALU_MFMA_MOPS_F8" in names:
+        derived.append("MFMA TFLOP/s (hw)")
+    if probe_rate and "SQ_VALU_MFMA_BUSY_CYCLES" in names:
+        derived.append("MFMA busy vs probe")
+    head = ["kernel", "grid threads", "dispatches", "us"] + derived + names
+    lines += ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for (k, g), r in sorted(tab.items(), key=lambda kv: -kv[1]["us"] * kv[1]["n"]):
+        cells = [f"`{k if len(k) <= 60 else k[:57] + '...'}`", str(g), str(r["n"]), f"{r['us']:.1f}"]
+        if "MFMA TFLOP/s (hw)" in derived:
+            mops = r.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + r.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+            cells.append(f"{MOPS_FLOP * mops / r['us'] / 1e6:.0f}" if mops else "")
+        if "MFMA busy vs probe" in derived:
+            b = r.get("SQ_VALU_MFMA_BUSY_CYCLES")
+            cells.append(f"{b / r['us'] / probe_rate[0]:.2f}" if b is not None else "")
+        for c in names:
+            v = r.get(c)
+            cells.append("" if v is None else (f"{v:.0f}" if abs(v) >= 100 else f"{v:.3g}"))
+        lines.append("| " + " | ".join(cells) + " |")
+    lines.append("")
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "summary":
         print(summary_md(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif sys.argv[1] == "stats":
         for name, calls, avg_us, pct in kernel_stats(sys.argv[2]):
             print(f"{avg_us:10.1f} us  {calls:6d}  {pct:6.2f}%  {name[:110]}")
+    elif sys.argv[1] == "counters":
+        print(counters_md(sys.argv[4:], sys.argv[2], sys.argv[3]))
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(*sys.argv[2:7]), indent=1))

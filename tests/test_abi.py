@@ -9,11 +9,13 @@ import pytest
 import head_latent_attention_amd as mla
 from head_latent_attention_amd import binding as B
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "mla.h")
+PEAKS_HEADER = os.path.join(INCLUDE, "mla_peaks.h")
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
@@ -24,6 +26,28 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(B.SYMBOLS), names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_headers_are_all_covered():
+    assert sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h")) == ["mla.h", "mla_peaks.h"]
+
+
+def test_peak_probes_exported_and_validate():
+    """The measurement probes' library exports what its header declares and refuses bad
+    arguments before any launch."""
+    from head_latent_attention_amd import measure as M
+    lib = M.load()
+    names = _declared(PEAKS_HEADER)
+    assert set(names) == set(M.SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.mla_peak_read(None, 16, 1, 1, None) == -1
+    assert lib.mla_peak_read(16, 24, 1, 1, None) == -1           # not a multiple of 16
+    assert lib.mla_peak_read(8, 16, 1, 1, None) == -1            # misaligned
+    assert lib.mla_peak_copy(0x1000, 0x1010, 64, 1, None) == -1  # overlapping
+    assert lib.mla_peak_mfma_bf16(8, 1, 1.0, 16, 1, 256, None) == -1
+    assert lib.mla_peak_mfma_bf16(16, 1, 1.0, 16, 1, 128, None) == -1
+    assert lib.mla_peak_mfma_bf16(32, 0, 1.0, 16, 1, 256, None) == -1
 
 
 def _cfg(**kw):
