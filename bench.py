@@ -187,8 +187,7 @@ def run_prefill(w, reps):
         if rec:
             ev[3].record()
 
-    once(False)
-    torch.cuda.synchronize()
+    warm(lambda: once(False), 1)
     tq = ta = to = 0.0
     t0 = time.perf_counter()
     for _ in range(reps):
@@ -259,8 +258,7 @@ def run_chunked(w, prefix, T, reps):
         if rec:
             ev[3].record()
 
-    once(False)
-    torch.cuda.synchronize()
+    warm(lambda: once(False), 1)
     tq = ta = to = 0.0
     for _ in range(reps):
         once(True)
@@ -328,6 +326,22 @@ def decode_parts(S):
     return front, (lambda: attn_call(S)), out
 
 
+WARM_S = 0.3   # least wall time of warm-up work before a timed region (clocks ramp up under load)
+
+
+def warm(fn, n):
+    """n untimed calls of fn, then more until WARM_S seconds have passed."""
+    import torch
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < WARM_S:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def graph_of(fn):
     import torch
     g = torch.cuda.CUDAGraph()
@@ -355,18 +369,18 @@ def run_decode_leg(w, steps, warmup, device_fill, graphs=True, cold=True):
         decode_step(S)
     torch.cuda.synchronize()
     step = graph_of(lambda: decode_step(S)).replay if graphs else (lambda: decode_step(S))
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(step, warmup)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     res = dict(S=S, ctx=S["ctx"], ms_step=(time.perf_counter() - t0) * 1e3 / steps)
     calls = [graph_of(p).replay for p in parts] if graphs else list(parts)
-    for _ in range(warmup):
+
+    def all_parts():
         for c in calls:
             c()
+    warm(all_parts, warmup)
 
     def timed(n, before=None):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
@@ -515,6 +529,7 @@ def main():
             "n_gpus": 1,
             "steps": args.steps,
             "warmup": args.warmup,
+            "warmup_note": f"each timed region is preceded by its warm-up steps and then more, to at least {WARM_S} s",
             "ms_per_step": ds["ms_per_step"],
             "higher_is_better": True,
             "scaling": "weak",

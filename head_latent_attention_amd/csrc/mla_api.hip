@@ -85,7 +85,7 @@ WeightView view(const Dims& d, const mla_weight& w, int64_t N) {
 // Every projection result is kept as fp32 split-K partial sums (one part on the general
 // path) and summed by the kernel that consumes it.
 size_t proj_out_bytes(const Dims& d, int M, int N, int K) {
-  if (fast_proj_supported(d)) return fast_gemm_out_bytes(M, N, K);
+  if (fast_proj_supported(d)) return fast_gemm_out_bytes(d, M, N, K);
   return (size_t)M * N * sizeof(float);
 }
 

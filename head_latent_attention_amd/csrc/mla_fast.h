@@ -29,7 +29,7 @@ struct GemmEpilogue {
 // (fast_gemm_out_bytes(M, N, K) bytes) as split-K partial sums, described by *res; or, when
 // `epi` asks for a consumer and K is not split, written straight to it (*fused = true).
 bool fast_proj_supported(const Dims& d);
-size_t fast_gemm_out_bytes(int M, int N, int K);
+size_t fast_gemm_out_bytes(const Dims& d, int M, int N, int K);
 // whether fast_gemm hands the result of this shape straight to a consumer of `kind`
 bool fast_gemm_fusable(const Dims& d, int M, int N, int K, int n_split, int kind);
 hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split,

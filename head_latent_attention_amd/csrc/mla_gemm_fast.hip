@@ -721,6 +721,187 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
                lane);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Mid-M projection with fp8 weights (64 < M <= 1024, bf16 activations; the decode step of a
+// large batch): the 256 x 256 tile, 8-wave layout, activation stream and epilogue of
+// gemm_big_kernel, with the weights kept at one byte per element all the way into LDS.  Each K
+// step of 32 copies [32 k][256 n] E4M3 bytes (8 KB, one 16-byte copy per lane) by
+// buffer_load ... lds, four stages deep; a wave gets a B operand (8 k of one column per lane)
+// from one transposing byte read ds_read_b64_tr_b8 and decodes it in registers: E4M3 -> fp32,
+// times the 128 x 128 block scale, -> bf16 (exact for power-of-two block scales, the same
+// numbers gemm_kernel's staging produces).  The block scales of the workgroup's K range are
+// staged in LDS once, before the first copy.
+#ifndef MLA_W8_MIN_KSPLIT
+#define MLA_W8_MIN_KSPLIT 512
+#endif
+constexpr int kW8MinKSplit = MLA_W8_MIN_KSPLIT;  // least K range of one split-K part
+#ifndef MLA_W8_STAGES
+#define MLA_W8_STAGES 4
+#endif
+constexpr int kW8Stages = MLA_W8_STAGES;  // K steps in LDS (four and five measured the same;
+                                         // six spill registers)
+constexpr int kW8Copies = 3;         // per wave per stage: 2 activation + 1 weight copy of 1 KB
+constexpr int kW8MaxKBlocks = 128;   // 128-row scale blocks of one workgroup's K range
+constexpr int kW8StageA = kBigM * 4, kW8StageW = kBigK * 16;  // 16-byte chunks per stage
+// the stages, or the epilogue's 128 KB bf16 tile where that is larger (same array)
+constexpr int kW8Smem = kW8Stages * (kW8StageA + kW8StageW) > 8192 ? kW8Stages * (kW8StageA + kW8StageW) : 8192;
+static_assert(kW8Stages >= 4 && kW8Smem <= 9216, "stages and the scale table must fit in 160 KB of LDS");
+
+typedef int i32x2w __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2w lds_i32x2w;
+
+// W stage [32 k][16 chunks of 16 columns]: chunk c of row k at slot 16k + (c ^ (k & 15)).  A
+// transposing byte read runs as two 32-lane passes, each over 16 consecutive rows of one
+// chunk, which this swizzle puts on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int w8_swz(int k) { return k & 15; }
+
+struct W8CopyPlan {
+  uint32_t off[3];
+};
+
+__device__ __forceinline__ W8CopyPlan w8_offsets(const BigArgs& G, const WeightView& W, int m0, int wn0, int wn_end,
+                                                 int w, int lane) {
+  W8CopyPlan cp;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = 64 * (2 * w + i) + lane, r = e >> 2, c = (e & 3) ^ a4_swz(r);
+    const int m = min(m0 + r, G.M - 1);
+    cp.off[i] = (uint32_t)((m * G.lda + 8 * c) * 2);
+  }
+  const int e = 64 * w + lane, k = e >> 4, c = (e & 15) ^ w8_swz(k);
+  const int n = min(wn0 + 16 * c, wn_end - 16);
+  cp.off[2] = (uint32_t)(k * W.ld + n);
+  return cp;
+}
+
+__device__ __forceinline__ void w8_issue(const BigArgs& G, const WeightView& W, const W8CopyPlan& cp, int k0,
+                                         uint4* __restrict__ as, uint4* __restrict__ ws, int w) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) dma16_buf(G.A + k0, 0x7FFFFFF0u, cp.off[i], as + 64 * (2 * w + i));
+  dma16_buf((const uint8_t*)W.w + (int64_t)k0 * W.ld, 0x7FFFFFF0u, cp.off[2], ws + 64 * w);
+}
+
+// B operand of 16-column tile nt of the wave: lane (g, j) gets k = 8g .. 8g+7 of column
+// 64*(w & 3) + 16*nt + j (byte b of the read = row 8g + b), decoded with block scale s.
+__device__ __forceinline__ bf16x8 w8_b(const uint4* __restrict__ ws, int nt, int w, int lane, float s) {
+  const int g = lane >> 4, j = lane & 15;
+  const int k = 8 * g + (j >> 1);
+  const int c = (4 * (w & 3) + nt) ^ w8_swz(k);
+  const i32x2w p = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2w*)((const char*)ws + (16 * k + c) * 16 + 8 * (j & 1)));
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(p[q], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(p[q], true);
+    o[2 * q] = pack_bf16x2(lo[0] * s, lo[1] * s);
+    o[2 * q + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
+  }
+  return as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// One K step, as big_step: matrix ops of the current stage, this step's copies, then the first
+// operands of the next stage (its B operands decoded with that step's block scale s1, read
+// from the scale table sc).  Every LDS access goes through restrict pointers.
+__device__ __forceinline__ void w8_step(const BigArgs& G, const WeightView& W, const W8CopyPlan& cp, bool copy,
+                                        int k_pf, bool compute, bool pre, int sc_idx, const float* __restrict__ sc,
+                                        const uint4* __restrict__ as, const uint4* __restrict__ as1,
+                                        const uint4* __restrict__ ws1, uint4* __restrict__ as_nx,
+                                        uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4], bf16x8 (&apre)[kBigPreA],
+                                        bf16x8 (&bpre)[4], int w, int lane) {
+  if (compute) {
+    bf16x8 af[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) af[mt] = mt < kBigPreA ? apre[mt] : big_a(as, mt, w, lane);
+    if (copy) w8_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bpre[nt], acc[mt][nt], 0, 0, 0);
+  } else if (copy) {
+    w8_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
+  }
+  if (pre) {
+    const float s1 = sc[sc_idx];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) bpre[nt] = w8_b(ws1, nt, w, lane, s1);
+#pragma unroll
+    for (int mt = 0; mt < kBigPreA; ++mt) apre[mt] = big_a(as1, mt, w, lane);
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_w8_kernel(BigArgs G, EpiArgs E) {
+  // kW8Stages stages of A (16 KB) and W (8 KB), also the epilogue's 128 KB bf16 tile
+  __shared__ __attribute__((aligned(16))) uint4 smem[kW8Smem];
+  __shared__ float scl[2][kW8MaxKBlocks];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * kBigN, m0 = blockIdx.y * kBigM;
+  const bool seg1 = n0 >= G.n_split;
+  const WeightView W = seg1 ? G.W1 : G.W0;
+  const int wn0 = seg1 ? n0 - G.n_split : n0, wn_end = seg1 ? G.N - G.n_split : G.n_split;
+  const int kbeg = blockIdx.z * G.k_split, kend = min(G.K, kbeg + G.k_split);
+  const int nsteps = (kend - kbeg) / kBigK;
+  // block scales of the tile's two 128-column blocks over the K range (columns past the
+  // segment, which are not stored, read the last block's scale)
+  const int kg0 = kbeg / 128, nkb = (kend + 127) / 128 - kg0;
+  for (int t = tid; t < 2 * nkb; t += 512) {
+    const int lb = t / nkb, i = t - lb * nkb;
+    const int nb = min(wn0 / 128 + lb, W.scale_ld - 1);
+    scl[lb][i] = W.scale[(int64_t)(kg0 + i) * W.scale_ld + nb];
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  lds_barrier();
+  const W8CopyPlan cp = w8_offsets(G, W, m0, wn0, wn_end, w, lane);
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 apre[kBigPreA], bpre[4];
+#pragma unroll
+  for (int i = 0; i < kBigPreA; ++i) apre[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bpre[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+  // the wave's 64 columns lie in one 128-column block: row (w & 3) >> 1 of the scale table
+  const int sc_row = ((w & 3) >> 1) * kW8MaxKBlocks - kg0;
+  // iteration s: matrix ops of step s (s >= 0), copies of step s + kW8Stages - 1, first
+  // operands of step s + 1
+  for (int s = -(kW8Stages - 1); s < nsteps; ++s) {
+    if (s >= -1) {
+      // steps s and s+1 in LDS: in the steady state the copies of the kW8Stages - 3 steps after
+      // them stay in flight; near the end every copy is waited for
+      constexpr int kAhead = kW8Copies * (kW8Stages - 3);
+      if (s + kW8Stages - 2 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F70 | (kAhead & 15) | ((kAhead >> 4) << 14));
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      lds_barrier();
+    }
+    const int s_pf = s + kW8Stages - 1;
+    const int b_pf = (s_pf + kW8Stages) % kW8Stages, b_cur = s < 0 ? 0 : s % kW8Stages;
+    const int b_1 = (s + 1 + kW8Stages) % kW8Stages;
+    typedef __attribute__((address_space(3))) uint4 lds_uint4;
+    typedef __attribute__((address_space(3))) float lds_float;
+    lds_uint4* base = (lds_uint4*)smem;
+    lds_uint4 *a_cur = base + kW8StageA * b_cur, *a_1 = base + kW8StageA * b_1;
+    lds_uint4 *w_1 = base + kW8StageA * kW8Stages + kW8StageW * b_1;
+    lds_uint4 *a_nx = base + kW8StageA * b_pf, *w_nx = base + kW8StageA * kW8Stages + kW8StageW * b_pf;
+    lds_float* sc = (lds_float*)&scl[0][0];
+    asm volatile("" : "+s"(a_cur), "+s"(a_1), "+s"(w_1), "+s"(a_nx), "+s"(w_nx), "+s"(sc));
+    const int sc_idx = sc_row + (kbeg + (s + 1) * kBigK) / 128;
+    w8_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s >= -1 && s + 1 < nsteps, sc_idx,
+            (const float*)sc, (const uint4*)a_cur, (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx,
+            acc, apre, bpre, w, lane);
+  }
+  big_epilogue(E, acc, (bf16_t*)&smem[0], G.M, G.N, G.C, G.ldc, (int64_t)blockIdx.z * G.split_stride, m0, n0, w,
+               lane);
+}
+
+bool w8_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda, int k_split) {
+  return d.wk == W_FP8 && M > 64 && M <= 1024 && K % kBigK == 0 && k_split % kBigK == 0 &&
+         (k_split + 127) / 128 + 1 <= kW8MaxKBlocks && (n_split >= N || n_split % kBigN == 0) && N % 16 == 0 &&
+         (n_split >= N || (N - n_split) % 16 == 0) && ((int64_t)M * lda + K) * 2 < 0x7FFFFFF0LL;
+}
+
 bool big_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda) {
   // activation offsets are 32-bit byte offsets from the K step's column
   return d.wk == W_BF16 && M > 1024 && K % kBigK == 0 && (n_split >= N || n_split % kBigN == 0) && N % 8 == 0 &&
@@ -731,7 +912,7 @@ struct Plan {
   int bm, splits, k_split;
 };
 
-Plan plan(int M, int N, int K) {
+Plan plan(int M, int N, int K, int wk) {
   Plan p;
   if (M > 1024) {  // prefill shapes (256 x 256 tiles): whole K per workgroup, unless the
     // tile count leaves most of a last round of one workgroup per CU idle and K is long:
@@ -745,6 +926,16 @@ Plan plan(int M, int N, int K) {
       p.splits = 2;
       p.k_split = K / 2;
     }
+    return p;
+  }
+  if (wk == W_FP8 && M > 64) {  // gemm_w8_kernel (256 x 256 tiles): K spread over the CUs, but
+    // >= kW8MinKSplit k per split, so that the fp32 partial sums stay a fraction of the weights
+    p.bm = 256;
+    const int tiles = ((N + kBigN - 1) / kBigN) * ((M + kBigM - 1) / kBigM);
+    int splits = max(1, 256 / tiles);
+    while (splits > 1 && K / splits < kW8MinKSplit) --splits;
+    p.k_split = ((K + splits - 1) / splits + 127) / 128 * 128;
+    p.splits = (K + p.k_split - 1) / p.k_split;
     return p;
   }
   p.bm = M <= 64 ? 64 : 128;
@@ -987,9 +1178,9 @@ bool fast_proj_supported(const Dims& d) {
          (d.H * d.dv) % 8 == 0;
 }
 
-size_t fast_gemm_out_bytes(int M, int N, int K) {
+size_t fast_gemm_out_bytes(const Dims& d, int M, int N, int K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return (size_t)plan(M, N, K).splits * M * N * sizeof(float);
+  return (size_t)plan(M, N, K, d.wk).splits * M * N * sizeof(float);
 }
 
 bool fast_gemm_fusable(const Dims& d, int M, int N, int K, int n_split, int kind) {
@@ -999,14 +1190,14 @@ bool fast_gemm_fusable(const Dims& d, int M, int N, int K, int n_split, int kind
   const bool pairs_ok = d.dn % 2 == 0 && (d.dn + d.dr) % 2 == 0;
   // the k/v consumer stores 16-byte chunks of 8 columns, which must stay inside one head part
   const bool kv_ok = d.dn % 8 == 0 && d.dv % 8 == 0 && (d.dn + d.dr) % 8 == 0;
-  return plan(M, N, K).splits == 1 && aligned && (kind != GemmEpilogue::QUERY || pairs_ok) &&
+  return plan(M, N, K, d.wk).splits == 1 && aligned && (kind != GemmEpilogue::QUERY || pairs_ok) &&
          (kind != GemmEpilogue::KV || kv_ok);
 }
 
 hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView& W0, int n_split, const WeightView& W1,
                      int M, int N, int K, float* out, Partials* res, const GemmEpilogue* epi, bool* fused,
                      hipStream_t s) {
-  const Plan p = plan(M, N, K);
+  const Plan p = plan(M, N, K, d.wk);
   const int64_t stride = (int64_t)M * N;
   *res = Partials{out, p.splits, stride, N};
   if (fused) *fused = false;
@@ -1020,6 +1211,11 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
     E.cosT = epi->cosT;
     E.sinT = epi->sinT;
     if (fused) *fused = true;
+  }
+  if (p.bm == kBigM && w8_ok(d, M, N, K, n_split, lda, p.k_split)) {
+    BigArgs G{(const bf16_t*)A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, p.k_split, stride};
+    gemm_w8_kernel<<<dim3((N + kBigN - 1) / kBigN, (M + kBigM - 1) / kBigM, p.splits), 512, 0, s>>>(G, E);
+    return hipGetLastError();
   }
   if (big_ok(d, M, N, K, n_split, lda)) {
     BigArgs G{(const bf16_t*)A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, p.k_split, stride};
@@ -1035,13 +1231,13 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
 
 bool fast_gemm_f8_ok(const Dims& d, int M, int N, int K, int n_split) {
   if (!fast_proj_supported(d) || M <= 0 || N <= 0 || K <= 0) return false;
-  return f8_ok(d, M, N, K, n_split, plan(M, N, K).k_split);
+  return f8_ok(d, M, N, K, n_split, plan(M, N, K, d.wk).k_split);
 }
 
 hipError_t fast_gemm_f8(const Dims& d, const uint8_t* A8, const uint8_t* Ae, const WeightView& W0, int n_split,
                         const WeightView& W1, int M, int N, int K, float* out, Partials* res,
                         const GemmEpilogue* epi, bool* fused, hipStream_t s) {
-  const Plan p = plan(M, N, K);
+  const Plan p = plan(M, N, K, d.wk);
   const int64_t stride = (int64_t)M * N;
   *res = Partials{out, p.splits, stride, N};
   if (fused) *fused = false;

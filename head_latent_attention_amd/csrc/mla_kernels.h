@@ -48,6 +48,50 @@ __device__ __forceinline__ float part_ld(const Partials& P, int64_t m, int64_t n
   return (s0 + s1) + (s2 + s3);
 }
 
+// part_ld of eight consecutive columns n .. n+7 with 16-byte loads, the same summation order
+// (P.p + m * P.ld + n and P.stride keep 16-byte alignment).
+__device__ __forceinline__ void part_ld8(const Partials& P, int64_t m, int64_t n, float (&r)[8]) {
+  const float* q = P.p + m * P.ld + n;
+  auto ld8 = [&](int z, float (&v)[8]) {
+    const float4 a = *(const float4*)(q + (int64_t)z * P.stride), b = *(const float4*)(q + (int64_t)z * P.stride + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  };
+  if (P.splits == 1) {
+    ld8(0, r);
+    return;
+  }
+  float s[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[u][i] = 0.f;
+  int z = 0;
+  for (; z + 4 <= P.splits; z += 4) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ld8(z + u, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[u][i] += v[u][i];
+  }
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    if (z + u < P.splits) {
+      float v[8];
+      ld8(z + u, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[u][i] += v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (s[0][i] + s[1][i]) + (s[2][i] + s[3][i]);
+}
+
+__host__ __device__ __forceinline__ bool part_vec8_ok(const Partials& P) {
+  return ((uintptr_t)P.p & 15) == 0 && P.ld % 4 == 0 && (P.splits == 1 || P.stride % 4 == 0);
+}
+
 // ---- rotary tables and the layer-input RMSNorm ---------------------------------------
 // inv_freq [dr/2] fp64: theta^(-2i/dr), or its YaRN blend when factor > 1.
 hipError_t rope_inv_freq(int dr, double theta, double factor, int original_max_position, double beta_fast,

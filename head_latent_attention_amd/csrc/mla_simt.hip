@@ -226,9 +226,43 @@ __global__ __launch_bounds__(256) void q_epilogue_kernel(Partials Y, int H, int 
   }
 }
 
+// bf16 queries with dn and dr multiples of 8: one thread per 8 consecutive columns (16-byte
+// partial loads, one 16-byte store); a chunk in the rope part holds four whole pairs.
+__global__ __launch_bounds__(256) void q_epilogue_bf16x8_kernel(Partials Y, int64_t chunks, int H, int dn, int dr,
+                                                                const float* __restrict__ cosT,
+                                                                const float* __restrict__ sinT, bf16_t* __restrict__ q) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= chunks) return;
+  const int dqk = dn + dr, half = dr >> 1, per_row = H * dqk / 8;
+  const int64_t t = e / per_row;
+  const int n = 8 * (int)(e - t * per_row), h = n / dqk, u = n - h * dqk;
+  float v[8];
+  part_ld8(Y, t, n, v);
+  if (u >= dn) {
+    const int p0 = (u - dn) >> 1;
+    const float4 c4 = *(const float4*)(cosT + t * half + p0), s4 = *(const float4*)(sinT + t * half + p0);
+    const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = v[2 * i], x1 = v[2 * i + 1];
+      v[2 * i] = x0 * c[i] - x1 * sn[i];
+      v[2 * i + 1] = x0 * sn[i] + x1 * c[i];
+    }
+  }
+  *(uint4*)(q + t * H * dqk + n) =
+      make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
 hipError_t q_epilogue(const Dims& d, const Partials& Y, int T, const float* cosT, const float* sinT, void* q,
                       hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (d.act == 1 && d.dn % 8 == 0 && d.dr % 8 == 0 && part_vec8_ok(Y) && ((uintptr_t)cosT & 15) == 0 &&
+      ((uintptr_t)sinT & 15) == 0 && ((uintptr_t)q & 15) == 0) {
+    const int64_t chunks = (int64_t)T * d.H * (d.dn + d.dr) / 8;
+    q_epilogue_bf16x8_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, s>>>(Y, chunks, d.H, d.dn, d.dr, cosT, sinT,
+                                                                               (bf16_t*)q);
+    return hipGetLastError();
+  }
   dim3 grid(T, (d.H * (d.dn + d.dr / 2) + 255) / 256);
   if (d.act == 0) q_epilogue_kernel<float><<<grid, 256, 0, s>>>(Y, d.H, d.dn, d.dr, cosT, sinT, (float*)q);
   else q_epilogue_kernel<bf16_t><<<grid, 256, 0, s>>>(Y, d.H, d.dn, d.dr, cosT, sinT, (bf16_t*)q);
@@ -267,9 +301,25 @@ __global__ __launch_bounds__(256) void cast_kernel(Partials Y, int M, int N, T* 
   }
 }
 
+// bf16 rows with N a multiple of 8: one thread per 8 consecutive columns.
+__global__ __launch_bounds__(256) void cast_bf16x8_kernel(Partials Y, int64_t chunks, int N, bf16_t* __restrict__ y) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= chunks) return;
+  const int64_t m = (8 * e) / N, n = 8 * e - m * N;
+  float v[8];
+  part_ld8(Y, m, n, v);
+  *(uint4*)(y + 8 * e) =
+      make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
 hipError_t cast_rows(const Dims& d, const Partials& Y, int M, int N, void* y, hipStream_t s) {
   const int64_t n = (int64_t)M * N;
   if (n <= 0) return hipSuccess;
+  if (d.act == 1 && N % 8 == 0 && part_vec8_ok(Y) && ((uintptr_t)y & 15) == 0) {
+    const int64_t chunks = n / 8;
+    cast_bf16x8_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, s>>>(Y, chunks, N, (bf16_t*)y);
+    return hipGetLastError();
+  }
   const int grid = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
   if (d.act == 0) cast_kernel<float><<<grid, 256, 0, s>>>(Y, M, N, (float*)y);
   else cast_kernel<bf16_t><<<grid, 256, 0, s>>>(Y, M, N, (bf16_t*)y);

@@ -24,6 +24,9 @@ ODD_HEADS = synth.custom(W[4], 109, "odd-heads-prefill", hidden=1024, n_heads=10
 EDGE_DEC16 = synth.custom(W[3], 103, "edge-decode-h16", hidden=1024, n_heads=16, q_lora_rank=256, B=6)
 EDGE_DEC128 = synth.custom(W[3], 104, "edge-decode-h128", B=6)
 EDGE_FP8 = synth.custom(W[5], 105, "edge-decode-fp8", B=6)
+# fp8 weights at 64 < M <= 1024 (the mid-M fp8 kernel): ragged rows, a partial last column tile of
+# the kv segment, the query up-projection unsplit (RoPE fused in the kernel)
+MID_FP8 = synth.custom(W[5], 110, "mid-fp8-h16", hidden=1024, n_heads=16, q_lora_rank=256, B=130)
 EDGE_CTX = np.array([1, 63, 64, 65, 200, 1000], np.int32)
 
 _cache = {}
@@ -118,7 +121,7 @@ def test_prefill_attn(w, T, q_std):
 
 
 # ----------------------------------------------------------------------------- decode front end
-@pytest.mark.parametrize("w", [EDGE_DEC16, W[3], W[5]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [EDGE_DEC16, W[3], W[5], MID_FP8], ids=lambda w: w.name)
 def test_decode_qkv_and_scatter(w):
     need_gpu()
     import head_latent_attention_amd as mla
@@ -248,7 +251,8 @@ def test_decode_attn_many_short_sequences(w):
 
 
 # ----------------------------------------------------------------------------- output projection
-@pytest.mark.parametrize("w,M", [(SMALL_V3, 300), (EDGE_FP8, 7), (W[2], 4096), (W[3], 64), (W[4], 8192), (W[5], 256)],
+@pytest.mark.parametrize("w,M", [(SMALL_V3, 300), (EDGE_FP8, 7), (W[2], 4096), (W[3], 64), (W[4], 8192), (W[5], 256),
+                                 (MID_FP8, 300), (W[5], 1000)],
                          ids=lambda c: str(c) if isinstance(c, int) else c.name)
 def test_out_proj(w, M):
     need_gpu()
