@@ -270,11 +270,13 @@ def run_chunked(w, prefix, T, reps):
     D, H, Lq, Lkv, dn, dr, dv = s.hidden, s.n_heads, s.q_lora_rank, s.kv_lora_rank, s.qk_nope, s.qk_rope, s.v_dim
     seen = T * prefix + T * (T + 1) // 2          # (query, row) pairs
     f_qkv = 2 * T * D * (Lq + Lkv + dr) + 2 * T * Lq * H * (dn + dr)
-    f_attn = 2 * seen * H * (Lkv + dr + Lkv) + 2 * T * H * dn * Lkv + 2 * T * H * Lkv * dv
+    # attention as the layer defines it (per-head keys and values): 2*H*(dqk + dv) per pair
+    f_attn = 2 * seen * H * (dn + dr + dv)
     f_out = 2 * T * H * dv * D
     return dict(ms=tq + ta + to, ms_qkv=tq, ms_attn=ta, ms_out=to, pairs=seen,
                 tflops=(f_qkv + f_attn + f_out) / ((tq + ta + to) * 1e-3) / 1e12,
-                attn_tflops=f_attn / (ta * 1e-3) / 1e12, flops=f_qkv + f_attn + f_out)
+                attn_tflops=f_attn / (ta * 1e-3) / 1e12, flops=f_qkv + f_attn + f_out,
+                expansion_flops=2 * (prefix + T) * Lkv * H * (dn + dv))
 
 
 def cpu_baseline(w, S, budget_s=12.0):
@@ -606,7 +608,9 @@ def main():
                "ms_out_proj": round(ch["ms_out"], 3), "TFLOPs": round(ch["tflops"], 2),
                "attn_TFLOPs": round(ch["attn_tflops"], 2),
                "frac_bf16_peak": round(ch["tflops"] / BF16_PEAK_TFLOPS, 4),
-               "absorbed_counted_flops": ch["flops"], "query_row_pairs": ch["pairs"]}
+               "flops": ch["flops"], "flops_note": "attention counted as 2*H*(dqk+dv) per (query, row) pair; the "
+               "expanded form also expands the sequence's rows by wkv_b (expansion_flops), not counted",
+               "expansion_flops": ch["expansion_flops"], "query_row_pairs": ch["pairs"]}
         if args.only:
             print(json.dumps({"leg": "chunk", **chs}), flush=True)
             return

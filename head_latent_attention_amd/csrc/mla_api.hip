@@ -182,6 +182,48 @@ size_t chunk_attn_ws(const Dims& d, int T, int max_context, void* base, DecodeAt
   return c.used;
 }
 
+// Expanded chunk attention: rows 0 .. N-1 of the sequence gathered from the paged cache
+// (latent parts, rope part of K), expanded by wkv_b into K (k_nope) and V.
+struct ChunkExpWs {
+  void* c;     // [N, Lkv]
+  void* K;     // [N, H, dqk]
+  void* V;     // [N, H, dv]
+  float* PKV;  // [N, H*(dn+dv)] partials, when the expansion is not handed straight to K and V
+};
+
+size_t chunk_exp_ws(const Dims& d, int N, void* base, ChunkExpWs* out) {
+  Carver c(base);
+  ChunkExpWs w;
+  const int NKV = d.H * (d.dn + d.dv);
+  const bool fused = fast_gemm_fusable(d, N, NKV, d.Lkv, NKV, GemmEpilogue::KV);
+  w.c = c.take<char>((size_t)N * d.Lkv * 2);
+  w.K = c.take<char>((size_t)N * d.H * d.dqk() * 2);
+  w.V = c.take<char>((size_t)N * d.H * d.dv * 2);
+  w.PKV = (float*)c.take<char>(fused ? 0 : proj_out_bytes(d, N, NKV, d.Lkv));
+  if (out) *out = w;
+  return c.used;
+}
+
+// Whether T queries after `prefix` cached rows take the expanded form: 2*H*(dqk+dv) flop per
+// (query, row) pair instead of the absorbed 2*H*(2*Lkv+dr), for 2*H*Lkv*(dn+dv) per row of
+// expansion.  The advantage grows with prefix (for a fixed T), so the largest prefix decides
+// whether any call of a given T and max_context can take it.
+bool chunk_expanded(const Dims& d, int T, int prefix) {
+  if (d.aq || d.act != 1 || !fast_prefill_attn_supported(d) || !fast_proj_supported(d) || d.Lkv % 8 || d.dr % 8 ||
+      d.dn % 8)
+    return false;
+  const double N = (double)prefix + T, pairs = (double)T * prefix + (double)T * (T + 1) / 2;
+  const double saved = 2.0 * (2 * d.Lkv + d.dr) - 2.0 * (d.dqk() + d.dv);
+  return pairs * saved > N * 2.0 * d.Lkv * (d.dn + d.dv);
+}
+
+size_t chunk_ws_need(const Dims& d, int T, int max_context) {
+  size_t need = chunk_attn_ws(d, T, max_context, nullptr, nullptr, nullptr);
+  if (chunk_expanded(d, T, std::max(0, max_context - T)))
+    need = std::max(need, chunk_exp_ws(d, std::max(max_context, T), nullptr, nullptr));
+  return need;
+}
+
 size_t out_proj_ws(const Dims& d, int M, void* base, float** Y, void** qz = nullptr) {
   Carver c(base);
   const bool fused = fast_gemm_fusable(d, M, d.D, d.H * d.dv, d.D, GemmEpilogue::STORE);
@@ -372,7 +414,7 @@ size_t mla_workspace_size(const mla_config* cfg, int32_t fn, int32_t n, int32_t 
     case MLA_FN_OUT_PROJ: return out_proj_ws(d, n, nullptr, nullptr);
     case MLA_FN_PREFILL_ATTN_PAGED:
       if (max_context <= 0) return 0;
-      return chunk_attn_ws(d, n, max_context, nullptr, nullptr, nullptr);
+      return chunk_ws_need(d, n, max_context);
   }
   return 0;
 }
@@ -503,12 +545,33 @@ mla_status mla_prefill_attn_paged(const mla_config* cfg, const mla_weights* w, c
   if ((int64_t)prefix_len + T > max_ctx64) return MLA_ERR_INVALID_ARG;
   if (max_ctx64 > (1 << 30)) return MLA_ERR_UNSUPPORTED;
   const int max_ctx = (int)max_ctx64;
+  hipStream_t s = (hipStream_t)stream;
+  const int NKV = d.H * (d.dn + d.dv);
+  const WeightView wkv_b = view(d, w->wkv_b, NKV);
+  if (chunk_expanded(d, T, prefix_len)) {
+    // rows 0 .. N-1 expanded to per-head keys and values, then causal attention with the
+    // queries at positions prefix_len ..
+    const int N = prefix_len + T;
+    ChunkExpWs E;
+    const size_t need = chunk_exp_ws(d, N, ws, &E);
+    if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+    HIP_TRY(chunk_gather(d, kv_cache, n_blocks, block_table, N, E.c, E.K, s));
+    Partials PKV;
+    GemmEpilogue epi;
+    epi.kind = GemmEpilogue::KV;
+    epi.y = E.K;
+    epi.y2 = E.V;
+    bool fused = false;
+    st = project(d, E.c, d.Lkv, wkv_b, NKV, wkv_b, N, NKV, d.Lkv, E.PKV, &PKV, s, &epi, &fused, nullptr);
+    if (st != MLA_OK) return st;
+    if (!fused) HIP_TRY(kv_split(d, PKV, N, E.K, E.V, s));
+    HIP_TRY(fast_prefill_attn_offset(d, q, E.K, E.V, T, prefix_len, o, nullptr, s));
+    return MLA_OK;
+  }
   DecodeAttnWs L;
   int32_t* ctx = nullptr;
   const size_t need = chunk_attn_ws(d, T, max_ctx, ws, &L, &ctx);
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  const WeightView wkv_b = view(d, w->wkv_b, (int64_t)d.H * (d.dn + d.dv));
   HIP_TRY(chunk_ctx(T, prefix_len, ctx, s));
   // every query of the chunk is a decode query of the same sequence at its own position:
   // one block-table row shared by all (stride 0) and context length prefix + t + 1

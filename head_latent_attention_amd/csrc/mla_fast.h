@@ -72,5 +72,9 @@ bool fast_prefill_attn_supported(const Dims& d);
 size_t fast_prefill_attn_ws_bytes(const Dims& d, int T);
 hipError_t fast_prefill_attn(const Dims& d, const void* q, const void* k, const void* v, int T, void* o,
                              void* ws, hipStream_t s);
+// The same with query row t at position q_off + t: k and v hold q_off + T rows, and query t sees
+// rows 0 .. q_off + t (a chunk of a sequence after q_off cached positions).
+hipError_t fast_prefill_attn_offset(const Dims& d, const void* q, const void* k, const void* v, int T, int q_off,
+                                    void* o, void* ws, hipStream_t s);
 
 }  // namespace mla

@@ -148,6 +148,10 @@ hipError_t decode_attn_simt(const Dims& d, const float* Qabs, int B, const void*
                             float* part_ml, hipStream_t s);
 // ctx[t] = prefix + t + 1 for t < T (the rows query t of a prefill chunk sees).
 hipError_t chunk_ctx(int T, int prefix, int32_t* ctx, hipStream_t s);
+// rows 0 .. N-1 of the sequence the block-table row `table` maps: latent parts into c [N, Lkv],
+// rope parts broadcast into k [N, H, dqk] columns dn .. dqk (bf16, dims multiples of 8)
+hipError_t chunk_gather(const Dims& d, const void* cache, int64_t n_blocks, const int32_t* table, int N, void* c,
+                        void* k, hipStream_t s);
 // Log-sum-exp merge of the splits, then o[b, h] = o_lat @ W_UV[h] (act).
 hipError_t combine_simt(const Dims& d, int B, int nsplit, const float* part_o, const float* part_ml,
                         const WeightView& wkv_b, void* o, hipStream_t s);

@@ -1,6 +1,8 @@
 // Causal prefill attention on CDNA4 matrix cores (gfx950) for the V2/V3 head
-// shape: q, k [T, H, 192] and v [T, H, 128] in bf16, o [T, H, 128].
-//   o[t, h] = sum_{j <= t} softmax_j(scale * q[t,h] . k[j,h]) v[j,h]
+// shape: q [T, H, 192], k [Tk, H, 192] and v [Tk, H, 128] in bf16, o [T, H, 128], query row t
+// at position q_off + t (Tk = q_off + T; q_off = 0 for a whole prefill, the cached prefix
+// length for a chunk of a longer sequence):
+//   o[t, h] = sum_{j <= q_off + t} softmax_j(scale * q[t,h] . k[j,h]) v[j,h]
 // (NeMo "MLA" module: forward with a causal attention mask and softmax_scale).
 //
 // Flash-style: a workgroup owns 32*NW queries of one head and streams 64-key tiles
@@ -53,12 +55,13 @@ struct PrefillArgs {
   const bf16_t* v;
   bf16_t* o;
   int T, H;
+  int q_off, Tk;  // position of query row 0; keys (rows of k and v)
   float scale_log2;
   int n_qtiles;
 };
 
 // Copies of key tile kt: NW waves share K_SLOTS + V_SLOTS 16-byte slots, KI + VI per lane.
-// Keys past T repeat the last key (their scores are masked).  Offsets are taken from the
+// Keys past Tk repeat the last key (their scores are masked).  Offsets are taken from the
 // tile's first row of head h, so they stay far below 4 GB; a lane's offsets within a tile
 // are the same for every tile but the last, so they are computed once (copy_offsets).
 template <int NW>
@@ -92,14 +95,14 @@ template <int NW>
 __device__ __forceinline__ void issue_kv_copy(const PrefillArgs& P, int h, int kt, const CopyPlan<NW>& cp,
                                               uint4* __restrict__ kb, uint4* __restrict__ vb, int w, int lane) {
   constexpr int KI = CopyPlan<NW>::KI, VI = CopyPlan<NW>::VI;
-  const int k0 = kt * KT, t_max = P.T - 1 - k0;
+  const int k0 = kt * KT, t_max = P.Tk - 1 - k0;
   const bf16_t* kbase = P.k + ((int64_t)k0 * P.H + h) * DQK;
   const bf16_t* vbase = P.v + ((int64_t)k0 * P.H + h) * DV;
   uint32_t off[KI + VI];
   if (t_max >= KT - 1) {
 #pragma unroll
     for (int i = 0; i < KI + VI; ++i) off[i] = cp.off[i];
-  } else {  // the tile runs past T
+  } else {  // the tile runs past Tk
     int l = lane;
     asm volatile("" : "+v"(l));
 #pragma unroll
@@ -188,7 +191,7 @@ __device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, const Cop
 }
 
 // Online softmax of one tile's scores (keys k0 .. k0+63) for the wave's 32 queries (lane's
-// query: qw0 + 16*nt + j): probabilities into pb (bf16, the B-operand layout of the value
+// query at position qw0 + 16*nt + j): probabilities into pb (bf16, the B-operand layout of the value
 // product), running max and sum updated, O rescaled when the max moves.  Every query sees
 // key 0 in tile 0, so the running max is finite from the first tile on.  The max is taken
 // over the raw scores and scaled afterwards (the scale is positive).
@@ -266,7 +269,8 @@ __device__ __forceinline__ void pb_clear(bf16x8 (&pb)[2][2]) {
 // copies tile t+2, into the stage of tile t-2, which step t-1 finished with.
 constexpr int kStages = 4;
 
-// Steps -2 .. n_kt of one item for a wave of group GRP (see prefill_attn_kernel).
+// Steps -2 .. n_kt of one item for a wave of group GRP (see prefill_attn_kernel); qw0 is the
+// position of the wave's first query.
 template <int NW, int GRP>
 __device__ __forceinline__ void item_steps(const PrefillArgs& P, const CopyPlan<NW>& cp, int h, int n_kt, int qw0,
                                            uint4 (*kbuf)[K_SLOTS],
@@ -364,9 +368,9 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
       h = m % P.H;
       qt = P.n_qtiles - 1 - m / P.H;
     }
-    const int q0 = qt * BQ, qw0 = q0 + 32 * w;
+    const int q0 = qt * BQ, qw0 = q0 + 32 * w;  // rows of q and o
     const int q_last = min(P.T, q0 + BQ) - 1;
-    const int n_kt = q_last / KT + 1;
+    const int n_kt = (P.q_off + q_last) / KT + 1;
     bf16x8 qf[2][DQK / 32];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -382,8 +386,9 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
     // the query fragments are complete before the loop, so no read in it waits for the copies
     __builtin_amdgcn_s_waitcnt(0);
     // one loop per group, so that each has its own register liveness
-    if (grp == 0) item_steps<NW, 0>(P, cp, h, n_kt, qw0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
-    else item_steps<NW, 1>(P, cp, h, n_kt, qw0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
+    const int qp0 = P.q_off + qw0;  // position of the wave's first query
+    if (grp == 0) item_steps<NW, 0>(P, cp, h, n_kt, qp0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
+    else item_steps<NW, 1>(P, cp, h, n_kt, qp0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int qi = qw0 + 16 * nt + j;
@@ -421,8 +426,13 @@ bool fast_prefill_attn_supported(const Dims& d) {
 
 size_t fast_prefill_attn_ws_bytes(const Dims&, int) { return 0; }
 
-hipError_t fast_prefill_attn(const Dims& d, const void* q, const void* k, const void* v, int T, void* o, void*,
+hipError_t fast_prefill_attn(const Dims& d, const void* q, const void* k, const void* v, int T, void* o, void* ws,
                              hipStream_t s) {
+  return fast_prefill_attn_offset(d, q, k, v, T, 0, o, ws, s);
+}
+
+hipError_t fast_prefill_attn_offset(const Dims& d, const void* q, const void* k, const void* v, int T, int q_off,
+                                    void* o, void*, hipStream_t s) {
   PrefillArgs P;
   P.q = (const bf16_t*)q;
   P.k = (const bf16_t*)k;
@@ -430,14 +440,25 @@ hipError_t fast_prefill_attn(const Dims& d, const void* q, const void* k, const 
   P.o = (bf16_t*)o;
   P.T = T;
   P.H = d.H;
+  P.q_off = q_off;
+  P.Tk = q_off + T;
   P.scale_log2 = d.scale * 1.4426950408889634f;
-  // 256 queries per workgroup when that still gives every CU work, else 128
-  const bool big = (int64_t)d.H * ((T + 255) / 256) >= 1024;
+  // one workgroup per CU (the four K/V stages take all 160 KB of a CU's LDS).  256 queries per
+  // workgroup (8 waves, two per SIMD playing ping-pong) unless the items are then too few and
+  // uneven to share out: the larger of the heaviest item and the mean load per workgroup must
+  // stay within 1.25x the mean; else 128 queries (4 waves)
+  const int cus = device_cu_count();
+  const int nq8 = (T + 255) / 256;
+  int64_t sum8 = 0;
+  for (int i = 0; i < nq8; ++i) sum8 += (q_off + std::min(T, 256 * (i + 1)) - 1) / KT + 1;
+  const int64_t max8 = (q_off + T - 1) / KT + 1;
+  const int64_t items8 = (int64_t)d.H * nq8;
+  const double mean8 = (double)sum8 * d.H / (double)std::min<int64_t>(items8, cus);
+  const bool big = (double)std::max<int64_t>(max8, 1) <= 1.25 * mean8;
   const int BQ = big ? 256 : 128;
   P.n_qtiles = (T + BQ - 1) / BQ;
   const int total = d.H * P.n_qtiles;
-  // one workgroup per CU (the four K/V stages take all 160 KB of a CU's LDS)
-  const int grid = std::min(total, device_cu_count());
+  const int grid = std::min(total, cus);
   if (big) prefill_attn_kernel<8><<<grid, 512, 0, s>>>(P);
   else prefill_attn_kernel<4><<<grid, 256, 0, s>>>(P);
   return hipGetLastError();

@@ -601,4 +601,34 @@ hipError_t chunk_ctx(int T, int prefix, int32_t* ctx, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Rows 0 .. N-1 of one sequence's paged cache for the expanded chunk attention: the latent part
+// of row r into c[r] (Lkv values), its rope part into k[r, h, dn:dqk] for every head (the rope
+// key is shared by all heads).  One workgroup per row; rows whose block id is out of range are
+// zero.  bf16 rows; Lkv, dr, dn multiples of 8.
+__global__ __launch_bounds__(256) void chunk_gather_kernel(const bf16_t* __restrict__ cache, int64_t n_blocks, int bs,
+                                                           const int32_t* __restrict__ table, int Lkv, int dr, int H,
+                                                           int dn, bf16_t* __restrict__ c, bf16_t* __restrict__ k) {
+  const int64_t r = blockIdx.x;
+  const int t = threadIdx.x;
+  const int blk = table[r / bs];
+  const bool ok = blk >= 0 && blk < n_blocks;
+  const bf16_t* src = cache + ((int64_t)(ok ? blk : 0) * bs + r % bs) * (Lkv + dr);
+  const int lc = Lkv / 8, pc = dr / 8, dqk = dn + dr;
+  for (int i = t; i < lc; i += 256)
+    *(uint4*)(c + r * Lkv + 8 * i) = ok ? *(const uint4*)(src + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+  // rope chunk t % pc of every head h = t / pc, t / pc + 256 / pc, ...
+  const int ch = t % pc, hstep = 256 / pc;
+  if (t >= hstep * pc) return;
+  const uint4 v = ok ? *(const uint4*)(src + Lkv + 8 * ch) : make_uint4(0u, 0u, 0u, 0u);
+  for (int h = t / pc; h < H; h += hstep) *(uint4*)(k + (r * H + h) * dqk + dn + 8 * ch) = v;
+}
+
+hipError_t chunk_gather(const Dims& d, const void* cache, int64_t n_blocks, const int32_t* table, int N, void* c,
+                        void* k, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  chunk_gather_kernel<<<N, 256, 0, s>>>((const bf16_t*)cache, n_blocks, d.bs, table, d.Lkv, d.dr, d.H, d.dn,
+                                        (bf16_t*)c, (bf16_t*)k);
+  return hipGetLastError();
+}
+
 }  // namespace mla

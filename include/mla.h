@@ -247,11 +247,17 @@ mla_status mla_decode_attn_absorbed_noalloc(const mla_config* cfg, const mla_wei
                                             const int32_t* context_lens, void* o, void* stream);
 
 /* Chunked prefill over a paged prefix: causal attention of T new tokens of one sequence over
- * that sequence's latent cache, in the absorbed form ([MlaWeights] w_uk_block_diag /
- * w_uv_block_diag: query absorption and value extraction used for prefill too; [NKI-Decode]
- * paged kv_cache).  Query t sits at position prefix_len + t and attends to rows
- * 0 .. prefix_len + t, read through block_table; each query is computed exactly as
- * mla_decode_attn_absorbed computes a decode query with context prefix_len + t + 1.
+ * that sequence's latent cache ([NKI-Decode] paged kv_cache).  Query t sits at position
+ * prefix_len + t and attends to rows 0 .. prefix_len + t, read through block_table.  Two forms
+ * compute the same attention; the cheaper one is taken:
+ *   absorbed ([MlaWeights] w_uk_block_diag / w_uv_block_diag: query absorption and value
+ *     extraction used for prefill too): each query as mla_decode_attn_absorbed computes a decode
+ *     query with context prefix_len + t + 1;
+ *   expanded (bf16 activations without act_quant, V2/V3 head shape): the sequence's rows are
+ *     expanded by wkv_b into per-head keys and values once, then causal attention as
+ *     mla_prefill_attn with the queries offset by prefix_len.  Taken when the chunk has enough
+ *     queries per row that 2*H*(dqk+dv) flop per (query, row) pair plus 2*H*Lkv*(dn+dv) per row
+ *     is less than the absorbed 2*H*(2*Lkv+dr) per pair (about T > 170 at the V3 shape).
  *   q        [T, H, dqk] act: per head [q_nope | RoPE(q_pe)] at the tokens' positions
  *            (mla_qkv_prefill with the tables of positions prefix_len ..).
  *   kv_cache [n_blocks, 1, bs, R] act (read only); rows prefix_len .. prefix_len + T - 1 must
@@ -259,7 +265,8 @@ mla_status mla_decode_attn_absorbed_noalloc(const mla_config* cfg, const mla_wei
  *   block_table  int32 [max_blocks]: the sequence's blocks; prefix_len + T <= max_blocks * bs.
  *   o        [T, H, dv] act out.
  * T >= 1, prefix_len >= 0.  Workspace: mla_workspace_size(cfg, MLA_FN_PREFILL_ATTN_PAGED, T,
- * max_blocks * bs). */
+ * max_blocks * bs), which covers the expanded form's keys and values (about 83 KB per row at
+ * the V3 shape) whenever some prefix_len would take it. */
 mla_status mla_prefill_attn_paged(const mla_config* cfg, const mla_weights* w, const void* q, int32_t T,
                                   const void* kv_cache, int64_t n_blocks, const int32_t* block_table,
                                   int32_t max_blocks, int32_t prefix_len, void* o, void* ws, size_t ws_bytes,

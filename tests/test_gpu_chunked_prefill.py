@@ -62,8 +62,11 @@ def test_chunks_after_prefill_tiny_fp32():
         start += T
 
 
+# (0, 130), (1000, 77) and (64, 1) take the absorbed form; (3000, 300), (600, 400) and (4096, 512)
+# the expanded one (more than ~170 queries per cached row), (600, 400) with its expansion through
+# the smaller projection kernel (1000 rows)
 @pytest.mark.parametrize("w,prefix,T", [(CH_V3, 0, 130), (CH_V3, 1000, 77), (CH_V3, 3000, 300), (CH_V3, 64, 1),
-                                        (CH_V3_FULL, 4096, 512)],
+                                        (CH_V3, 600, 400), (CH_V3_FULL, 4096, 512)],
                          ids=lambda c: str(c) if isinstance(c, int) else c.name)
 def test_chunk_over_cached_history(w, prefix, T):
     """A chunk of T tokens over `prefix` history rows already in the paged cache (V2/V3 per-head
