@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <vector>
 
 namespace mla {
 
@@ -49,6 +50,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 __device__ __forceinline__ int k_swz(int t) { return (t >> 1) & 7; }
 __device__ __forceinline__ int v_swz(int t) { return 2 * (t & 7); }
 
+// Work items of one head, heaviest first: a query tile, or one part of its key tiles when a
+// query tile alone would leave the workgroups uneven (the parts write partial results that
+// prefill_merge_kernel combines).  Entry: query tile (bits 0-9), part (10-12), parts (13-15),
+// partial-result slot within the head (16-31).
+constexpr int kMaxItemsPerHead = 256;
+
 struct PrefillArgs {
   const bf16_t* q;
   const bf16_t* k;
@@ -58,6 +65,12 @@ struct PrefillArgs {
   int q_off, Tk;  // position of query row 0; keys (rows of k and v)
   float scale_log2;
   int n_qtiles;
+  int n_items;               // entries of items per head; 0: whole query tiles, heaviest first
+  int cost_major;            // XCD lists ordered by item cost across the XCD's heads (few rounds)
+  int slots_per_head;        // partial-result slots per head
+  float* part_o;             // [H][slots_per_head][BQ][DV] fp32, normalised by its own sum
+  float* part_ml;            // [H][slots_per_head][BQ][2]  (running max, log2 units; sum)
+  uint32_t items[kMaxItemsPerHead];
 };
 
 // Copies of key tile kt: NW waves share K_SLOTS + V_SLOTS 16-byte slots, KI + VI per lane.
@@ -269,10 +282,11 @@ __device__ __forceinline__ void pb_clear(bf16x8 (&pb)[2][2]) {
 // copies tile t+2, into the stage of tile t-2, which step t-1 finished with.
 constexpr int kStages = 4;
 
-// Steps -2 .. n_kt of one item for a wave of group GRP (see prefill_attn_kernel); qw0 is the
-// position of the wave's first query.
+// Steps -2 .. n_kt of one item (key tiles kt0 .. kt0 + n_kt - 1) for a wave of group GRP (see
+// prefill_attn_kernel); qw0 is the position of the wave's first query.
 template <int NW, int GRP>
-__device__ __forceinline__ void item_steps(const PrefillArgs& P, const CopyPlan<NW>& cp, int h, int n_kt, int qw0,
+__device__ __forceinline__ void item_steps(const PrefillArgs& P, const CopyPlan<NW>& cp, int h, int kt0, int n_kt,
+                                           int qw0,
                                            uint4 (*kbuf)[K_SLOTS],
                                            uint4 (*vbuf)[V_SLOTS], const bf16x8 (&qf)[2][DQK / 32],
                                            f32x4 (&o)[DV / 16][2], float (&m_run)[2], float (&l_run)[2],
@@ -295,24 +309,24 @@ __device__ __forceinline__ void item_steps(const PrefillArgs& P, const CopyPlan<
     lds_barrier();
     const int kt_pf = kt + 2;
     const bool copy = kt_pf < n_kt;
-    const bool qk = kt >= 0 && kt < n_kt && kt * KT <= qw0 + 31;    // this wave's queries see tile kt
-    const bool pv = kt >= 1 && (kt - 1) * KT <= qw0 + 31;           // ... and tile kt-1
+    const bool qk = kt >= 0 && kt < n_kt && (kt0 + kt) * KT <= qw0 + 31;  // this wave's queries see tile kt
+    const bool pv = kt >= 1 && (kt0 + kt - 1) * KT <= qw0 + 31;         // ... and tile kt-1
     // opaque copies of the stage pointers keep the restrict scopes of mma_block's parameters
     lds_uint4 *kc = (lds_uint4*)kbuf[kt & 3], *vp = (lds_uint4*)vbuf[(kt + 3) & 3];
     lds_uint4 *kn = (lds_uint4*)kbuf[kt_pf & 3], *vn = (lds_uint4*)vbuf[kt_pf & 3];
     asm volatile("" : "+s"(kc), "+s"(vp), "+s"(kn), "+s"(vn));
     if constexpr (GRP == 0) {
-      mma_block<NW>(P, h, cp, copy, kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn, qf, s,
-                    pb, o, kbase, vbase, w, lane);
+      mma_block<NW>(P, h, cp, copy, kt0 + kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn,
+                    qf, s, pb, o, kbase, vbase, w, lane);
       lds_barrier();
-      if (qk) softmax_block(P, kt * KT, qw0, s, pb, o, m_run, l_run, g, j);
+      if (qk) softmax_block(P, (kt0 + kt) * KT, qw0, s, pb, o, m_run, l_run, g, j);
       else pb_clear(pb);
     } else {
-      if (pv) softmax_block(P, (kt - 1) * KT, qw0, s, pb, o, m_run, l_run, g, j);
+      if (pv) softmax_block(P, (kt0 + kt - 1) * KT, qw0, s, pb, o, m_run, l_run, g, j);
       else pb_clear(pb);
       lds_barrier();
-      mma_block<NW>(P, h, cp, copy, kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn, qf, s,
-                    pb, o, kbase, vbase, w, lane);
+      mma_block<NW>(P, h, cp, copy, kt0 + kt_pf, qk, pv, (const uint4*)kc, (const uint4*)vp, (uint4*)kn, (uint4*)vn,
+                    qf, s, pb, o, kbase, vbase, w, lane);
     }
   }
 }
@@ -355,22 +369,38 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
   const bool by_xcd = (gridDim.x & 7) == 0 && (P.H & 7) == 0;
   const int J = by_xcd ? (int)gridDim.x >> 3 : (int)gridDim.x;       // workgroups sharing one list
   const int slot = by_xcd ? (int)blockIdx.x >> 3 : (int)blockIdx.x;  // this workgroup's place in it
-  const int n_list = by_xcd ? (P.H >> 3) * P.n_qtiles : P.H * P.n_qtiles;
+  const int per_head = P.n_items > 0 ? P.n_items : P.n_qtiles;
+  const int n_list = by_xcd ? (P.H >> 3) * per_head : P.H * per_head;
   for (int r = 0; r * J < n_list; ++r) {
     const int m = r * J + ((r & 1) ? J - 1 - slot : slot);
     if (m >= n_list) continue;
-    int h, qt;
-    if (by_xcd) {  // XCD list: heads x, x + 8, ... one after another, query tiles heaviest first
-      const int hi = m / P.n_qtiles;
+    int h, e;
+    if (by_xcd) {  // XCD list: heads x, x + 8, ... one after another, items heaviest first
+      // (with few rounds, heaviest first across those heads instead)
+      const int hx = P.H >> 3;
+      const int hi = P.cost_major ? m % hx : m / per_head;
       h = 8 * hi + ((int)blockIdx.x & 7);
-      qt = P.n_qtiles - 1 - (m - hi * P.n_qtiles);
-    } else {       // whole list: query tiles heaviest first, heads within
+      e = P.cost_major ? m / hx : m - hi * per_head;
+    } else {       // whole list: items heaviest first, heads within
       h = m % P.H;
-      qt = P.n_qtiles - 1 - m / P.H;
+      e = m / P.H;
+    }
+    int qt = P.n_qtiles - 1 - e, part = 0, parts = 1, pslot = 0;
+    if (P.n_items > 0) {
+      const uint32_t ent = P.items[e];
+      qt = (int)(ent & 0x3FF);
+      part = (int)((ent >> 10) & 7);
+      parts = (int)((ent >> 13) & 7);
+      pslot = (int)(ent >> 16);
     }
     const int q0 = qt * BQ, qw0 = q0 + 32 * w;  // rows of q and o
     const int q_last = min(P.T, q0 + BQ) - 1;
-    const int n_kt = (P.q_off + q_last) / KT + 1;
+    const int n_all = (P.q_off + q_last) / KT + 1;
+    // part p of `parts` covers key tiles [b_p, b_(p+1)): every boundary lies below the tiles the
+    // query tile's first row cannot see whole, so each part's first tile is visible to all rows
+    const int n_full = (P.q_off + q0) / KT;
+    auto bound = [&](int p) { return p == 0 ? 0 : (p >= parts ? n_all : min(p * n_all / parts, n_full - 1)); };
+    const int kt0 = bound(part), n_kt = bound(part + 1) - kt0;
     bf16x8 qf[2][DQK / 32];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -387,13 +417,21 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
     __builtin_amdgcn_s_waitcnt(0);
     // one loop per group, so that each has its own register liveness
     const int qp0 = P.q_off + qw0;  // position of the wave's first query
-    if (grp == 0) item_steps<NW, 0>(P, cp, h, n_kt, qp0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
-    else item_steps<NW, 1>(P, cp, h, n_kt, qp0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
+    if (grp == 0) item_steps<NW, 0>(P, cp, h, kt0, n_kt, qp0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
+    else item_steps<NW, 1>(P, cp, h, kt0, n_kt, qp0, kbuf, vbuf, qf, o, m_run, l_run, kbase, vbase, w, lane);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int qi = qw0 + 16 * nt + j;
       if (qi >= P.T) continue;
       const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
+      if (parts > 1) {  // a part: fp32 output normalised by its own sum, running max and sum
+        const int64_t row = ((int64_t)h * P.slots_per_head + pslot) * BQ + (qi - q0);
+        float* dst = P.part_o + row * DV + 4 * g;
+#pragma unroll
+        for (int mt = 0; mt < DV / 16; ++mt) *(f32x4*)(dst + 16 * mt) = o[mt][nt] * inv;
+        if (g == 0) *(float2*)(P.part_ml + row * 2) = make_float2(m_run[nt], l_run[nt]);
+        continue;
+      }
       bf16_t* dst = P.o + ((int64_t)qi * P.H + h) * DV + 4 * g;
 #pragma unroll
       for (int mt = 0; mt < DV / 16; ++mt) {
@@ -404,6 +442,120 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attn_kernel(PrefillArgs P)
     // every wave is done with the last tiles' stages before the next item's copies refill them
     lds_barrier();
   }
+}
+
+// Query tiles whose key tiles were split into parts: entry = query tile (bits 0-9), parts
+// (10-12), first partial-result slot within the head (16-31).
+struct MergeArgs {
+  const float* part_o;
+  const float* part_ml;
+  bf16_t* o;
+  int T, H, BQ, slots_per_head;
+  uint32_t tiles[kMaxItemsPerHead];
+};
+
+// o[q, h] of a split query tile from its parts: each part's output (normalised by its own sum
+// l_p, running max m_p in log2 units) weighted by 2^(m_p - M) * l_p, M the largest m_p, in part
+// order.  One thread per (row, four value columns); grid (split tiles x heads, BQ * DV / 4 / 256).
+__global__ __launch_bounds__(256) void prefill_merge_kernel(MergeArgs M) {
+  const int th = blockIdx.x, tile = th / M.H, h = th - tile * M.H;
+  const uint32_t ent = M.tiles[tile];
+  const int qt = (int)(ent & 0x3FF), parts = (int)((ent >> 10) & 7), slot0 = (int)(ent >> 16);
+  const int e = blockIdx.y * 256 + threadIdx.x, r = e / (DV / 4), c = e - r * (DV / 4);
+  const int qi = qt * M.BQ + r;
+  if (r >= M.BQ || qi >= M.T) return;
+  const int64_t row0 = ((int64_t)h * M.slots_per_head + slot0) * M.BQ + r;
+  float mx = -INFINITY;
+  for (int p = 0; p < parts; ++p) mx = fmaxf(mx, M.part_ml[(row0 + (int64_t)p * M.BQ) * 2]);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int p = 0; p < parts; ++p) {
+    const int64_t row = row0 + (int64_t)p * M.BQ;
+    const float2 ml = *(const float2*)(M.part_ml + row * 2);
+    const float wgt = __builtin_amdgcn_exp2f(ml.x - mx) * ml.y;
+    acc += *(const f32x4*)(M.part_o + row * DV + 4 * c) * wgt;
+    wsum += wgt;
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  acc *= inv;
+  *(uint2*)(M.o + ((int64_t)qi * M.H + h) * DV + 4 * c) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+}
+
+// Launch plan of the prefill attention: 256 queries per workgroup (8 waves) unless the work
+// items are then too uneven; on the 8-wave path with no query offset, query tiles whose key
+// tiles exceed the mean load per workgroup are split into up to four parts of whole key tiles
+// (partials merged afterwards), so that few heads or short sequences still fill every CU.
+struct PrefillPlan {
+  bool big = true, cost_major = false;
+  int BQ = 256, n_qtiles = 0;
+  std::vector<uint32_t> items;  // empty: whole query tiles, heaviest first
+  std::vector<uint32_t> split_tiles;
+  int slots_per_head = 0;
+  size_t ws_bytes = 0;
+};
+
+PrefillPlan prefill_plan(const Dims& d, int T, int q_off, bool allow_split, int cus) {
+  PrefillPlan pl;
+  const int nq = (T + 255) / 256;
+  auto tiles_of = [&](int i) { return (q_off + std::min(T, 256 * (i + 1)) - 1) / KT + 1; };
+  int64_t total = 0;
+  for (int i = 0; i < nq; ++i) total += tiles_of(i);
+  total *= d.H;
+  std::vector<int> parts(nq, 1);
+  if (allow_split) {
+    // parts of at most 3/4 of the mean load per workgroup (a finer cut evens out the last round)
+    const int64_t target = std::max<int64_t>(3 * ((total + cus - 1) / cus) / 4, 16);
+    for (int i = 0; i < nq; ++i) {
+      const int n_full = (q_off + 256 * i) / KT, c = tiles_of(i);
+      if (c > target && n_full >= 2) parts[i] = (int)std::min<int64_t>({4, (c + target - 1) / target, n_full});
+    }
+  }
+  // entries (cost, query tile, part), with the kernel's part boundaries
+  struct Ent { int cost, qt, part, parts; };
+  std::vector<Ent> ents;
+  bool any_split = false;
+  for (int i = 0; i < nq; ++i) {
+    const int n_all = tiles_of(i), n_full = (q_off + 256 * i) / KT, np = parts[i];
+    auto bound = [&](int p) { return p == 0 ? 0 : (p >= np ? n_all : std::min(p * n_all / np, n_full - 1)); };
+    for (int p = 0; p < np; ++p) ents.push_back({bound(p + 1) - bound(p), i, p, np});
+    any_split |= np > 1;
+  }
+  std::stable_sort(ents.begin(), ents.end(), [](const Ent& a, const Ent& b) {
+    return a.cost != b.cost ? a.cost > b.cost : a.qt > b.qt;
+  });
+  int max_item = 0;
+  for (const Ent& e : ents) max_item = std::max(max_item, e.cost);
+  const int64_t n_items = (int64_t)d.H * (int64_t)ents.size();
+  const double mean = (double)total / (double)std::min<int64_t>(n_items, cus);
+  pl.big = (double)std::max(max_item, 1) <= 1.25 * mean;
+  if (!pl.big) {  // 128 queries per workgroup, whole query tiles
+    pl.BQ = 128;
+    pl.n_qtiles = (T + 127) / 128;
+    return pl;
+  }
+  pl.n_qtiles = nq;
+  if (!any_split || ents.size() > (size_t)kMaxItemsPerHead) return pl;
+  {  // rounds of an XCD's list: with few, order it by cost rather than head by head
+    const int grid = (int)std::min<int64_t>(n_items, cus);
+    if (grid % 8 == 0 && d.H % 8 == 0) {
+      const int64_t J = grid / 8, list = (int64_t)(d.H / 8) * (int64_t)ents.size();
+      pl.cost_major = (list + J - 1) / J <= 4;
+    }
+  }
+  // partial-result slots: the parts of each split query tile, consecutive
+  std::vector<int> slot0(nq, -1);
+  for (int i = 0; i < nq; ++i)
+    if (parts[i] > 1) {
+      slot0[i] = pl.slots_per_head;
+      pl.split_tiles.push_back((uint32_t)i | ((uint32_t)parts[i] << 10) | ((uint32_t)pl.slots_per_head << 16));
+      pl.slots_per_head += parts[i];
+    }
+  for (const Ent& e : ents) {
+    const int sl = e.parts > 1 ? slot0[e.qt] + e.part : 0;
+    pl.items.push_back((uint32_t)e.qt | ((uint32_t)e.part << 10) | ((uint32_t)e.parts << 13) | ((uint32_t)sl << 16));
+  }
+  pl.ws_bytes = (size_t)d.H * pl.slots_per_head * pl.BQ * (DV * 4 + 8);
+  return pl;
 }
 
 }  // namespace
@@ -424,7 +576,10 @@ bool fast_prefill_attn_supported(const Dims& d) {
   return d.act == 1 && d.dn + d.dr == DQK && d.dv == DV && d.scale > 0.f;
 }
 
-size_t fast_prefill_attn_ws_bytes(const Dims&, int) { return 0; }
+size_t fast_prefill_attn_ws_bytes(const Dims& d, int T) {
+  if (!fast_prefill_attn_supported(d) || T <= 0) return 0;
+  return prefill_plan(d, T, 0, true, device_cu_count()).ws_bytes;
+}
 
 hipError_t fast_prefill_attn(const Dims& d, const void* q, const void* k, const void* v, int T, void* o, void* ws,
                              hipStream_t s) {
@@ -432,7 +587,7 @@ hipError_t fast_prefill_attn(const Dims& d, const void* q, const void* k, const 
 }
 
 hipError_t fast_prefill_attn_offset(const Dims& d, const void* q, const void* k, const void* v, int T, int q_off,
-                                    void* o, void*, hipStream_t s) {
+                                    void* o, void* ws, hipStream_t s) {
   PrefillArgs P;
   P.q = (const bf16_t*)q;
   P.k = (const bf16_t*)k;
@@ -443,24 +598,32 @@ hipError_t fast_prefill_attn_offset(const Dims& d, const void* q, const void* k,
   P.q_off = q_off;
   P.Tk = q_off + T;
   P.scale_log2 = d.scale * 1.4426950408889634f;
-  // one workgroup per CU (the four K/V stages take all 160 KB of a CU's LDS).  256 queries per
-  // workgroup (8 waves, two per SIMD playing ping-pong) unless the items are then too few and
-  // uneven to share out: the larger of the heaviest item and the mean load per workgroup must
-  // stay within 1.25x the mean; else 128 queries (4 waves)
+  // one workgroup per CU (the four K/V stages take all 160 KB of a CU's LDS)
   const int cus = device_cu_count();
-  const int nq8 = (T + 255) / 256;
-  int64_t sum8 = 0;
-  for (int i = 0; i < nq8; ++i) sum8 += (q_off + std::min(T, 256 * (i + 1)) - 1) / KT + 1;
-  const int64_t max8 = (q_off + T - 1) / KT + 1;
-  const int64_t items8 = (int64_t)d.H * nq8;
-  const double mean8 = (double)sum8 * d.H / (double)std::min<int64_t>(items8, cus);
-  const bool big = (double)std::max<int64_t>(max8, 1) <= 1.25 * mean8;
-  const int BQ = big ? 256 : 128;
-  P.n_qtiles = (T + BQ - 1) / BQ;
-  const int total = d.H * P.n_qtiles;
-  const int grid = std::min(total, cus);
-  if (big) prefill_attn_kernel<8><<<grid, 512, 0, s>>>(P);
+  const PrefillPlan pl = prefill_plan(d, T, q_off, q_off == 0 && ws != nullptr, cus);
+  P.n_qtiles = pl.n_qtiles;
+  P.n_items = (int)pl.items.size();
+  P.cost_major = pl.cost_major ? 1 : 0;
+  P.slots_per_head = pl.slots_per_head;
+  P.part_o = (float*)ws;
+  P.part_ml = ws ? (float*)((char*)ws + (size_t)d.H * pl.slots_per_head * pl.BQ * DV * 4) : nullptr;
+  for (size_t i = 0; i < pl.items.size(); ++i) P.items[i] = pl.items[i];
+  const int per_head = P.n_items > 0 ? P.n_items : P.n_qtiles;
+  const int grid = std::min(d.H * per_head, cus);
+  if (pl.big) prefill_attn_kernel<8><<<grid, 512, 0, s>>>(P);
   else prefill_attn_kernel<4><<<grid, 256, 0, s>>>(P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.split_tiles.empty()) return e;
+  MergeArgs M;
+  M.part_o = P.part_o;
+  M.part_ml = P.part_ml;
+  M.o = P.o;
+  M.T = T;
+  M.H = d.H;
+  M.BQ = pl.BQ;
+  M.slots_per_head = pl.slots_per_head;
+  for (size_t i = 0; i < pl.split_tiles.size(); ++i) M.tiles[i] = pl.split_tiles[i];
+  prefill_merge_kernel<<<dim3((unsigned)pl.split_tiles.size() * d.H, pl.BQ * (DV / 4) / 256), 256, 0, s>>>(M);
   return hipGetLastError();
 }
 
