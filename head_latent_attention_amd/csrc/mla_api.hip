@@ -321,8 +321,17 @@ mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, 
   }
   Partials P1;
   const WeightView w1q = d.Lq > 0 ? view(d, w->wq_a, d.Lq) : view(d, w->wq_b, HQ);
-  mla_status st = project(d, x, d.D, w1q, NQ1, view(d, w->wkv_a, d.R()), n, NQ1 + d.R(), d.D, ws.P1, &P1, s, nullptr,
-                          nullptr, ws.qz);
+  // without a query latent the stage-1 projection holds the query itself: its RoPE may run in
+  // the projection (the other columns stay partial sums for the row builder)
+  GemmEpilogue e1;
+  e1.kind = GemmEpilogue::QUERY;
+  e1.seg1_partials = true;
+  e1.y = q;
+  e1.cosT = cosT;
+  e1.sinT = sinT;
+  bool q_done = false;
+  mla_status st = project(d, x, d.D, w1q, NQ1, view(d, w->wkv_a, d.R()), n, NQ1 + d.R(), d.D, ws.P1, &P1, s,
+                          d.Lq > 0 ? nullptr : &e1, &q_done, ws.qz);
   if (st != MLA_OK) return st;
   HIP_TRY(row_builder(d, P1, P1.offset(NQ1), n, w->q_norm_w, w->kv_norm_w, cosT, sinT, ws.cqn, ws.cn, kv_cache,
                       n_slots, slot_mapping, kbuf, s));
@@ -339,6 +348,7 @@ mla_status front_end(const Dims& d, const mla_weights* w, const void* x, int n, 
     if (st != MLA_OK) return st;
     if (fused) return MLA_OK;
   }
+  if (q_done) return MLA_OK;
   HIP_TRY(q_epilogue(d, PQ, n, cosT, sinT, q, s));
   return MLA_OK;
 }

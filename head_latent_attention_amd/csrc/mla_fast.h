@@ -18,6 +18,10 @@ struct FastDecodeWs {
 struct GemmEpilogue {
   enum Kind { PARTIALS = 0, STORE = 1, QUERY = 2, KV = 3 };
   int kind = PARTIALS;
+  // the consumer takes W0's columns [0, n_split) only (y with row stride n_split); W1's columns
+  // stay partial sums in `out` (QUERY on the large-tile path: the query RoPE of a projection
+  // without a query latent, whose other columns feed the row builder)
+  bool seg1_partials = false;
   void* y = nullptr;   // STORE: y; QUERY: q; KV: k
   void* y2 = nullptr;  // KV: v
   const float* cosT = nullptr;

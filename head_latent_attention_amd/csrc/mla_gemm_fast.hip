@@ -56,6 +56,8 @@ struct EpiArgs {
   const float* cosT;
   const float* sinT;
   int H, dn, dr, dv;
+  int kind1 = GemmEpilogue::PARTIALS;  // the large-tile kernels: consumer of the W1 segment's tiles
+  int64_t ldy = 0;                     // row stride of y for STORE / QUERY (0: N)
 };
 
 // Epilogue of the BM x 128 tile kernels (4 waves; acc[mt][nt][i] is tile row
@@ -579,13 +581,13 @@ __device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, 
 // row; `st` is 128 KB of stage buffers no wave reads any more) so that global stores are
 // whole 16-byte chunks of 8 consecutive columns; the query's RoPE is applied on the way (the
 // partner column of a pair sits in lane j ^ 1).
-__device__ __forceinline__ void big_epilogue(const EpiArgs& E, f32x4 (&acc)[8][4], bf16_t* st, int M, int N,
-                                             float* C, int64_t ldc, int64_t split_off, int m0, int n0, int w,
+__device__ __forceinline__ void big_epilogue(const EpiArgs& E, int kind, f32x4 (&acc)[8][4], bf16_t* st, int M,
+                                             int N, float* C, int64_t ldc, int64_t split_off, int m0, int n0, int w,
                                              int lane) {
   const int tid = threadIdx.x, g = lane >> 4, j = lane & 15, wm = w >> 2, wn = w & 3;
   const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
   const int mb = 128 * wm + 4 * g;  // tile row of acc[mt][.][i]: mb + 16 mt + i
-  if (E.kind == GemmEpilogue::PARTIALS) {
+  if (kind == GemmEpilogue::PARTIALS) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int n = n0 + 64 * wn + 16 * nt + j;
@@ -602,7 +604,7 @@ __device__ __forceinline__ void big_epilogue(const EpiArgs& E, f32x4 (&acc)[8][4
   }
   lds_barrier();  // every wave is done with the stage buffers
   auto chunk_of = [](int r, int c) { return 32 * r + (c ^ (r & 31)); };  // 16-byte chunk slot
-  const bool query = E.kind == GemmEpilogue::QUERY;
+  const bool query = kind == GemmEpilogue::QUERY;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int c = 64 * wn + 16 * nt + j;
@@ -662,12 +664,12 @@ __device__ __forceinline__ void big_epilogue(const EpiArgs& E, f32x4 (&acc)[8][4
     const int m = m0 + r, n = n0 + 8 * c8;
     if (m >= M || n >= N) continue;
     const uint4 v = *(const uint4*)&st[chunk_of(r, c8) * 8];
-    if (E.kind == GemmEpilogue::KV) {
+    if (kind == GemmEpilogue::KV) {
       const int h = n / dkv, u = n - h * dkv;
       bf16_t* dst = u < E.dn ? E.y + ((int64_t)m * E.H + h) * dqk + u : E.y2 + ((int64_t)m * E.H + h) * E.dv + (u - E.dn);
       *(uint4*)dst = v;
     } else {
-      *(uint4*)&E.y[(int64_t)m * N + n] = v;
+      *(uint4*)&E.y[(int64_t)m * (E.ldy > 0 ? E.ldy : N) + n] = v;
     }
   }
 }
@@ -717,8 +719,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
     big_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s >= -1 && s + 1 < nsteps, (const uint4*)a_cur,
              (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx, acc, apre, bpre, w, lane);
   }
-  big_epilogue(E, acc, (bf16_t*)&As[0][0], G.M, G.N, G.C, G.ldc, (int64_t)blockIdx.z * G.split_stride, m0, n0, w,
-               lane);
+  big_epilogue(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&As[0][0], G.M, G.N, G.C, G.ldc,
+               (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -892,8 +894,8 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(BigArgs G, EpiArgs E) {
             (const float*)sc, (const uint4*)a_cur, (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx,
             acc, apre, bpre, w, lane);
   }
-  big_epilogue(E, acc, (bf16_t*)&smem[0], G.M, G.N, G.C, G.ldc, (int64_t)blockIdx.z * G.split_stride, m0, n0, w,
-               lane);
+  big_epilogue(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&smem[0], G.M, G.N, G.C, G.ldc,
+               (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
 }
 
 bool w8_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda, int k_split) {
@@ -1158,8 +1160,8 @@ __global__ __launch_bounds__(512, 1) void gemm_f8_kernel(F8Args G, EpiArgs E) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{NAN, NAN, NAN, NAN};
   }
-  big_epilogue(E, acc, (bf16_t*)&smem[0][0], G.M, G.N, G.C, G.ldc, (int64_t)blockIdx.z * G.split_stride, m0, n0, w,
-               lane);
+  big_epilogue(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&smem[0][0], G.M, G.N, G.C, G.ldc,
+               (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
 }
 
 bool f8_ok(const Dims& d, int M, int N, int K, int n_split, int k_split) {
@@ -1204,8 +1206,21 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   EpiArgs E{GemmEpilogue::PARTIALS, nullptr, nullptr, nullptr, nullptr, d.H, d.dn, d.dr, d.dv};
   const bool aligned = n_split >= N || n_split % BN == 0;
-  if (epi && fast_gemm_fusable(d, M, N, K, n_split, epi->kind)) {
-    E.kind = epi->kind;
+  if (epi && epi->seg1_partials) {
+    // W0's tiles to the query consumer, W1's as partial sums: the large-tile kernel, K unsplit
+    const bool pairs_ok = d.dn % 2 == 0 && (d.dn + d.dr) % 2 == 0;
+    if (epi->kind == GemmEpilogue::QUERY && pairs_ok && n_split < N && n_split % kBigN == 0 && n_split % 8 == 0 &&
+        p.splits == 1 && big_ok(d, M, N, K, n_split, lda)) {
+      E.kind = GemmEpilogue::QUERY;
+      E.kind1 = GemmEpilogue::PARTIALS;
+      E.y = (bf16_t*)epi->y;
+      E.ldy = n_split;
+      E.cosT = epi->cosT;
+      E.sinT = epi->sinT;
+      if (fused) *fused = true;
+    }
+  } else if (epi && fast_gemm_fusable(d, M, N, K, n_split, epi->kind)) {
+    E.kind = E.kind1 = epi->kind;
     E.y = (bf16_t*)epi->y;
     E.y2 = (bf16_t*)epi->y2;
     E.cosT = epi->cosT;
@@ -1243,8 +1258,8 @@ hipError_t fast_gemm_f8(const Dims& d, const uint8_t* A8, const uint8_t* Ae, con
   if (fused) *fused = false;
   if (!fast_gemm_f8_ok(d, M, N, K, n_split)) return hipErrorInvalidValue;
   EpiArgs E{GemmEpilogue::PARTIALS, nullptr, nullptr, nullptr, nullptr, d.H, d.dn, d.dr, d.dv};
-  if (epi && fast_gemm_fusable(d, M, N, K, n_split, epi->kind)) {
-    E.kind = epi->kind;
+  if (epi && !epi->seg1_partials && fast_gemm_fusable(d, M, N, K, n_split, epi->kind)) {
+    E.kind = E.kind1 = epi->kind;
     E.y = (bf16_t*)epi->y;
     E.y2 = (bf16_t*)epi->y2;
     E.cosT = epi->cosT;
