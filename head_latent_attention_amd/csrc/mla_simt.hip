@@ -186,10 +186,117 @@ __global__ __launch_bounds__(512) void row_builder_kernel(
   }
 }
 
+// bf16 rows with every width a multiple of 8: one 256-thread workgroup per token, each thread
+// handling up to MAXC 8-column chunks of [q latent | kv latent | k_pe] (16-byte partial loads in
+// part_ld's order, both sums of squares in one block reduction, 16-byte stores), the roped k_pe
+// staged in LDS for the per-head broadcast.
+template <int MAXC>
+__global__ __launch_bounds__(256) void row_builder_bf16x8_kernel(
+    Partials Yq, Partials Ykv, int Lq, int Lkv, int dr, const float* __restrict__ gq, const float* __restrict__ gkv,
+    float eps, const float* __restrict__ cosT, const float* __restrict__ sinT, bf16_t* __restrict__ cqn,
+    bf16_t* __restrict__ cn, bf16_t* __restrict__ cache, int64_t n_slots, const int32_t* __restrict__ slot_mapping,
+    bf16_t* __restrict__ kbuf, int H, int dn) {
+  __shared__ float red[2][4];
+  __shared__ __attribute__((aligned(16))) uint4 kpe_s[32];  // dr <= 256
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nq = Lq / 8, nk = Lkv / 8, nr = dr / 8, total = nq + nk + nr;
+  const int R = Lkv + dr, dqk = dn + dr, half = dr >> 1;
+  float v[MAXC][8];
+  float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int e = tid + 256 * c;
+    if (e < nq) {
+      part_ld8(Yq, t, 8 * e, v[c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ssq += v[c][i] * v[c][i];
+    } else if (e < nq + nk) {
+      part_ld8(Ykv, t, 8 * (e - nq), v[c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ssk += v[c][i] * v[c][i];
+    } else if (e < total) {
+      part_ld8(Ykv, t, Lkv + 8 * (e - nq - nk), v[c]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ssq += __shfl_xor(ssq, off);
+    ssk += __shfl_xor(ssk, off);
+  }
+  if (lane == 0) {
+    red[0][w] = ssq;
+    red[1][w] = ssk;
+  }
+  __syncthreads();
+  const float rq = nq > 0 ? rsqrtf(((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / (float)Lq + eps) : 0.f;
+  const float rk = rsqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / (float)Lkv + eps);
+  int64_t slot = -1;
+  if (cache != nullptr && slot_mapping != nullptr) {
+    slot = slot_mapping[t];
+    if (slot >= n_slots) slot = -1;
+  }
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int e = tid + 256 * c;
+    float y[8];
+    if (e < nq) {
+      if (!cqn) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = v[c][i] * rq * gq[8 * e + i];
+      *(uint4*)(cqn + t * Lq + 8 * e) =
+          make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+    } else if (e < nq + nk) {
+      const int i0 = 8 * (e - nq);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = v[c][i] * rk * gkv[i0 + i];
+      const uint4 pk =
+          make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+      if (cn) *(uint4*)(cn + t * Lkv + i0) = pk;
+      if (slot >= 0) *(uint4*)(cache + slot * R + i0) = pk;
+    } else if (e < total) {
+      const int ch = e - nq - nk, p0 = 4 * ch;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float cs = cosT[t * half + p0 + i], sn = sinT[t * half + p0 + i];
+        const float x0 = v[c][2 * i], x1 = v[c][2 * i + 1];
+        y[2 * i] = x0 * cs - x1 * sn;
+        y[2 * i + 1] = x0 * sn + x1 * cs;
+      }
+      const uint4 pk =
+          make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+      if (slot >= 0) *(uint4*)(cache + slot * R + Lkv + 8 * ch) = pk;
+      kpe_s[ch] = pk;
+    }
+  }
+  if (!kbuf) return;
+  __syncthreads();
+  bf16_t* krow = kbuf + t * H * dqk + dn;
+  for (int e = tid; e < H * nr; e += 256) {
+    const int h = e / nr, c = e - h * nr;
+    *(uint4*)(krow + (int64_t)h * dqk + 8 * c) = kpe_s[c];
+  }
+}
+
 hipError_t row_builder(const Dims& d, const Partials& Yq, const Partials& Ykv, int T, const float* gq, const float* gkv, const float* cosT,
                        const float* sinT, void* cqn, void* cn, void* cache, int64_t n_slots,
                        const int32_t* slot_mapping, void* kbuf, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  const int total8 = (d.Lq + d.Lkv + d.dr) / 8;
+  auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (d.act == 1 && d.Lq % 8 == 0 && d.Lkv % 8 == 0 && d.dr % 8 == 0 && d.dn % 8 == 0 && d.dr <= 256 &&
+      total8 <= 512 && (d.Lq == 0 || part_vec8_ok(Yq)) && part_vec8_ok(Ykv) && al16(cqn) && al16(cn) && al16(cache) &&
+      al16(kbuf)) {
+    if (total8 <= 256)
+      row_builder_bf16x8_kernel<1><<<T, 256, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT,
+                                                     (bf16_t*)cqn, (bf16_t*)cn, (bf16_t*)cache, n_slots, slot_mapping,
+                                                     (bf16_t*)kbuf, d.H, d.dn);
+    else
+      row_builder_bf16x8_kernel<2><<<T, 256, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT,
+                                                     (bf16_t*)cqn, (bf16_t*)cn, (bf16_t*)cache, n_slots, slot_mapping,
+                                                     (bf16_t*)kbuf, d.H, d.dn);
+    return hipGetLastError();
+  }
   dim3 grid(T, 2);
   if (d.act == 0)
     row_builder_kernel<float><<<grid, 512, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT, (float*)cqn,
