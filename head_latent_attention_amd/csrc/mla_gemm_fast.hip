@@ -906,7 +906,7 @@ bool w8_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda, int k_s
 
 bool big_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda) {
   // activation offsets are 32-bit byte offsets from the K step's column
-  return d.wk == W_BF16 && M > 1024 && K % kBigK == 0 && (n_split >= N || n_split % kBigN == 0) && N % 8 == 0 &&
+  return d.wk == W_BF16 && M > 512 && K % kBigK == 0 && (n_split >= N || n_split % kBigN == 0) && N % 8 == 0 &&
          (n_split >= N || (N - n_split) % 8 == 0) && ((int64_t)M * lda + K) * 2 < 0x7FFFFFF0LL;
 }
 
@@ -916,6 +916,25 @@ struct Plan {
 
 Plan plan(int M, int N, int K, int wk) {
   Plan p;
+  if (M > 512 && M <= 1024 && wk == W_BF16) {  // 256 x 256 tiles, few of them: K split in 1, 2 or 4
+    // ranges (>= 1024 k each), whichever gives the fewest rounds of 256 workgroups per unit of
+    // work (the partial sums of M <= 1024 rows are small)
+    p.bm = 128;
+    const int64_t tiles = (int64_t)((N + 255) / 256) * ((M + 255) / 256);
+    int best = 1;
+    double best_t = (double)((tiles + 255) / 256);
+    for (int sp = 2; sp <= 4; sp *= 2) {
+      if (K % (64 * sp) != 0 || K / sp < 1024) break;
+      const double t = (double)((tiles * sp + 255) / 256) / sp;
+      if (t < best_t) {
+        best = sp;
+        best_t = t;
+      }
+    }
+    p.splits = best;
+    p.k_split = K / best;
+    return p;
+  }
   if (M > 1024) {  // prefill shapes (256 x 256 tiles): whole K per workgroup, unless the
     // tile count leaves most of a last round of one workgroup per CU idle and K is long:
     // then two K ranges (partial sums) halve the rounds' length

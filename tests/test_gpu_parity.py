@@ -27,6 +27,8 @@ EDGE_FP8 = synth.custom(W[5], 105, "edge-decode-fp8", B=6)
 # fp8 weights at 64 < M <= 1024 (the mid-M fp8 kernel): ragged rows, a partial last column tile of
 # the kv segment, the query up-projection unsplit (RoPE fused in the kernel)
 MID_FP8 = synth.custom(W[5], 110, "mid-fp8-h16", hidden=1024, n_heads=16, q_lora_rank=256, B=130)
+# bf16 projections at 512 < M <= 1024 (the large-tile kernel with few tiles, K split by rounds)
+MID_V3 = synth.custom(W[4], 111, "mid-v3-prefill", hidden=1024, n_heads=16, q_lora_rank=256, T=700)
 EDGE_CTX = np.array([1, 63, 64, 65, 200, 1000], np.int32)
 
 _cache = {}
@@ -48,7 +50,7 @@ def _sample_rows(T, n_rand=12, seed=0):
 
 
 # ----------------------------------------------------------------------------- qkv prefill
-@pytest.mark.parametrize("w", [SMALL_V3, SMALL_V2, W[2], W[4]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [SMALL_V3, SMALL_V2, MID_V3, W[2], W[4]], ids=lambda w: w.name)
 def test_qkv_prefill(w):
     need_gpu()
     import head_latent_attention_amd as mla
@@ -252,7 +254,7 @@ def test_decode_attn_many_short_sequences(w):
 
 # ----------------------------------------------------------------------------- output projection
 @pytest.mark.parametrize("w,M", [(SMALL_V3, 300), (EDGE_FP8, 7), (W[2], 4096), (W[3], 64), (W[4], 8192), (W[5], 256),
-                                 (MID_FP8, 300), (W[5], 1000)],
+                                 (MID_FP8, 300), (W[5], 1000), (MID_V3, 700), (W[4], 1000)],
                          ids=lambda c: str(c) if isinstance(c, int) else c.name)
 def test_out_proj(w, M):
     need_gpu()
