@@ -541,37 +541,46 @@ __device__ __forceinline__ bf16x8 big_b(const uint4* __restrict__ ws, int nt, in
   return __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-constexpr int kBigPreA = 2;  // A operands of the next step read ahead (with all of its B operands)
-
-// One K step: the matrix ops of stage `as/ws` (compute), whose B operands and first kBigPreA A
-// operands were read during the previous step (apre, bpre), then this step's share of the
-// copies, then (pre) the first operands of the next stage `as1/ws1`, so that the next step's
-// first matrix op does not wait for LDS.  Every LDS access of a step is issued here, through
-// restrict pointers.
+// One K step: this step's share of the copies into the free stage `as_nx/ws_nx`, then the
+// matrix ops of the current stage, whose operands af/bf were read during the previous step.
+// The ops run column block by column block (nt outer), so that each operand register is dead
+// right after its last op: the B operand of block nt after the block, the A operand of row
+// block mt after the last block's op mt.  The operand of the next stage `as1/ws1` is read into
+// that register at once, so that every read of the next step is in flight (most of them long
+// done) when the barrier in front of it releases, and no wave waits for LDS after a barrier.
+// The next stage is complete for this whole step (its copies were waited for, and made visible
+// by the barrier, at the top of the step); in the last step the reads return unused values.
+// `pre` alone (no compute) reads all operands of the next stage: the first step's.  Every LDS
+// access of a step is issued here, through restrict pointers.
 __device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, const BigCopyPlan& cp, bool copy,
-                                         int k_pf, bool compute, bool pre, const uint4* __restrict__ as,
-                                         const uint4* __restrict__ as1, const uint4* __restrict__ ws1,
-                                         uint4* __restrict__ as_nx, uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4],
-                                         bf16x8 (&apre)[kBigPreA], bf16x8 (&bpre)[4], int w, int lane) {
+                                         int k_pf, bool compute, bool pre, const uint4* __restrict__ as1,
+                                         const uint4* __restrict__ ws1, uint4* __restrict__ as_nx,
+                                         uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4], bf16x8 (&af)[8],
+                                         bf16x8 (&bf)[4], int w, int lane) {
+  if (copy) big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
   if (compute) {
-    bf16x8 af[8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) af[mt] = mt < kBigPreA ? apre[mt] : big_a(as, mt, w, lane);
-    // the copies go behind the operand reads, which the matrix ops wait for
-    if (copy) big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
+    for (int nt = 0; nt < 4; ++nt) {
+      // the B reads after blocks 0 and 1 are long done; retiring them keeps at most 12 LDS reads
+      // in flight at the loop's back edge, so that the compiler's count of them stays exact and
+      // the next step's first op waits for its own operands only (lgkmcnt(2))
+      if (nt == 3) __builtin_amdgcn_s_waitcnt(0xC27F);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 8; ++mt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+        if (nt == 3) af[mt] = big_a(as1, mt, w, lane);
+      }
+      bf[nt] = big_b(ws1, nt, w, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if (pre) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bpre[nt], acc[mt][nt], 0, 0, 0);
-  } else if (copy) {
-    big_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
-  }
-  if (pre) {
+    for (int nt = 0; nt < 4; ++nt) bf[nt] = big_b(ws1, nt, w, lane);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) bpre[nt] = big_b(ws1, nt, w, lane);
-#pragma unroll
-    for (int mt = 0; mt < kBigPreA; ++mt) apre[mt] = big_a(as1, mt, w, lane);
+    for (int mt = 0; mt < 8; ++mt) af[mt] = big_a(as1, mt, w, lane);
+    // these 16 reads are more than the LDS counter tracks in order: completing them here keeps
+    // the loop's wait model exact
+    __builtin_amdgcn_s_waitcnt(0xC07F);
   }
 }
 
@@ -693,12 +702,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 apre[kBigPreA], bpre[4];
+  bf16x8 af[8], bf[4];
 #pragma unroll
-  for (int i = 0; i < kBigPreA; ++i) apre[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+  for (int i = 0; i < 8; ++i) af[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) bpre[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
-  // iteration s: matrix ops of step s (s >= 0), copies of step s+3, first operands of step s+1
+  for (int i = 0; i < 4; ++i) bf[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+  // iteration s: copies of step s+3, matrix ops of step s (s >= 0), operands of step s+1
   for (int s = -(kBigStages - 1); s < nsteps; ++s) {
     if (s >= -1) {
       // steps s and s+1 in LDS: the copies issued after step s+1's are those of step s+2
@@ -707,17 +716,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
       lds_barrier();
     }
     const int s_pf = s + kBigStages - 1;
-    const int b_pf = (s_pf + kBigStages) % kBigStages, b_cur = s < 0 ? 0 : s % kBigStages;
+    const int b_pf = (s_pf + kBigStages) % kBigStages;
     const int b_1 = (s + 1 + kBigStages) % kBigStages;
     // opaque copies of the stage pointers: accesses through them keep the restrict scopes of
     // big_step's parameters (pointers the compiler can trace to the __shared__ arrays lose them,
     // and every operand read would then wait for the copies in flight)
     typedef __attribute__((address_space(3))) uint4 lds_uint4;
-    lds_uint4 *a_cur = (lds_uint4*)As[b_cur], *a_1 = (lds_uint4*)As[b_1], *w_1 = (lds_uint4*)Ws[b_1];
+    lds_uint4 *a_1 = (lds_uint4*)As[b_1], *w_1 = (lds_uint4*)Ws[b_1];
     lds_uint4 *a_nx = (lds_uint4*)As[b_pf], *w_nx = (lds_uint4*)Ws[b_pf];
-    asm volatile("" : "+s"(a_cur), "+s"(a_1), "+s"(w_1), "+s"(a_nx), "+s"(w_nx));
-    big_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s >= -1 && s + 1 < nsteps, (const uint4*)a_cur,
-             (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx, acc, apre, bpre, w, lane);
+    asm volatile("" : "+s"(a_1), "+s"(w_1), "+s"(a_nx), "+s"(w_nx));
+    big_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s == -1, (const uint4*)a_1, (const uint4*)w_1,
+             (uint4*)a_nx, (uint4*)w_nx, acc, af, bf, w, lane);
   }
   big_epilogue(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&As[0][0], G.M, G.N, G.C, G.ldc,
                (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
@@ -800,6 +809,8 @@ __device__ __forceinline__ bf16x8 w8_b(const uint4* __restrict__ ws, int nt, int
   }
   return as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
 }
+
+constexpr int kBigPreA = 2;  // A operands of the next step read ahead (with all of its B operands)
 
 // One K step, as big_step: matrix ops of the current stage, this step's copies, then the first
 // operands of the next stage (its B operands decoded with that step's block scale s1, read
