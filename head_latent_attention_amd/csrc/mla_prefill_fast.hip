@@ -195,8 +195,13 @@ __device__ __forceinline__ void mma_block(const PrefillArgs& P, int h, const Cop
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
+    // no scores: the registers are only redefined (no instructions), so that the previous
+    // tile's scores are dead here; the softmax does not read them on this path
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 4; ++mt) {
+      asm volatile("" : "=v"(s[mt][0]));
+      asm volatile("" : "=v"(s[mt][1]));
+    }
   }
   // the copies go last, behind this step's LDS reads
   if (copy) issue_kv_copy<NW>(P, h, kt_pf, cp, kn, vn, w, lane);
@@ -234,10 +239,14 @@ __device__ __forceinline__ void softmax_block(const PrefillArgs& P, int k0, int 
   float m_new[2], corr[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    float mm[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) mm[mt] = fmaxf(fmaxf(x[nt][mt][0], x[nt][mt][1]), fmaxf(x[nt][mt][2], x[nt][mt][3]));
-    const float mx = xmax16_32(fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]))) * P.scale_log2;
+    // two chains of three-input maxima over the lane's 16 scores (8 instructions)
+    float ma = fmaxf(fmaxf(x[nt][0][0], x[nt][0][1]), x[nt][0][2]);
+    float mb = fmaxf(fmaxf(x[nt][2][0], x[nt][2][1]), x[nt][2][2]);
+    ma = fmaxf(fmaxf(ma, x[nt][0][3]), x[nt][1][0]);
+    mb = fmaxf(fmaxf(mb, x[nt][2][3]), x[nt][3][0]);
+    ma = fmaxf(fmaxf(ma, x[nt][1][1]), x[nt][1][2]);
+    mb = fmaxf(fmaxf(mb, x[nt][3][1]), x[nt][3][2]);
+    const float mx = xmax16_32(fmaxf(fmaxf(ma, x[nt][1][3]), fmaxf(mb, x[nt][3][3]))) * P.scale_log2;
     m_new[nt] = (m_run[nt] == -INFINITY || mx > m_run[nt] + kRescaleThreshold) ? mx : m_run[nt];
     corr[nt] = m_run[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new[nt]);
   }
