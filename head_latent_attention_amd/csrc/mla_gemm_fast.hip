@@ -792,13 +792,17 @@ __device__ __forceinline__ void w8_issue(const BigArgs& G, const WeightView& W, 
   dma16_buf((const uint8_t*)W.w + (int64_t)k0 * W.ld, 0x7FFFFFF0u, cp.off[2], ws + 64 * w);
 }
 
-// B operand of 16-column tile nt of the wave: lane (g, j) gets k = 8g .. 8g+7 of column
-// 64*(w & 3) + 16*nt + j (byte b of the read = row 8g + b), decoded with block scale s.
-__device__ __forceinline__ bf16x8 w8_b(const uint4* __restrict__ ws, int nt, int w, int lane, float s) {
+// B operand of 16-column tile nt of the wave, as one transposing byte read (w8_raw: lane (g, j)
+// gets k = 8g .. 8g+7 of column 64*(w & 3) + 16*nt + j, byte b = row 8g + b) decoded with block
+// scale s (w8_dec).
+__device__ __forceinline__ i32x2w w8_raw(const uint4* __restrict__ ws, int nt, int w, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int k = 8 * g + (j >> 1);
   const int c = (4 * (w & 3) + nt) ^ w8_swz(k);
-  const i32x2w p = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2w*)((const char*)ws + (16 * k + c) * 16 + 8 * (j & 1)));
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2w*)((const char*)ws + (16 * k + c) * 16 + 8 * (j & 1)));
+}
+
+__device__ __forceinline__ bf16x8 w8_dec(i32x2w p, float s) {
   uint32_t o[4];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -810,36 +814,44 @@ __device__ __forceinline__ bf16x8 w8_b(const uint4* __restrict__ ws, int nt, int
   return as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-constexpr int kBigPreA = 2;  // A operands of the next step read ahead (with all of its B operands)
-
-// One K step, as big_step: matrix ops of the current stage, this step's copies, then the first
-// operands of the next stage (its B operands decoded with that step's block scale s1, read
-// from the scale table sc).  Every LDS access goes through restrict pointers.
+// One K step, as big_step: this step's copies, then the matrix ops of the current stage column
+// block by column block, each operand register refilled from the next stage `as1/ws1` right
+// after its last op.  A B operand's byte read is issued one block before the block that last
+// uses the register, and decoded (with the next step's block scale, from the scale table sc)
+// right after that block, so no decode waits for a fresh read.  `pre` alone (no compute) reads
+// and decodes all operands of the next stage: the first step's.  Every LDS access goes through
+// restrict pointers.
 __device__ __forceinline__ void w8_step(const BigArgs& G, const WeightView& W, const W8CopyPlan& cp, bool copy,
                                         int k_pf, bool compute, bool pre, int sc_idx, const float* __restrict__ sc,
-                                        const uint4* __restrict__ as, const uint4* __restrict__ as1,
-                                        const uint4* __restrict__ ws1, uint4* __restrict__ as_nx,
-                                        uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4], bf16x8 (&apre)[kBigPreA],
-                                        bf16x8 (&bpre)[4], int w, int lane) {
+                                        const uint4* __restrict__ as1, const uint4* __restrict__ ws1,
+                                        uint4* __restrict__ as_nx, uint4* __restrict__ ws_nx, f32x4 (&acc)[8][4],
+                                        bf16x8 (&af)[8], bf16x8 (&bf)[4], int w, int lane) {
+  if (copy) w8_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
+  const float s1 = sc[sc_idx];
   if (compute) {
-    bf16x8 af[8];
+    i32x2w raw = w8_raw(ws1, 0, w, lane);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) af[mt] = mt < kBigPreA ? apre[mt] : big_a(as, mt, w, lane);
-    if (copy) w8_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
+    for (int nt = 0; nt < 4; ++nt) {
+      if (nt == 3) __builtin_amdgcn_s_waitcnt(0xC17F);  // lgkmcnt(1): all but the last B read
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 8; ++mt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+        if (nt == 3) {
+          af[mt] = big_a(as1, mt, w, lane);
+          __builtin_amdgcn_sched_barrier(0);  // each refill after its op: old and new never both live
+        }
+      }
+      const i32x2w nxt = nt < 3 ? w8_raw(ws1, nt + 1, w, lane) : raw;
+      bf[nt] = w8_dec(raw, s1);
+      raw = nxt;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if (pre) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bpre[nt], acc[mt][nt], 0, 0, 0);
-  } else if (copy) {
-    w8_issue(G, W, cp, k_pf, as_nx, ws_nx, w);
-  }
-  if (pre) {
-    const float s1 = sc[sc_idx];
+    for (int mt = 0; mt < 8; ++mt) af[mt] = big_a(as1, mt, w, lane);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) bpre[nt] = w8_b(ws1, nt, w, lane, s1);
-#pragma unroll
-    for (int mt = 0; mt < kBigPreA; ++mt) apre[mt] = big_a(as1, mt, w, lane);
+    for (int nt = 0; nt < 4; ++nt) bf[nt] = w8_dec(w8_raw(ws1, nt, w, lane), s1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
   }
 }
 
@@ -871,17 +883,27 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(BigArgs G, EpiArgs E) {
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 apre[kBigPreA], bpre[4];
+  bf16x8 af[8], bf[4];
 #pragma unroll
-  for (int i = 0; i < kBigPreA; ++i) apre[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+  for (int i = 0; i < 8; ++i) af[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) bpre[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+  for (int i = 0; i < 4; ++i) bf[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
   // the wave's 64 columns lie in one 128-column block: row (w & 3) >> 1 of the scale table
   const int sc_row = ((w & 3) >> 1) * kW8MaxKBlocks - kg0;
-  // iteration s: matrix ops of step s (s >= 0), copies of step s + kW8Stages - 1, first
-  // operands of step s + 1
-  for (int s = -(kW8Stages - 1); s < nsteps; ++s) {
-    if (s >= -1) {
+  // iteration s: copies of step s + kW8Stages - 1, matrix ops of step s (s >= 0), operands of
+  // step s + 1.  The first kW8Stages - 2 iterations (copies only) run before the loop, so that
+  // the loop's liveness is that of the matrix steps alone.
+  typedef __attribute__((address_space(3))) uint4 lds_uint4;
+  for (int s = -(kW8Stages - 1); s < -1; ++s) {
+    const int s_pf = s + kW8Stages - 1;
+    if (s_pf < nsteps) {
+      lds_uint4* base = (lds_uint4*)smem;
+      w8_issue(G, W, cp, kbeg + s_pf * kBigK, (uint4*)(base + kW8StageA * s_pf),
+               (uint4*)(base + kW8StageA * kW8Stages + kW8StageW * s_pf), w);
+    }
+  }
+  for (int s = -1; s < nsteps; ++s) {
+    {
       // steps s and s+1 in LDS: in the steady state the copies of the kW8Stages - 3 steps after
       // them stay in flight; near the end every copy is waited for
       constexpr int kAhead = kW8Copies * (kW8Stages - 3);
@@ -890,20 +912,19 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(BigArgs G, EpiArgs E) {
       lds_barrier();
     }
     const int s_pf = s + kW8Stages - 1;
-    const int b_pf = (s_pf + kW8Stages) % kW8Stages, b_cur = s < 0 ? 0 : s % kW8Stages;
+    const int b_pf = (s_pf + kW8Stages) % kW8Stages;
     const int b_1 = (s + 1 + kW8Stages) % kW8Stages;
-    typedef __attribute__((address_space(3))) uint4 lds_uint4;
     typedef __attribute__((address_space(3))) float lds_float;
     lds_uint4* base = (lds_uint4*)smem;
-    lds_uint4 *a_cur = base + kW8StageA * b_cur, *a_1 = base + kW8StageA * b_1;
+    lds_uint4 *a_1 = base + kW8StageA * b_1;
     lds_uint4 *w_1 = base + kW8StageA * kW8Stages + kW8StageW * b_1;
     lds_uint4 *a_nx = base + kW8StageA * b_pf, *w_nx = base + kW8StageA * kW8Stages + kW8StageW * b_pf;
     lds_float* sc = (lds_float*)&scl[0][0];
-    asm volatile("" : "+s"(a_cur), "+s"(a_1), "+s"(w_1), "+s"(a_nx), "+s"(w_nx), "+s"(sc));
-    const int sc_idx = sc_row + (kbeg + (s + 1) * kBigK) / 128;
-    w8_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s >= -1 && s + 1 < nsteps, sc_idx,
-            (const float*)sc, (const uint4*)a_cur, (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx,
-            acc, apre, bpre, w, lane);
+    asm volatile("" : "+s"(a_1), "+s"(w_1), "+s"(a_nx), "+s"(w_nx), "+s"(sc));
+    // the next step's block scale (in the last step, a valid entry whose value is unused)
+    const int sc_idx = sc_row + (kbeg + min(s + 1, nsteps - 1) * kBigK) / 128;
+    w8_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s == -1, sc_idx, (const float*)sc,
+            (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx, acc, af, bf, w, lane);
   }
   big_epilogue(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&smem[0], G.M, G.N, G.C, G.ldc,
                (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
