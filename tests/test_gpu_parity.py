@@ -123,7 +123,7 @@ def test_prefill_attn(w, T, q_std):
 
 
 # ----------------------------------------------------------------------------- decode front end
-@pytest.mark.parametrize("w", [EDGE_DEC16, W[3], W[5], MID_FP8], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [EDGE_DEC16, EDGE_DEC128, W[3], W[5], MID_FP8], ids=lambda w: w.name)
 def test_decode_qkv_and_scatter(w):
     need_gpu()
     import head_latent_attention_amd as mla
