@@ -584,25 +584,28 @@ __device__ __forceinline__ void big_step(const BigArgs& G, const WeightView& W, 
   }
 }
 
-// Epilogue of the 256 x 256 tile kernels (8 waves of 128 x 64; acc[mt][nt][i] is tile row
-// 128*wm + 4*g + 16*mt + i, column 64*wn + 16*nt + j).  PARTIALS stores fp32 sums; the bf16
-// consumers stage the tile in LDS (row-major, 512-byte rows, 16-byte chunks XOR-swizzled by
-// row; `st` is 128 KB of stage buffers no wave reads any more) so that global stores are
-// whole 16-byte chunks of 8 consecutive columns; the query's RoPE is applied on the way (the
-// partner column of a pair sits in lane j ^ 1).
-__device__ __forceinline__ void big_epilogue(const EpiArgs& E, int kind, f32x4 (&acc)[8][4], bf16_t* st, int M,
+// Epilogue of the large-tile kernels: a TM x TN tile (256 x 256 with 8 waves of 128 x 64, or
+// 128 x 128 with 4 waves of 64 x 64; acc[mt][nt][i] is tile row (TM/2)*wm + 4*g + 16*mt + i,
+// column 64*wn + 16*nt + j).  PARTIALS stores fp32 sums; the bf16 consumers stage the tile in
+// LDS (row-major, TN*2-byte rows, 16-byte chunks XOR-swizzled by row; `st` is TM*TN*2 bytes of
+// stage buffers no wave reads any more) so that global stores are whole 16-byte chunks of 8
+// consecutive columns; the query's RoPE is applied on the way (the partner column of a pair
+// sits in lane j ^ 1).
+template <int TM, int TN>
+__device__ __forceinline__ void big_epilogue(const EpiArgs& E, int kind, f32x4 (&acc)[TM / 32][4], bf16_t* st, int M,
                                              int N, float* C, int64_t ldc, int64_t split_off, int m0, int n0, int w,
                                              int lane) {
-  const int tid = threadIdx.x, g = lane >> 4, j = lane & 15, wm = w >> 2, wn = w & 3;
+  constexpr int NWN = TN / 64, MT = TM / 32, CH = TN / 8;  // waves along N, row tiles, chunks per row
+  const int tid = threadIdx.x, g = lane >> 4, j = lane & 15, wm = w / NWN, wn = w % NWN;
   const int dqk = E.dn + E.dr, half = E.dr >> 1, dkv = E.dn + E.dv;
-  const int mb = 128 * wm + 4 * g;  // tile row of acc[mt][.][i]: mb + 16 mt + i
+  const int mb = (TM / 2) * wm + 4 * g;  // tile row of acc[mt][.][i]: mb + 16 mt + i
   if (kind == GemmEpilogue::PARTIALS) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int n = n0 + 64 * wn + 16 * nt + j;
       if (n >= N) continue;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = m0 + mb + 16 * mt + i;
@@ -612,7 +615,7 @@ __device__ __forceinline__ void big_epilogue(const EpiArgs& E, int kind, f32x4 (
     return;
   }
   lds_barrier();  // every wave is done with the stage buffers
-  auto chunk_of = [](int r, int c) { return 32 * r + (c ^ (r & 31)); };  // 16-byte chunk slot
+  auto chunk_of = [](int r, int c) { return CH * r + (c ^ (r & (CH - 1))); };  // 16-byte chunk slot
   const bool query = kind == GemmEpilogue::QUERY;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
@@ -624,7 +627,7 @@ __device__ __forceinline__ void big_epilogue(const EpiArgs& E, int kind, f32x4 (
     // (the barriers keep the next batch's loads from being hoisted above this one's uses)
     const uint32_t tbytes = (uint32_t)min((int64_t)M * half * 4, (int64_t)0x7FFFFFF0);
 #pragma unroll
-    for (int hm = 0; hm < 2; ++hm) {
+    for (int hm = 0; hm < MT / 4; ++hm) {
       __builtin_amdgcn_sched_barrier(0);
       float cs[4][4], sn[4][4];
       if (rope) {
@@ -668,8 +671,8 @@ __device__ __forceinline__ void big_epilogue(const EpiArgs& E, int kind, f32x4 (
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's part of the tile is in LDS
   lds_barrier();
-  for (int e = tid; e < kBigM * kBigN / 8; e += 512) {
-    const int r = e >> 5, c8 = e & 31;
+  for (int e = tid; e < TM * TN / 8; e += 2 * TN) {  // 2 * TN threads
+    const int r = e / CH, c8 = e % CH;
     const int m = m0 + r, n = n0 + 8 * c8;
     if (m >= M || n >= N) continue;
     const uint4 v = *(const uint4*)&st[chunk_of(r, c8) * 8];
@@ -728,7 +731,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(BigArgs G, EpiArgs E) 
     big_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s == -1, (const uint4*)a_1, (const uint4*)w_1,
              (uint4*)a_nx, (uint4*)w_nx, acc, af, bf, w, lane);
   }
-  big_epilogue(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&As[0][0], G.M, G.N, G.C, G.ldc,
+  big_epilogue<256, 256>(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&As[0][0], G.M, G.N, G.C, G.ldc,
                (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
 }
 
@@ -926,8 +929,159 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(BigArgs G, EpiArgs E) {
     w8_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s == -1, sc_idx, (const float*)sc,
             (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx, acc, af, bf, w, lane);
   }
-  big_epilogue(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&smem[0], G.M, G.N, G.C, G.ldc,
+  big_epilogue<256, 256>(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&smem[0], G.M, G.N, G.C, G.ldc,
                (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The same fp8-weight kernel with 128 x 128 tiles (4 waves of 64 x 64) for 64 < M <= 256: at
+// M = 256 the 256 x 256 tile leaves too few workgroups (the v3 stage-1 projection 126, wq_b 96
+// without a K split).  The W stage is [32 k][8 chunks of 16 columns], chunk c of row k at slot
+// 8k + (c ^ ((k >> 1) & 7)): a 32-lane pass of the transposing byte read covers rows k0..k0+15
+// of one chunk, the even rows in one 128-byte half of the 64 banks and the odd rows in the
+// other, each half on 8 distinct 16-byte groups.
+constexpr int kW8sStageA = 128 * 4, kW8sStageW = kBigK * 8;  // 16-byte chunks per stage
+constexpr int kW8sSmem = kW8Stages * (kW8sStageA + kW8sStageW) > 2048 ? kW8Stages * (kW8sStageA + kW8sStageW) : 2048;
+
+__device__ __forceinline__ int w8s_swz(int k) { return (k >> 1) & 7; }
+
+__device__ __forceinline__ W8CopyPlan w8s_offsets(const BigArgs& G, const WeightView& W, int m0, int wn0, int wn_end,
+                                                  int w, int lane) {
+  W8CopyPlan cp;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = 64 * (2 * w + i) + lane, r = e >> 2, c = (e & 3) ^ a4_swz(r);
+    const int m = min(m0 + r, G.M - 1);
+    cp.off[i] = (uint32_t)((m * G.lda + 8 * c) * 2);
+  }
+  const int e = 64 * w + lane, k = e >> 3, c = (e & 7) ^ w8s_swz(k);
+  const int n = min(wn0 + 16 * c, wn_end - 16);
+  cp.off[2] = (uint32_t)(k * W.ld + n);
+  return cp;
+}
+
+// A rows 64*(w >> 1) + 16*mt + j; B columns 64*(w & 1) + 16*nt + j (k = 8g .. 8g+7).
+__device__ __forceinline__ bf16x8 w8s_a(const uint4* __restrict__ as, int mt, int w, int lane) {
+  const int r = 64 * (w >> 1) + 16 * mt + (lane & 15);
+  return as_bf16x8(as[4 * r + ((lane >> 4) ^ a4_swz(r))]);
+}
+
+__device__ __forceinline__ i32x2w w8s_raw(const uint4* __restrict__ ws, int nt, int w, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int k = 8 * g + (j >> 1);
+  const int c = (4 * (w & 1) + nt) ^ w8s_swz(k);
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2w*)((const char*)ws + (8 * k + c) * 16 + 8 * (j & 1)));
+}
+
+// One K step, as w8_step (16 matrix ops per wave, column block by column block, operands
+// refilled from the next stage right after their last use).
+__device__ __forceinline__ void w8s_step(const BigArgs& G, const WeightView& W, const W8CopyPlan& cp, bool copy,
+                                         int k_pf, bool compute, bool pre, int sc_idx, const float* __restrict__ sc,
+                                         const uint4* __restrict__ as1, const uint4* __restrict__ ws1,
+                                         uint4* __restrict__ as_nx, uint4* __restrict__ ws_nx, f32x4 (&acc)[4][4],
+                                         bf16x8 (&af)[4], bf16x8 (&bf)[4], int w, int lane) {
+  if (copy) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16_buf(G.A + k_pf, 0x7FFFFFF0u, cp.off[i], as_nx + 64 * (2 * w + i));
+    dma16_buf((const uint8_t*)W.w + (int64_t)k_pf * W.ld, 0x7FFFFFF0u, cp.off[2], ws_nx + 64 * w);
+  }
+  const float s1 = sc[sc_idx];
+  if (compute) {
+    i32x2w raw = w8s_raw(ws1, 0, w, lane);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      if (nt == 3) __builtin_amdgcn_s_waitcnt(0xC17F);  // lgkmcnt(1): all but the last B read
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+        if (nt == 3) {
+          af[mt] = w8s_a(as1, mt, w, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      const i32x2w nxt = nt < 3 ? w8s_raw(ws1, nt + 1, w, lane) : raw;
+      bf[nt] = w8_dec(raw, s1);
+      raw = nxt;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if (pre) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) af[mt] = w8s_a(as1, mt, w, lane);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) bf[nt] = w8_dec(w8s_raw(ws1, nt, w, lane), s1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+  }
+}
+
+__global__ __launch_bounds__(256) void gemm_w8s_kernel(BigArgs G, EpiArgs E) {
+  __shared__ __attribute__((aligned(16))) uint4 smem[kW8sSmem];
+  __shared__ float scl[kW8MaxKBlocks];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128;
+  const bool seg1 = n0 >= G.n_split;
+  const WeightView W = seg1 ? G.W1 : G.W0;
+  const int wn0 = seg1 ? n0 - G.n_split : n0, wn_end = seg1 ? G.N - G.n_split : G.n_split;
+  const int kbeg = blockIdx.z * G.k_split, kend = min(G.K, kbeg + G.k_split);
+  const int nsteps = (kend - kbeg) / kBigK;
+  // the tile's block scales over the K range (one 128-column block)
+  const int kg0 = kbeg / 128, nkb = (kend + 127) / 128 - kg0;
+  const int nb = min(wn0 / 128, W.scale_ld - 1);
+  for (int t = tid; t < nkb; t += 256) scl[t] = W.scale[(int64_t)(kg0 + t) * W.scale_ld + nb];
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  lds_barrier();
+  const W8CopyPlan cp = w8s_offsets(G, W, m0, wn0, wn_end, w, lane);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 af[4], bf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) af[i] = bf[i] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+  typedef __attribute__((address_space(3))) uint4 lds_uint4;
+  typedef __attribute__((address_space(3))) float lds_float;
+  // copy-only iterations first (as in gemm_w8_kernel), then step -1 (operands of step 0) and
+  // the matrix steps
+  for (int s = -(kW8Stages - 1); s < -1; ++s) {
+    const int s_pf = s + kW8Stages - 1;
+    if (s_pf < nsteps) {
+      lds_uint4* base = (lds_uint4*)smem;
+      uint4* an = (uint4*)(base + kW8sStageA * s_pf);
+      uint4* wn = (uint4*)(base + kW8sStageA * kW8Stages + kW8sStageW * s_pf);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16_buf(G.A + kbeg + s_pf * kBigK, 0x7FFFFFF0u, cp.off[i], an + 64 * (2 * w + i));
+      dma16_buf((const uint8_t*)W.w + (int64_t)(kbeg + s_pf * kBigK) * W.ld, 0x7FFFFFF0u, cp.off[2], wn + 64 * w);
+    }
+  }
+  for (int s = -1; s < nsteps; ++s) {
+    {
+      constexpr int kAhead = kW8Copies * (kW8Stages - 3);
+      if (s + kW8Stages - 2 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F70 | (kAhead & 15) | ((kAhead >> 4) << 14));
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      lds_barrier();
+    }
+    const int s_pf = s + kW8Stages - 1;
+    const int b_pf = (s_pf + kW8Stages) % kW8Stages;
+    const int b_1 = (s + 1 + kW8Stages) % kW8Stages;
+    lds_uint4* base = (lds_uint4*)smem;
+    lds_uint4 *a_1 = base + kW8sStageA * b_1;
+    lds_uint4 *w_1 = base + kW8sStageA * kW8Stages + kW8sStageW * b_1;
+    lds_uint4 *a_nx = base + kW8sStageA * b_pf, *w_nx = base + kW8sStageA * kW8Stages + kW8sStageW * b_pf;
+    lds_float* sc = (lds_float*)&scl[0];
+    asm volatile("" : "+s"(a_1), "+s"(w_1), "+s"(a_nx), "+s"(w_nx), "+s"(sc));
+    const int sc_idx = (kbeg + min(s + 1, nsteps - 1) * kBigK) / 128 - kg0;
+    w8s_step(G, W, cp, s_pf < nsteps, kbeg + s_pf * kBigK, s >= 0, s == -1, sc_idx, (const float*)sc,
+             (const uint4*)a_1, (const uint4*)w_1, (uint4*)a_nx, (uint4*)w_nx, acc, af, bf, w, lane);
+  }
+  big_epilogue<128, 128>(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&smem[0], G.M, G.N, G.C, G.ldc,
+                         (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
+}
+
+bool w8s_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda, int k_split) {
+  return d.wk == W_FP8 && M > 64 && M <= 256 && K % kBigK == 0 && k_split % 128 == 0 &&
+         (k_split + 127) / 128 + 1 <= kW8MaxKBlocks && (n_split >= N || n_split % 128 == 0) && N % 16 == 0 &&
+         (n_split >= N || (N - n_split) % 16 == 0) && ((int64_t)M * lda + K) * 2 < 0x7FFFFFF0LL;
 }
 
 bool w8_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda, int k_split) {
@@ -944,6 +1098,7 @@ bool big_ok(const Dims& d, int M, int N, int K, int n_split, int64_t lda) {
 
 struct Plan {
   int bm, splits, k_split;
+  bool w8s = false;  // fp8 weights, 64 < M <= 256: gemm_w8s_kernel's 128 x 128 tiles
 };
 
 Plan plan(int M, int N, int K, int wk) {
@@ -983,12 +1138,21 @@ Plan plan(int M, int N, int K, int wk) {
   }
   if (wk == W_FP8 && M > 64) {  // gemm_w8_kernel (256 x 256 tiles): K spread over the CUs, but
     // >= kW8MinKSplit k per split, so that the fp32 partial sums stay a fraction of the weights
+    auto split_k = [&](int tiles) {
+      int splits = max(1, 256 / tiles);
+      while (splits > 1 && K / splits < kW8MinKSplit) --splits;
+      p.k_split = ((K + splits - 1) / splits + 127) / 128 * 128;
+      p.splits = (K + p.k_split - 1) / p.k_split;
+    };
     p.bm = 256;
-    const int tiles = ((N + kBigN - 1) / kBigN) * ((M + kBigM - 1) / kBigM);
-    int splits = max(1, 256 / tiles);
-    while (splits > 1 && K / splits < kW8MinKSplit) --splits;
-    p.k_split = ((K + splits - 1) / splits + 127) / 128 * 128;
-    p.splits = (K + p.k_split - 1) / p.k_split;
+    split_k(((N + kBigN - 1) / kBigN) * ((M + kBigM - 1) / kBigM));
+    // up to 256 rows, when those tiles leave the CUs short of work (fewer than 224 workgroups),
+    // gemm_w8s_kernel's 128 x 128 tiles instead (v3 at B = 256: stage-1 126 -> 238 workgroups,
+    // wq_b 192 -> 384 without a K split, so its RoPE runs in the epilogue; wo stays at 252)
+    if (M <= 256 && (int64_t)((N + kBigN - 1) / kBigN) * ((M + kBigM - 1) / kBigM) * p.splits < 224) {
+      p.w8s = true;
+      split_k(((N + 127) / 128) * ((M + 127) / 128));
+    }
     return p;
   }
   p.bm = M <= 64 ? 64 : 128;
@@ -1211,7 +1375,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f8_kernel(F8Args G, EpiArgs E) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{NAN, NAN, NAN, NAN};
   }
-  big_epilogue(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&smem[0][0], G.M, G.N, G.C, G.ldc,
+  big_epilogue<256, 256>(E, seg1 ? E.kind1 : E.kind, acc, (bf16_t*)&smem[0][0], G.M, G.N, G.C, G.ldc,
                (int64_t)blockIdx.z * G.split_stride, m0, n0, w, lane);
 }
 
@@ -1278,7 +1442,12 @@ hipError_t fast_gemm(const Dims& d, const void* A, int64_t lda, const WeightView
     E.sinT = epi->sinT;
     if (fused) *fused = true;
   }
-  if (p.bm == kBigM && w8_ok(d, M, N, K, n_split, lda, p.k_split)) {
+  if (p.w8s && w8s_ok(d, M, N, K, n_split, lda, p.k_split)) {
+    BigArgs G{(const bf16_t*)A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, p.k_split, stride};
+    gemm_w8s_kernel<<<dim3((N + 127) / 128, (M + 127) / 128, p.splits), 256, 0, s>>>(G, E);
+    return hipGetLastError();
+  }
+  if (p.bm == kBigM && !p.w8s && w8_ok(d, M, N, K, n_split, lda, p.k_split)) {
     BigArgs G{(const bf16_t*)A, lda, W0, W1, n_split < N ? n_split : N, out, N, M, N, K, p.k_split, stride};
     gemm_w8_kernel<<<dim3((N + kBigN - 1) / kBigN, (M + kBigM - 1) / kBigM, p.splits), 512, 0, s>>>(G, E);
     return hipGetLastError();
