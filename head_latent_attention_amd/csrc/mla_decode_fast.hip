@@ -157,9 +157,11 @@ __device__ void plan_block(const int32_t* __restrict__ ctx, int B, int32_t* __re
 
 // ------------------------------------------------------------------------------ fold
 // Qabs[b][h] = [q_nope[b][h] @ W_UK[h] | q_pe[b][h]] in bf16, W_UK[h][p][c] = wkv_b[c][h*256 + p].
-// Grid (H + 1, 4, ceil(B/64)): workgroup (h, cg) covers latent columns [128cg, 128cg + 128) of 64
-// rows, wave w the 32 columns [128cg + 32w, 128cg + 32w + 32).  Every operand load of a wave is
-// issued before its first matrix op.
+// Grid (H + 1, 4, ceil(B / 256)): workgroup (h, cg, z) covers latent columns [128cg, 128cg + 128)
+// of rows [256z, 256z + 256), wave w the 32 columns [128cg + 32w, 128cg + 32w + 32); its W_UK
+// operands are loaded once and kept in registers while it walks its rows in groups of 64 (so
+// W_UK is read once per 256 rows).  Every operand load of a group is issued before its first
+// matrix op.
 template <int WK>
 __global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q, int B, WeightView W,
                                                    bf16_t* __restrict__ Qabs, const int32_t* __restrict__ ctx,
@@ -173,65 +175,71 @@ __global__ __launch_bounds__(256) void fold_kernel(const bf16_t* __restrict__ q,
     return;
   }
   __shared__ __attribute__((aligned(16))) uint4 tile[64 * 16];  // 64 rows x 128 columns, bf16
-  const int h = blockIdx.x, cg = blockIdx.y, b0 = blockIdx.z * 64;
+  const int h = blockIdx.x, cg = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
   constexpr int qs = kH * (kDn + kDr);
   const int c0 = 128 * cg + 32 * w;
-  uint4 a[kDn / 32][4], bw[kDn / 32][2];
-  // every load is issued unconditionally (rows past B repeat row B - 1 and are never stored),
-  // so all of them are in flight together
-#pragma unroll
-  for (int ks = 0; ks < kDn / 32; ++ks) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int b = min(b0 + 16 * mt + j, B - 1);
-      a[ks][mt] = *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + 32 * ks + 8 * g);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      bw[ks][nt] = load_w8<WK>(W, c0 + 16 * nt + j, (int64_t)h * (kDn + kDv) + 32 * ks + 8 * g);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep every load above the first matrix op
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 bw[kDn / 32][2];
 #pragma unroll
   for (int ks = 0; ks < kDn / 32; ++ks)
 #pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      bw[ks][nt] = load_w8<WK>(W, c0 + 16 * nt + j, (int64_t)h * (kDn + kDv) + 32 * ks + 8 * g);
+  bf16_t* tb = (bf16_t*)tile;
+  const int b_end = min(B, 256 * (int)blockIdx.z + 256);
+  for (int b0 = 256 * (int)blockIdx.z; b0 < b_end; b0 += 64) {
+    uint4 a[kDn / 32][4];
+    // every load is issued unconditionally (rows past B repeat row B - 1 and are never stored),
+    // so all of them are in flight together
+#pragma unroll
+    for (int ks = 0; ks < kDn / 32; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int b = min(b0 + 16 * mt + j, B - 1);
+        a[ks][mt] = *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + 32 * ks + 8 * g);
+      }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load above the first matrix op
+    f32x4 acc[4][2];
+#pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks][mt]), as_bf16x8(bw[ks][nt]),
-                                                              acc[mt][nt], 0, 0, 0);
-  // the 64 x 128 result through LDS (16-byte chunks, chunk c of row r at slot 16r + (c ^ (r & 15)))
-  // so that each row goes out as 16-byte stores
-  bf16_t* tb = (bf16_t*)tile;
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int ks = 0; ks < kDn / 32; ++ks)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mt + 4 * g + i;
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int c = 32 * w + 16 * nt + j;
-        tb[(16 * r + ((c >> 3) ^ (r & 15))) * 8 + (c & 7)] = f32_to_bf16(acc[mt][nt][i]);
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks][mt]), as_bf16x8(bw[ks][nt]),
+                                                                acc[mt][nt], 0, 0, 0);
+    if (b0 > 256 * (int)blockIdx.z) __syncthreads();  // the previous group's stores have read the tile
+    // the 64 x 128 result through LDS (16-byte chunks, chunk c of row r at slot 16r + (c ^ (r & 15)))
+    // so that each row goes out as 16-byte stores
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * g + i;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int c = 32 * w + 16 * nt + j;
+          tb[(16 * r + ((c >> 3) ^ (r & 15))) * 8 + (c & 7)] = f32_to_bf16(acc[mt][nt][i]);
+        }
       }
-    }
-  __syncthreads();
+    __syncthreads();
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int e = it * 256 + tid, r = e >> 4, ch = e & 15, b = b0 + r;
-    if (b < B) *(uint4*)(Qabs + ((size_t)b * kH + h) * kR + 128 * cg + 8 * ch) = tile[16 * r + (ch ^ (r & 15))];
-  }
-  // rope part of the query is carried over unchanged
-  if (cg == 0) {
-    for (int e = tid; e < 64 * kDr / 8; e += 256) {
-      const int r = e / (kDr / 8), c = e - r * (kDr / 8), b = b0 + r;
-      if (b < B)
-        *(uint4*)(Qabs + ((size_t)b * kH + h) * kR + kLkv + 8 * c) =
-            *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + kDn + 8 * c);
+    for (int it = 0; it < 4; ++it) {
+      const int e = it * 256 + tid, r = e >> 4, ch = e & 15, b = b0 + r;
+      if (b < B) *(uint4*)(Qabs + ((size_t)b * kH + h) * kR + 128 * cg + 8 * ch) = tile[16 * r + (ch ^ (r & 15))];
+    }
+    // rope part of the query is carried over unchanged
+    if (cg == 0) {
+      for (int e = tid; e < 64 * kDr / 8; e += 256) {
+        const int r = e / (kDr / 8), c = e - r * (kDr / 8), b = b0 + r;
+        if (b < B)
+          *(uint4*)(Qabs + ((size_t)b * kH + h) * kR + kLkv + 8 * c) =
+              *(const uint4*)(q + (size_t)b * qs + h * (kDn + kDr) + kDn + 8 * c);
+      }
     }
   }
 }
@@ -786,7 +794,7 @@ hipError_t fast_decode_attn(const Dims& d, const void* q, int B, const void* cac
                             const int32_t* block_table, int max_blocks, int64_t bt_stride, const int32_t* ctx,
                             const WeightView& wkv_b, void* o, const FastDecodeWs& ws, hipStream_t s) {
   const DecodeLayout L = layout(B, ws.base);
-  dim3 fgrid(kH + 1, kLkv / 128, (B + 63) / 64);
+  dim3 fgrid(kH + 1, kLkv / 128, (B + 255) / 256);
   if (d.wk == W_BF16)
     fold_kernel<W_BF16><<<fgrid, 256, 0, s>>>((const bf16_t*)q, B, wkv_b, L.Qabs, ctx, L.P, L.info, L.zero_row);
   else
