@@ -202,12 +202,17 @@ __global__ __launch_bounds__(256) void row_builder_bf16x8_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nq = Lq / 8, nk = Lkv / 8, nr = dr / 8, total = nq + nk + nr;
   const int R = Lkv + dr, dqk = dn + dr, half = dr >> 1;
+  // grid y = 2: workgroup y takes the query latent (y = 0) or the kv latent and rope key (y = 1)
+  // of its row, so that two workgroups share the row's partial sums; y = 1: all of them
+  const int e_lo = gridDim.y == 2 && blockIdx.y == 1 ? nq : 0;
+  const int e_hi = gridDim.y == 2 && blockIdx.y == 0 ? nq : total;
   float v[MAXC][8];
   float ssq = 0.f, ssk = 0.f;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    const int e = tid + 256 * c;
-    if (e < nq) {
+    const int e = e_lo + tid + 256 * c;
+    if (e >= e_hi) {
+    } else if (e < nq) {
       part_ld8(Yq, t, 8 * e, v[c]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) ssq += v[c][i] * v[c][i];
@@ -238,9 +243,10 @@ __global__ __launch_bounds__(256) void row_builder_bf16x8_kernel(
   }
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    const int e = tid + 256 * c;
+    const int e = e_lo + tid + 256 * c;
     float y[8];
-    if (e < nq) {
+    if (e >= e_hi) {
+    } else if (e < nq) {
       if (!cqn) continue;
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = v[c][i] * rq * gq[8 * e + i];
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(256) void row_builder_bf16x8_kernel(
       kpe_s[ch] = pk;
     }
   }
-  if (!kbuf) return;
+  if (!kbuf || e_hi < total) return;
   __syncthreads();
   bf16_t* krow = kbuf + t * H * dqk + dn;
   for (int e = tid; e < H * nr; e += 256) {
@@ -287,7 +293,13 @@ hipError_t row_builder(const Dims& d, const Partials& Yq, const Partials& Ykv, i
   if (d.act == 1 && d.Lq % 8 == 0 && d.Lkv % 8 == 0 && d.dr % 8 == 0 && d.dn % 8 == 0 && d.dr <= 256 &&
       total8 <= 512 && (d.Lq == 0 || part_vec8_ok(Yq)) && part_vec8_ok(Ykv) && al16(cqn) && al16(cn) && al16(cache) &&
       al16(kbuf)) {
-    if (total8 <= 256)
+    // two workgroups per row (query latent; kv latent and rope key) when each part fits one pass
+    const bool split = d.Lq > 0 && d.Lq / 8 <= 256 && (d.Lkv + d.dr) / 8 <= 256;
+    if (split)
+      row_builder_bf16x8_kernel<1><<<dim3(T, 2), 256, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT,
+                                                              (bf16_t*)cqn, (bf16_t*)cn, (bf16_t*)cache, n_slots,
+                                                              slot_mapping, (bf16_t*)kbuf, d.H, d.dn);
+    else if (total8 <= 256)
       row_builder_bf16x8_kernel<1><<<T, 256, 0, s>>>(Yq, Ykv, d.Lq, d.Lkv, d.dr, gq, gkv, d.eps, cosT, sinT,
                                                      (bf16_t*)cqn, (bf16_t*)cn, (bf16_t*)cache, n_slots, slot_mapping,
                                                      (bf16_t*)kbuf, d.H, d.dn);
