@@ -71,7 +71,9 @@ def decode_setup(w, device="cuda", device_fill=False):
     slot = torch.from_numpy(synth.decode_slot_mapping(pg)).to(device)
     bt = torch.from_numpy(pg.block_table).to(device)
     cl = torch.from_numpy(ctx).to(device)
-    # each step builds its rope tables on the device at positions context_lens - 1
+    # each step builds its rope tables on the device at positions context_lens - 1, from the
+    # model's inverse frequencies (plain RoPE, base 10000), built once like the weights
+    inv_freq = mla.mla_rope_inv_freq(mla.rope(theta=10000.0), s.qk_rope, device=device)
     cos = torch.empty((w.B, s.qk_rope // 2), dtype=torch.float32, device=device)
     sin = torch.empty_like(cos)
     q = torch.empty((w.B, s.n_heads, s.qk_head), dtype=torch.bfloat16, device=device)
@@ -83,7 +85,7 @@ def decode_setup(w, device="cuda", device_fill=False):
         "attn": mla.workspace(cfg, 3, w.B, max_ctx),
         "out": mla.workspace(cfg, 4, w.B),
     }
-    return dict(mla=mla, cfg=cfg, dw=dw, host=host, ctx=ctx, pg=pg, cache=cache, x=x, cos=cos, sin=sin,
+    return dict(mla=mla, cfg=cfg, dw=dw, host=host, ctx=ctx, pg=pg, cache=cache, x=x, cos=cos, sin=sin, inv_freq=inv_freq,
                 slot=slot, bt=bt, cl=cl, q=q, o=o, y=y, ws=ws)
 
 
@@ -91,7 +93,7 @@ def decode_step(S, ev=None):
     mla = S["mla"]
     if ev:
         ev[0].record()
-    mla.mla_rope_tables(S["cl"], S["cl"].numel(), S["cfg"].qk_rope, None, pos_offset=-1, cos=S["cos"], sin=S["sin"])
+    mla.mla_rope_tables(S["cl"], S["cl"].numel(), S["cfg"].qk_rope, S["inv_freq"], pos_offset=-1, cos=S["cos"], sin=S["sin"])
     mla.mla_decode_qkv_and_scatter(S["cfg"], S["dw"], S["x"], S["cos"], S["sin"], S["cache"], S["slot"], S["q"],
                                    ws=S["ws"]["qkv"])
     if ev:
@@ -318,7 +320,7 @@ def decode_parts(S):
     mla = S["mla"]
 
     def front():
-        mla.mla_rope_tables(S["cl"], S["cl"].numel(), S["cfg"].qk_rope, None, pos_offset=-1, cos=S["cos"],
+        mla.mla_rope_tables(S["cl"], S["cl"].numel(), S["cfg"].qk_rope, S["inv_freq"], pos_offset=-1, cos=S["cos"],
                             sin=S["sin"])
         mla.mla_decode_qkv_and_scatter(S["cfg"], S["dw"], S["x"], S["cos"], S["sin"], S["cache"], S["slot"], S["q"],
                                        ws=S["ws"]["qkv"])

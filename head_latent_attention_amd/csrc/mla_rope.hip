@@ -48,23 +48,26 @@ __global__ void rope_inv_freq_kernel(int dr, double theta, double factor, double
   out[i] = plain / factor * share + plain * (1.0 - share);
 }
 
-__global__ void rope_tables_kernel(int n, int half, const int32_t* __restrict__ positions, int pos_offset,
+// IDX: the index type of the flattened [n, half] table (32-bit division where the table allows).
+template <typename IDX>
+__global__ void rope_tables_kernel(IDX total, int half, const int32_t* __restrict__ positions, int pos_offset,
                                    const double* __restrict__ inv_freq, float* __restrict__ cosT,
                                    float* __restrict__ sinT) {
-  const int64_t total = (int64_t)n * half;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int t = (int)(e / half), i = (int)(e - (int64_t)t * half);
-    const int64_t pos = (int64_t)(positions ? positions[t] : t) + pos_offset;
+  for (IDX e = blockIdx.x * (IDX)blockDim.x + threadIdx.x; e < total; e += (IDX)gridDim.x * blockDim.x) {
+    const IDX t = e / (IDX)half;
+    const int i = (int)(e - t * (IDX)half);
+    const int64_t pos = (int64_t)(positions ? positions[t] : (int64_t)t) + pos_offset;
     const double f = inv_freq ? inv_freq[i] : pow(10000.0, -2.0 * i / (2 * half));
-    // the angle and its reduction to a quadrant, a = q pi/2 + r with |r| <= pi/4, in fp64
-    // (exact to ~1e-11 rad up to 1e5 rad); then fp32 cos/sin of r (rounding r to fp32 costs
+    // the angle and its reduction to a quadrant, a = q pi/2 + r with |r| <= pi/4 (up to the
+    // rounding of a * 2/pi near a quadrant boundary), in fp64: r is one fused multiply-add,
+    // exact to ~1e-11 rad up to 1e5 rad; then fp32 cos/sin of r (rounding r to fp32 costs
     // <= 3e-8 rad) rotated by the quadrant: a few fp32 ulps, at a fraction of fp64 sincos's cost
     const double a = (double)pos * f;
     const double half_pi = 1.5707963267948966192313216916398;
-    const double qd = rint(a / half_pi);
+    const double two_over_pi = 0.63661977236758134307553505349006;
+    const double qd = rint(a * two_over_pi);
     float sr, cr;
-    sincosf((float)(a - qd * half_pi), &sr, &cr);
+    sincosf((float)fma(-qd, half_pi, a), &sr, &cr);
     const int quad = (int)((int64_t)qd & 3);
     const float c = quad == 0 ? cr : quad == 1 ? -sr : quad == 2 ? -cr : sr;
     const float sn = quad == 0 ? sr : quad == 1 ? cr : quad == 2 ? -sr : -cr;
@@ -159,7 +162,11 @@ hipError_t rope_tables(int n, int dr, const int32_t* positions, int pos_offset, 
   const int half = dr / 2;
   const int64_t total = (int64_t)n * half;
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
-  rope_tables_kernel<<<blocks, 256, 0, s>>>(n, half, positions, pos_offset, inv_freq, cosT, sinT);
+  if (total <= INT32_MAX)
+    rope_tables_kernel<uint32_t><<<blocks, 256, 0, s>>>((uint32_t)total, half, positions, pos_offset, inv_freq, cosT,
+                                                        sinT);
+  else
+    rope_tables_kernel<int64_t><<<blocks, 256, 0, s>>>(total, half, positions, pos_offset, inv_freq, cosT, sinT);
   return hipGetLastError();
 }
 
