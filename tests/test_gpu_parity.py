@@ -206,6 +206,36 @@ def test_decode_attn_absorbed(w, q_std):
                  bs_)
 
 
+# Few long sequences: each one split across many attention shares, so the combine merges up to
+# 256 partial results per head and sequence (B = 1, 16384 tokens: exactly one 64-token tile per
+# share; B = 2: about 128 shares per sequence).  The weights are those of the full-size decode
+# workload (same shapes; the cases above leave them cached).
+LONG_ONE = synth.custom(W[3], 112, "long-one-h128", B=1, ctx_lo=16384, ctx_hi=16384)
+LONG_TWO = synth.custom(W[3], 113, "long-two-h128", B=2, ctx_lo=9000, ctx_hi=13000)
+
+
+@pytest.mark.parametrize("w", [LONG_ONE, LONG_TWO], ids=lambda w: w.name)
+def test_decode_attn_long_split(w):
+    need_gpu()
+    import head_latent_attention_amd as mla
+    s = w.shape
+    host, Wd, dw = _weights(W[3])
+    cfg = lib_config(s)
+    ctx = synth.context_lengths(w)
+    print(f"[decode_attn_long] {w.name} B={w.B} contexts {ctx.tolist()}", flush=True)
+    pg, cache = _paged_cache(w, ctx)
+    qh = synth.make_normal(w, "decode.q", (w.B, s.n_heads, s.qk_head), std=0.8)
+    o = torch_io.empty_act(s.act, (w.B, s.n_heads, s.v_dim))
+    mla.mla_decode_attn_absorbed(cfg, dw, torch_io.to_device(qh), cache, torch.from_numpy(pg.block_table).cuda(),
+                                 torch.from_numpy(ctx).cuda(), o)
+    torch.cuda.synchronize()
+    bs_ = np.arange(w.B)
+    q64 = O.decode_tensor(s.act, qh.data)
+    seqs = [O.decode_tensor(s.act, synth.history_rows(w, int(b), int(ctx[b])).data) for b in bs_]
+    ref = O.decode_attention(Wd, q64, seqs, O.dims_of(s))
+    assert_close(torch_io.to_f64(o), ref, s.act, f"o (contexts {ctx.tolist()})", bs_)
+
+
 # Many short sequences: several whole sequences inside one attention workgroup's share of the
 # 64-token tile list (so partial results are written and queries reloaded several times per
 # workgroup), and more sequences than the planner keeps in LDS (its global-memory path).
