@@ -23,6 +23,10 @@ SMALL_V2 = synth.custom(W[2], 102, "small-v2-prefill", hidden=512, n_heads=16, T
 ODD_HEADS = synth.custom(W[4], 109, "odd-heads-prefill", hidden=1024, n_heads=10, q_lora_rank=256, T=4000)
 EDGE_DEC16 = synth.custom(W[3], 103, "edge-decode-h16", hidden=1024, n_heads=16, q_lora_rank=256, B=6)
 EDGE_DEC128 = synth.custom(W[3], 104, "edge-decode-h128", B=6)
+# the same sequences in 32- and 96-token cache blocks (a 32-token attention sub-tile always lies in
+# one block; 96 is not a power of two); same number, so the same weights and rows
+EDGE_BS32 = synth.custom(W[3], 104, "edge-decode-h128-bs32", B=6, block_size=32)
+EDGE_BS96 = synth.custom(W[3], 104, "edge-decode-h128-bs96", B=6, block_size=96)
 EDGE_FP8 = synth.custom(W[5], 105, "edge-decode-fp8", B=6)
 # fp8 weights at 64 < M <= 1024 (the mid-M fp8 kernel): ragged rows, a partial last column tile of
 # the kv segment, the query up-projection unsplit (RoPE fused in the kernel)
@@ -123,7 +127,7 @@ def test_prefill_attn(w, T, q_std):
 
 
 # ----------------------------------------------------------------------------- decode front end
-@pytest.mark.parametrize("w", [EDGE_DEC16, EDGE_DEC128, W[3], W[5], MID_FP8], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [EDGE_DEC16, EDGE_DEC128, EDGE_BS32, EDGE_BS96, W[3], W[5], MID_FP8], ids=lambda w: w.name)
 def test_decode_qkv_and_scatter(w):
     need_gpu()
     import head_latent_attention_amd as mla
@@ -178,8 +182,8 @@ def _decode_sample(ctx):
 
 # q_std 6.4 (8x the usual 0.8) makes the softmax peaky: the lazy rescale runs along every long
 # sequence.
-DECODE_ATTN_CASES = [(EDGE_DEC16, 0.8), (EDGE_DEC128, 0.8), (EDGE_FP8, 0.8), (W[3], 0.8), (W[5], 0.8),
-                     (EDGE_DEC128, 6.4), (W[3], 6.4)]
+DECODE_ATTN_CASES = [(EDGE_DEC16, 0.8), (EDGE_DEC128, 0.8), (EDGE_BS32, 0.8), (EDGE_BS96, 0.8), (EDGE_FP8, 0.8),
+                     (W[3], 0.8), (W[5], 0.8), (EDGE_DEC128, 6.4), (W[3], 6.4)]
 
 
 @pytest.mark.parametrize("w,q_std", DECODE_ATTN_CASES,
