@@ -16,6 +16,9 @@ W = synth.WORKLOADS
 CH_TINY = synth.custom(W[1], 140, "chunk-tiny-fp32")
 CH_V3 = synth.custom(W[3], 141, "chunk-v3-heads", hidden=1024, q_lora_rank=256)
 CH_V3_FULL = synth.custom(W[3], 142, "chunk-v3")
+# the same workload in 96- and 32-token cache blocks
+CH_V3_BS96 = synth.custom(W[3], 141, "chunk-v3-heads-bs96", hidden=1024, q_lora_rank=256, block_size=96)
+CH_V3_BS32 = synth.custom(W[3], 141, "chunk-v3-heads-bs32", hidden=1024, q_lora_rank=256, block_size=32)
 
 
 def _run_chunk(w, dw, cfg, cache, table, prefix, T, xh):
@@ -66,7 +69,8 @@ def test_chunks_after_prefill_tiny_fp32():
 # the expanded one (more than ~170 queries per cached row), (600, 400) with its expansion through
 # the smaller projection kernel (1000 rows)
 @pytest.mark.parametrize("w,prefix,T", [(CH_V3, 0, 130), (CH_V3, 1000, 77), (CH_V3, 3000, 300), (CH_V3, 64, 1),
-                                        (CH_V3, 600, 400), (CH_V3_FULL, 4096, 512)],
+                                        (CH_V3, 600, 400), (CH_V3_FULL, 4096, 512), (CH_V3_BS96, 1000, 77),
+                                        (CH_V3_BS96, 3000, 300), (CH_V3_BS32, 600, 400)],
                          ids=lambda c: str(c) if isinstance(c, int) else c.name)
 def test_chunk_over_cached_history(w, prefix, T):
     """A chunk of T tokens over `prefix` history rows already in the paged cache (V2/V3 per-head
