@@ -627,23 +627,33 @@ template <int WK, int SG>
 __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, const int32_t* __restrict__ P,
                                                       int B, WeightView W, bf16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[16 * SG][kLkv + 8];
-  __shared__ __attribute__((aligned(16))) bf16_t Ws[128][kDv + 16];
+  // merged latent rows As [16 SG][512] and one 64-row chunk of W_UV[h] Ws [64][128], bf16, both
+  // unpadded with 16-byte chunks XOR-swizzled by row (As: chunk c of row r at 64r + (c ^ (r & 15));
+  // Ws: chunk c of row r at 16r + (c ^ ws_swz(r))), so that four groups of 16 sequences take
+  // 80 KB and two workgroups fit on a CU
+  __shared__ __attribute__((aligned(16))) uint4 As[16 * SG * (kLkv / 8)];
+  __shared__ __attribute__((aligned(16))) uint4 Ws[64 * (kDv / 8)];
   const int h = blockIdx.x, b0 = blockIdx.y * 16 * SG;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
   const int N = P[B];
   const int64_t col0 = (int64_t)h * (kDn + kDv) + kDn;
-  // W_UV[h] in four chunks of 128 rows: the first loads ahead of the merge, each later one while
-  // the previous one is multiplied; every chunk serves all SG groups of 16 sequences
-  uint4 wr[8];
+  // the rows of a 32-lane transposing read (8 rows: 4 consecutive, twice, 8 apart) get distinct
+  // even keys, so each row's 32 bytes land on their own banks
+  auto ws_swz = [](int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); };
+  // W_UV[h] in eight chunks of 64 rows, two in registers at a time: the first two load ahead of
+  // the merge, each later one once the chunk two before it is in LDS; every chunk serves all SG
+  // groups of 16 sequences
+  constexpr int AH = 2, kWc = kLkv / 64;
+  uint4 wr[AH][4];
   auto load_chunk = [&](int cc) {
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < 4; ++it) {
       const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
-      wr[it] = load_w8<WK>(W, 128 * cc + r, col0 + 8 * ch);
+      wr[cc % AH][it] = load_w8<WK>(W, 64 * cc + r, col0 + 8 * ch);
     }
   };
-  load_chunk(0);
+#pragma unroll
+  for (int cc = 0; cc < AH; ++cc) load_chunk(cc);
   __builtin_amdgcn_sched_barrier(0);  // the weight loads stay ahead of the merge
   // ---- merge: the 16 lanes of quarter g of wave w handle local row 4w + g of each group, each
   // lane 32 latent columns, so the four rows of a wave run their shares side by side (four
@@ -700,7 +710,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
-      *(uint4*)&As[lb][32 * j + 8 * q4] =
+      As[lb * (kLkv / 8) + ((4 * j + q4) ^ (lb & 15))] =
           make_uint4(pack_bf16x2(acc[8 * q4] * inv, acc[8 * q4 + 1] * inv),
                      pack_bf16x2(acc[8 * q4 + 2] * inv, acc[8 * q4 + 3] * inv),
                      pack_bf16x2(acc[8 * q4 + 4] * inv, acc[8 * q4 + 5] * inv),
@@ -710,29 +720,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   f32x4 acc[SG][2];
 #pragma unroll
   for (int sg = 0; sg < SG; ++sg) acc[sg][0] = acc[sg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int cc = 0; cc < kLkv / 128; ++cc) {
+  for (int cc = 0; cc < kWc; ++cc) {
     __syncthreads();
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < 4; ++it) {
       const int e = it * 256 + tid, r = e >> 4, ch = e & 15;
-      *(uint4*)&Ws[r][8 * ch] = wr[it];
+      Ws[16 * r + (ch ^ ws_swz(r))] = wr[cc % AH][it];
     }
     __syncthreads();
-    if (cc + 1 < kLkv / 128) load_chunk(cc + 1);
+    if (cc + AH < kWc) load_chunk(cc + AH);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       bf16x8 bop[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int col = 32 * w + 16 * nt + 4 * (j & 3);
-        const int row = 32 * ks + 8 * g + (j >> 2);
-        const bf16x4 b0v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&Ws[row][col]);
-        const bf16x4 b1v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&Ws[row + 4][col]);
+        // rows 32ks + 8g + j/4 (+4) of the chunk, columns 32w + 16nt + 4(j & 3) .. + 3
+        const int c = 4 * w + 2 * nt + ((j & 3) >> 1), r0 = 32 * ks + 8 * g + (j >> 2), r1 = r0 + 4;
+        const char* p0 = (const char*)&Ws[16 * r0 + (c ^ ws_swz(r0))] + 8 * (j & 1);
+        const char* p1 = (const char*)&Ws[16 * r1 + (c ^ ws_swz(r1))] + 8 * (j & 1);
+        const bf16x4 b0v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+        const bf16x4 b1v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
         bop[nt] = __builtin_shufflevector(b0v, b1v, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
       for (int sg = 0; sg < SG; ++sg) {
-        const bf16x8 a = as_bf16x8(*(const uint4*)&As[16 * sg + j][128 * cc + 32 * ks + 8 * g]);
+        const int r = 16 * sg + j;
+        const bf16x8 a = as_bf16x8(As[r * (kLkv / 8) + ((8 * cc + 4 * ks + g) ^ (r & 15))]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[sg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[nt], acc[sg][nt], 0, 0, 0);
       }
